@@ -1,0 +1,279 @@
+"""ctypes front-end of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark, never by the product package.  It holds no
+arithmetic of the method: every value is computed by the C oracle, this file
+only allocates numpy buffers and marshals pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+FLAG_NONFINITE = 1
+FLAG_DEGENERATE = 2
+SYM, AFFINE = 0, 1
+E4M3, E5M2 = 0, 1
+F32, BF16 = 0, 1
+
+# Strict binary32: no FMA contraction, no fast-math, no re-association.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-Wall", "-Wextra"]
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so with gcc (always recompiles)."""
+    tmp = LIB + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_INT = ctypes.c_int
+_F = ctypes.c_float
+_U32 = ctypes.c_uint32
+_U8 = ctypes.c_uint8
+
+_SIGS = {
+    "orc_q_range": (_INT, [_INT, _INT, _P, _P]),
+    "orc_finite_min_max": (_U32, [_P, _INT, _I64, _I64, _P, _P]),
+    "orc_params_from_minmax": (_U32, [_F, _F, _INT, _INT, _P, _P]),
+    "orc_quantize": (_I32, [_F, _F, _I32, _I32, _I32]),
+    "orc_dequantize": (_F, [_I32, _F, _I32]),
+    "orc_real_bounds": (None, [_F, _I32, _I32, _I32, _P, _P]),
+    "orc_tensor_params_int": (_U32, [_P, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "orc_fake_quant_int": (None, [_P, _I64, _INT, _INT, _F, _I32, _P, _P]),
+    "orc_dequantize_int": (None, [_P, _I64, _F, _I32, _P]),
+    "orc_ste_backward": (None, [_P, _P, _I64, _F, _F, _P]),
+    "orc_quant_rows": (_U32, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "orc_fp8_encode": (_U8, [_F, _INT]),
+    "orc_fp8_decode": (_F, [_U8, _INT]),
+    "orc_fp8_encode_n": (None, [_P, _I64, _INT, _P]),
+    "orc_fp8_decode_n": (None, [_P, _I64, _INT, _P]),
+    "orc_amax_finite": (_F, [_P, _I64]),
+    "orc_fp8_scale": (_U32, [_F, _INT, _P]),
+    "orc_fp8_quantize": (None, [_P, _I64, _INT, _F, _P, _P]),
+    "orc_fp8_dequantize": (None, [_P, _I64, _INT, _F, _P]),
+    "orc_q4dq_quantize": (_U32, [_P, _I64, _P, _P, _P, _P, _P]),
+    "orc_q4dq_dequantize": (None, [_P, _P, _P, _I64, _P]),
+    "orc_mxfp8_rows": (None, [_P, _INT, _I64, _I64, _P, _P, _P]),
+    "orc_bf16_to_f32": (_F, [ctypes.c_uint16]),
+}
+
+
+def lib():
+    """Load liboracle.so, building it first if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        handle = ctypes.CDLL(LIB)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _scalar_out(ctype):
+    return ctype()
+
+
+# --- scalar helpers -----------------------------------------------------------
+
+def q_range(bits: int, scheme: int):
+    lo, hi = _I32(), _I32()
+    st = lib().orc_q_range(bits, scheme, ctypes.byref(lo), ctypes.byref(hi))
+    if st != 0:
+        raise ValueError(f"unsupported width {bits}")
+    return lo.value, hi.value
+
+
+def params_from_minmax(mn: float, mx: float, bits: int, scheme: int):
+    s, z = _F(), _I32()
+    flags = lib().orc_params_from_minmax(mn, mx, bits, scheme, ctypes.byref(s), ctypes.byref(z))
+    return s.value, z.value, flags
+
+
+def quantize(x: float, scale: float, zp: int, qmin: int, qmax: int) -> int:
+    return lib().orc_quantize(x, scale, zp, qmin, qmax)
+
+
+def dequantize(q: int, scale: float, zp: int) -> float:
+    return lib().orc_dequantize(q, scale, zp)
+
+
+def fp8_encode(y: float, fmt: int) -> int:
+    return lib().orc_fp8_encode(y, fmt)
+
+
+def fp8_decode(b: int, fmt: int) -> float:
+    return lib().orc_fp8_decode(b, fmt)
+
+
+# --- array entry points ------------------------------------------------------
+
+def finite_min_max(x):
+    x = _f32(x)
+    mn, mx = _F(), _F()
+    flags = lib().orc_finite_min_max(_ptr(x), F32, x.size, 1, ctypes.byref(mn), ctypes.byref(mx))
+    return mn.value, mx.value, flags
+
+
+def tensor_params_int(x, bits: int, scheme: int):
+    """Returns dict(scale, zp, lo, hi, flags) of per_tensor_minmax calibration."""
+    x = _f32(x).ravel()
+    s, z, lo, hi = _F(), _I32(), _F(), _F()
+    flags = lib().orc_tensor_params_int(_ptr(x), x.size, bits, scheme, ctypes.byref(s),
+                                        ctypes.byref(z), ctypes.byref(lo), ctypes.byref(hi))
+    return dict(scale=np.float32(s.value), zp=z.value, lo=np.float32(lo.value),
+                hi=np.float32(hi.value), flags=flags)
+
+
+def fake_quant_int(x, bits: int, scheme: int, scale: float, zp: int):
+    x = _f32(x).ravel()
+    codes = np.empty(x.size, np.int8)
+    fq = np.empty(x.size, np.float32)
+    lib().orc_fake_quant_int(_ptr(x), x.size, bits, scheme, scale, zp, _ptr(codes), _ptr(fq))
+    return codes, fq
+
+
+def dequantize_int(codes, scale: float, zp: int):
+    codes = np.ascontiguousarray(codes, dtype=np.int8).ravel()
+    out = np.empty(codes.size, np.float32)
+    lib().orc_dequantize_int(_ptr(codes), codes.size, scale, zp, _ptr(out))
+    return out
+
+
+def ste_backward(g, x, b0: float, b1: float):
+    g = _f32(g).ravel()
+    x = _f32(x).ravel()
+    assert g.size == x.size
+    out = np.empty(x.size, np.float32)
+    lib().orc_ste_backward(_ptr(g), _ptr(x), x.size, b0, b1, _ptr(out))
+    return out
+
+
+def quant_rows(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True):
+    """x: [rows, cols] float32 array, or uint16 array of bfloat16 bits (dtype=BF16)."""
+    if dtype == BF16:
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+    else:
+        x = _f32(x)
+    rows, cols = x.shape
+    if bits == 8:
+        codes = np.empty((rows, cols), np.int8)
+    else:
+        codes = np.empty((rows, (cols + 1) // 2), np.uint8)
+    fq = np.empty((rows, cols), np.float32) if want_fq else None
+    scale = np.empty(rows, np.float32)
+    zp = np.empty(rows, np.int32)
+    flags = lib().orc_quant_rows(_ptr(x), dtype, rows, cols, bits, scheme, _ptr(codes), _ptr(fq),
+                                 _ptr(scale), _ptr(zp))
+    return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
+
+
+def fp8_encode_n(y, fmt: int):
+    y = _f32(y).ravel()
+    out = np.empty(y.size, np.uint8)
+    lib().orc_fp8_encode_n(_ptr(y), y.size, fmt, _ptr(out))
+    return out
+
+
+def fp8_decode_n(b, fmt: int):
+    b = np.ascontiguousarray(b, dtype=np.uint8).ravel()
+    out = np.empty(b.size, np.float32)
+    lib().orc_fp8_decode_n(_ptr(b), b.size, fmt, _ptr(out))
+    return out
+
+
+def amax_finite(x) -> np.float32:
+    x = _f32(x).ravel()
+    return np.float32(lib().orc_amax_finite(_ptr(x), x.size))
+
+
+def fp8_scale(amax: float, fmt: int):
+    s = _F()
+    flags = lib().orc_fp8_scale(amax, fmt, ctypes.byref(s))
+    return np.float32(s.value), flags
+
+
+def fp8_quantize(x, fmt: int, scale: float, want_q: bool = True, want_fq: bool = True):
+    x = _f32(x).ravel()
+    q = np.empty(x.size, np.uint8) if want_q else None
+    fq = np.empty(x.size, np.float32) if want_fq else None
+    lib().orc_fp8_quantize(_ptr(x), x.size, fmt, scale, _ptr(q), _ptr(fq))
+    return q, fq
+
+
+def fp8_dequantize(q, fmt: int, scale: float):
+    q = np.ascontiguousarray(q, dtype=np.uint8).ravel()
+    out = np.empty(q.size, np.float32)
+    lib().orc_fp8_dequantize(_ptr(q), q.size, fmt, scale, _ptr(out))
+    return out
+
+
+def q4dq_sizes(n: int):
+    nb = (n + 63) // 64
+    return (n + 1) // 2, nb, (nb + 255) // 256
+
+
+def q4dq_quantize(x, want_block_scale: bool = True, want_recon: bool = True):
+    x = _f32(x).ravel()
+    n = x.size
+    npk, nb, ns = q4dq_sizes(n)
+    packed = np.empty(npk, np.uint8)
+    qscale = np.empty(nb, np.uint8)
+    sup = np.empty(ns, np.float32)
+    bs = np.empty(nb, np.float32) if want_block_scale else None
+    recon = np.empty(n, np.float32) if want_recon else None
+    flags = lib().orc_q4dq_quantize(_ptr(x), n, _ptr(packed), _ptr(qscale), _ptr(sup), _ptr(bs),
+                                    _ptr(recon))
+    return dict(packed=packed, qscale=qscale, super=sup, block_scale=bs, recon=recon, flags=flags)
+
+
+def q4dq_dequantize(packed, qscale, sup, n: int):
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    qscale = np.ascontiguousarray(qscale, dtype=np.uint8)
+    sup = _f32(sup)
+    out = np.empty(n, np.float32)
+    lib().orc_q4dq_dequantize(_ptr(packed), _ptr(qscale), _ptr(sup), n, _ptr(out))
+    return out
+
+
+def mxfp8_rows(x, dtype: int = BF16, want_fq: bool = True):
+    if dtype == BF16:
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+    else:
+        x = _f32(x)
+    rows, cols = x.shape
+    nbr = (cols + 31) // 32
+    q = np.empty((rows, cols), np.uint8)
+    e8 = np.empty((rows, nbr), np.uint8)
+    fq = np.empty((rows, cols), np.float32) if want_fq else None
+    lib().orc_mxfp8_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(e8), _ptr(fq))
+    return dict(q=q, e8m0=e8, fq=fq)
