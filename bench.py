@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Benchmark of the fake-quant hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu]
+
+One step runs every operation of the path once, each on the full-size synthetic
+input of its workload (all inputs resident in HBM before timing starts):
+
+  tensor    per-tensor symmetric int8 of 2^20 N(0,1) fp32: calibration, fake-quant
+            (codes + fq), STE backward
+  rows_f32  per-row int8 / int4, symmetric / affine of a [4096, 4096] fp32 weight
+            (codes + fq + scale + zero-point)
+  fp8       finite-amax scale, E4M3 and E5M2 quantize (bytes + fq) and dequantize
+            of 2^26 log-uniform fp32 with +-Inf / NaN / zeros
+  q4dq      64-element 4-bit blocks + double-quantized scales of 2^30 Student-t
+            fp32 (packed + u8 scales + super-scales + reconstruction), dequantize
+  rows_bf16 per-token affine int8 and 32-element E4M3 blocks with E8M0 scales of a
+            [16384, 8192] bf16 ReLU activation with outlier channels
+
+`value` = algorithmic bytes of the step (each contract input read once, each
+output written once) / measured step time, in GB/s; `roofline` is the dominant
+kernel's achieved bandwidth against the 8 TB/s HBM peak; `cpu_baseline` is the
+CPU oracle on a bounded sample of the same work.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective GB/s of quantize/fake-quant kernels; % of MI355X HBM peak"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", nargs="*", default=None,
+                    help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+class Op:
+    def __init__(self, name, kernel, fn, nbytes):
+        self.name, self.kernel, self.fn, self.nbytes = name, kernel, fn, nbytes
+
+
+def ops_tensor(fq, syn, torch, dev):
+    n = syn.FULL["tensor"]["n"]
+    x, g = syn.tensor_inputs(n, device=dev)
+    wsb = fq.fq_workspace_bytes(n)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    params = torch.empty(4, dtype=torch.int32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    codes = torch.empty(n, dtype=torch.int8, device=dev)
+    fqo = torch.empty(n, dtype=torch.float32, device=dev)
+    gin = torch.empty(n, dtype=torch.float32, device=dev)
+    bounds = params.view(torch.float32)[2:4]
+    return [
+        Op("tensor.params_int8_sym", "k_reduce_partial+k_params_int_final",
+           lambda: fq.fq_tensor_params_int(x, n, 8, fq.SYM, ws, wsb, params, flags), 4 * n + 16),
+        Op("tensor.fake_quant_int8", "k_fq_int_tensor",
+           lambda: fq.fq_fake_quant_int_tensor(x, n, 8, fq.SYM, params, codes, fqo), 4 * n + n + 4 * n),
+        Op("tensor.ste_backward", "k_ste", lambda: fq.fq_ste_backward(g, n, x, n, bounds, gin), 12 * n),
+    ]
+
+
+def op_rows_f32(fq, torch, w, r, c, bits, scheme, sname, dev):
+    cb = r * c if bits == 8 else r * ((c + 1) // 2)
+    codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    fqo = torch.empty(r * c, dtype=torch.float32, device=dev)
+    sc = torch.empty(r, dtype=torch.float32, device=dev)
+    zp = torch.empty(r, dtype=torch.int32, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    return Op(f"rows_f32.int{bits}_{sname}", "k_quant_rows",
+              lambda: fq.fq_quant_rows(w, fq.F32, r, c, bits, scheme, codes, fqo, sc, zp, fl),
+              4 * r * c + cb + 4 * r * c + 8 * r)
+
+
+def ops_rows_f32(fq, syn, torch, dev):
+    r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
+    w = syn.rows_f32_inputs(r, c, device=dev)
+    return [op_rows_f32(fq, torch, w, r, c, bits, scheme, sname, dev)
+            for bits in (8, 4) for scheme, sname in ((fq.SYM, "sym"), (fq.AFFINE, "affine"))]
+
+
+def ops_fp8_format(fq, torch, x, n, scales, fmt, fname, dev):
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    fqo = torch.empty(n, dtype=torch.float32, device=dev)
+    deq = torch.empty(n, dtype=torch.float32, device=dev)
+    s = scales[fmt:fmt + 1]
+    return [Op(f"fp8.quantize_{fname}", "k_fp8_quant", lambda: fq.fq_fp8_quantize(x, n, fmt, s, q, fqo),
+               4 * n + n + 4 * n),
+            Op(f"fp8.dequantize_{fname}", "k_fp8_dequant", lambda: fq.fq_fp8_dequantize(q, n, fmt, s, deq),
+               n + 4 * n)]
+
+
+def ops_fp8(fq, syn, torch, dev):
+    n = syn.FULL["fp8"]["n"]
+    x = syn.fp8_inputs(n, device=dev)
+    wsb = fq.fq_workspace_bytes(n)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    scales = torch.empty(2, dtype=torch.float32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ops = [Op("fp8.tensor_scale", "k_reduce_partial+k_fp8_scale_final",
+              lambda: fq.fq_fp8_tensor_scale(x, n, ws, wsb, scales[0:1], scales[1:2], flags), 4 * n + 8)]
+    for fmt, fname in ((fq.E4M3, "e4m3"), (fq.E5M2, "e5m2")):
+        ops += ops_fp8_format(fq, torch, x, n, scales, fmt, fname, dev)
+    return ops
+
+
+def ops_q4dq(fq, syn, torch, dev):
+    n = syn.FULL["q4dq"]["n"]
+    x = syn.q4dq_inputs(n, device=dev)
+    npk, nb, ns = fq.fq_q4dq_sizes(n)
+    packed = torch.empty(npk, dtype=torch.uint8, device=dev)
+    qs = torch.empty(nb, dtype=torch.uint8, device=dev)
+    sup = torch.empty(ns, dtype=torch.float32, device=dev)
+    recon = torch.empty(n, dtype=torch.float32, device=dev)
+    deq = torch.empty(n, dtype=torch.float32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    return [
+        Op("q4dq.quantize_recon", "k_q4dq_full",
+           lambda: fq.fq_q4dq_quantize(x, n, packed, qs, sup, None, recon, flags),
+           4 * n + npk + nb + 4 * ns + 4 * n),
+        Op("q4dq.dequantize", "k_q4dq_dequant",
+           lambda: fq.fq_q4dq_dequantize(packed, qs, sup, n, deq), npk + nb + 4 * ns + 4 * n),
+    ]
+
+
+def ops_rows_bf16(fq, syn, torch, dev):
+    r, c = syn.FULL["rows_bf16"]["rows"], syn.FULL["rows_bf16"]["cols"]
+    a = syn.rows_bf16_inputs(r, c, device=dev)
+    codes = torch.empty(r * c, dtype=torch.int8, device=dev)
+    sc = torch.empty(r, dtype=torch.float32, device=dev)
+    zp = torch.empty(r, dtype=torch.int32, device=dev)
+    fl = torch.zeros(1, dtype=torch.int32, device=dev)
+    q = torch.empty(r * c, dtype=torch.uint8, device=dev)
+    e8 = torch.empty(r * ((c + 31) // 32), dtype=torch.uint8, device=dev)
+    return [
+        Op("rows_bf16.int8_affine", "k_quant_rows",
+           lambda: fq.fq_quant_rows(a, fq.BF16, r, c, 8, fq.AFFINE, codes, None, sc, zp, fl),
+           2 * r * c + r * c + 8 * r),
+        Op("rows_bf16.mxfp8_e4m3", "k_mx_vec",
+           lambda: fq.fq_mxfp8_rows(a, fq.BF16, r, c, q, e8, None), 2 * r * c + r * c + r * c // 32),
+    ]
+
+
+WORKLOADS = {"tensor": ops_tensor, "rows_f32": ops_rows_f32, "fp8": ops_fp8, "q4dq": ops_q4dq,
+             "rows_bf16": ops_rows_bf16}
+
+
+def build_ops(fq, syn, torch, only, dev="cuda"):
+    """Draw inputs and allocate outputs on the GPU, one workload per function (each
+    op's closure owns that workload's buffers); return the timed ops."""
+    ops = []
+    for name, make in WORKLOADS.items():
+        if only is None or name in only:
+            ops += make(fq, syn, torch, dev)
+    return ops
+
+
+def cpu_baseline(orc, syn, torch, only):
+    """The oracle, single-threaded, on a bounded sample of every workload."""
+    import numpy as np
+    dev = "cuda"
+    total_bytes, total_s = 0, 0.0
+    parts = []
+
+    def timed(fn, nbytes):
+        nonlocal total_bytes, total_s
+        t0 = time.perf_counter()
+        fn()
+        total_s += time.perf_counter() - t0
+        total_bytes += nbytes
+
+    def want(w):
+        return only is None or w in only
+
+    if want("tensor"):
+        n = syn.FULL["tensor"]["n"]
+        x, g = (t.cpu().numpy() for t in syn.tensor_inputs(n, device=dev))
+        p = {}
+        timed(lambda: p.update(orc.tensor_params_int(x, 8, orc.SYM)), 4 * n)
+        timed(lambda: orc.fake_quant_int(x, 8, orc.SYM, float(p["scale"]), p["zp"]), 9 * n)
+        timed(lambda: orc.ste_backward(g, x, float(p["lo"]), float(p["hi"])), 12 * n)
+        parts.append("tensor: all 2^20")
+    if want("rows_f32"):
+        r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
+        rs = r // 4
+        w = syn.rows_f32_inputs(r, c, device=dev)[:rs].cpu().numpy()
+        for bits in (8, 4):
+            for scheme in (orc.SYM, orc.AFFINE):
+                cb = rs * c if bits == 8 else rs * ((c + 1) // 2)
+                timed(lambda bits=bits, scheme=scheme: orc.quant_rows(w, bits, scheme), 8 * rs * c + cb + 8 * rs)
+        parts.append(f"rows_f32: {rs} of {r} rows")
+    if want("fp8"):
+        n = syn.FULL["fp8"]["n"]
+        m = n // 4
+        x = syn.fp8_inputs(n, device=dev)[:m].cpu().numpy()
+        amax = [0.0]
+        timed(lambda: amax.__setitem__(0, orc.amax_finite(x)), 4 * m)
+        for fmt in (orc.E4M3, orc.E5M2):
+            s, _ = orc.fp8_scale(float(amax[0]), fmt)
+            qq = {}
+            timed(lambda fmt=fmt, s=s: qq.update(q=orc.fp8_quantize(x, fmt, float(s))[0]), 9 * m)
+            timed(lambda fmt=fmt, s=s: orc.fp8_dequantize(qq["q"], fmt, float(s)), 5 * m)
+        parts.append(f"fp8: first {m} of {n} elements")
+    if want("q4dq"):
+        n = syn.FULL["q4dq"]["n"]
+        m = n // 4
+        x = syn.q4dq_inputs(n, device=dev)[:m].cpu().numpy()
+        res = {}
+        npk, nb, ns = (m + 1) // 2, (m + 63) // 64, (m + 16383) // 16384
+        timed(lambda: res.update(orc.q4dq_quantize(x, want_block_scale=False)), 4 * m + npk + nb + 4 * ns + 4 * m)
+        timed(lambda: orc.q4dq_dequantize(res["packed"], res["qscale"], res["super"], m), npk + nb + 4 * ns + 4 * m)
+        del x, res
+        parts.append(f"q4dq: first {m} of {n} elements")
+    if want("rows_bf16"):
+        r, c = syn.FULL["rows_bf16"]["rows"], syn.FULL["rows_bf16"]["cols"]
+        rs = r // 4
+        a = syn.bf16_bits(syn.rows_bf16_inputs(r, c, device=dev)[:rs])
+        timed(lambda: orc.quant_rows(a, 8, orc.AFFINE, dtype=orc.BF16, want_fq=False), 3 * rs * c + 8 * rs)
+        timed(lambda: orc.mxfp8_rows(a, dtype=orc.BF16, want_fq=False), 3 * rs * c + rs * c // 32)
+        parts.append(f"rows_bf16: {rs} of {r} rows")
+    return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample="; ".join(parts) + f" (single-threaded, {total_s:.1f} s of CPU work)",
+                seconds=round(total_s, 3))
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != sources_sha():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def sources_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fake_quant_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from fake_quant_amd import fq
+    from fake_quant_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    log("drawing inputs and allocating outputs")
+    ops = build_ops(fq, syn, torch, args.only)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    log(f"{len(ops)} ops per step; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        for op in ops:
+            op.fn()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, op in enumerate(ops):
+            op.fn()
+            ev[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    per_op_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+                 for i in range(len(ops))]
+    step_bytes = sum(op.nbytes for op in ops)
+    ms_step = total_ms / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    kernels = {}
+    for op, ms in zip(ops, per_op_ms):
+        gbs = op.nbytes / (ms * 1e-3) / 1e9
+        kernels[op.name] = dict(kernel=op.kernel, bytes=op.nbytes, us=round(ms * 1e3, 2), gbs=round(gbs, 1),
+                                frac=round(gbs / HBM_PEAK_GBS, 4))
+    dom_i = max(range(len(ops)), key=lambda i: per_op_ms[i])
+    dom = ops[dom_i]
+    achieved = dom.nbytes / (per_op_ms[dom_i] * 1e-3) / 1e9
+    roofline = dict(bound="hbm", kernel=dom.kernel, op=dom.name, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_record(dom.kernel),
+                    avg_launch_us=round(per_op_ms[dom_i] * 1e3, 2), bytes_per_launch=dom.nbytes)
+
+    cpu = None
+    if not args.no_cpu:
+        from oracle import oracle as orc
+        log("timing the CPU oracle on a bounded sample")
+        del ops
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(orc, syn, torch, args.only)
+
+    workloads = "tensor 2^20 f32 int8 + STE; rows_f32 [4096,4096] int8/int4 sym/affine; fp8 2^26 E4M3/E5M2; " \
+                "q4dq 2^30 f32 4-bit + double-quant; rows_bf16 [16384,8192] per-token int8 + 32-block E4M3/E8M0"
+    if args.only:
+        workloads = "only " + ",".join(args.only)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": workloads, "bytes_per_step": step_bytes, "ops_per_step": len(ops),
+                   "wall_s_timed": round(t_wall, 3)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

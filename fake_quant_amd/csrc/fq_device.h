@@ -1,0 +1,315 @@
+// fq_device.h -- device-side building blocks shared by the gfx950 kernels:
+// exact binary32 quotients with a fixed divisor, the saturating fp8 codec,
+// bfloat16 widening, wave64 DPP reductions and the scale rules of the pages.
+//
+// Sources (page title, section):
+//   [QAT] optirs-gpu 0.3.2 src/optirs_gpu/quantization.rs, "Quantization-Aware
+//         Training (QAT) primitives": module docs (integer grid, fp8 table,
+//         unified ULP rule), QuantParams::{from_minmax, from_absmax}.
+//   [DQ]  aprender-train 0.32.0 entrenar/quant/double_quant.rs.
+//   [CS]  CS349E 05_quantization_basics.py demo 4, `block_scaled` "e8m0".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fqk {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------------------
+// Exact quotient fl(x / s) for a divisor fixed per group.
+//
+// Every code the method produces is a function of the binary32 quotient x/s, so
+// the division must be correctly rounded; a multiply by a reciprocal is not.
+// With y = RN(1/s) (one true division per group) the quotient is refined by two
+// Markstein corrections (P. Markstein, IBM J. Res. Dev. 34(1), 1990):
+//   q0 = RN(x y); r0 = x - s q0 (fma); q1 = RN(q0 + r0 y);
+//   r1 = x - s q1 (fma);  q2 = RN(q1 + r1 y).
+// q1 is within one ulp of x/s, r1 is exact and y is within half an ulp of 1/s, so
+// q2 = RN(x/s) whenever no intermediate overflows or underflows.  The group is
+// admitted to this path only for 2^-60 <= s <= 2^60; then
+//   * |x/s| in the normal range: q2 == x / s bit for bit;
+//   * tiny x: the residuals may round, but then |x/s| < 2^-17, below half the
+//     smallest fp8 subnormal and below every integer rounding threshold, and q2
+//     stays in that range -- every code taken from it is the same;
+//   * x = +-Inf, NaN, or x*y overflowing: q2 is NaN, and x*y (+-Inf, NaN or a huge
+//     finite value) carries the same code (saturation / NaN).
+// The corrections add +0 to -0 when x is a zero, so the sign of x (the sign of
+// x/s, as s > 0) is put back on the result.
+// Other divisors take the compiler's correctly rounded division.
+// ---------------------------------------------------------------------------
+struct ExactDiv {
+    float s, y;
+    bool fast;
+    __device__ __forceinline__ explicit ExactDiv(float s_) : s(s_) {
+        y = 1.0f / s_;
+        fast = (s_ >= 0x1p-60f) && (s_ <= 0x1p60f);
+    }
+    // Markstein path only; valid when `fast`.
+    __device__ __forceinline__ float quick(float x) const {
+        float q = x * y;
+        float r = __builtin_fmaf(-s, q, x);
+        q = __builtin_fmaf(r, y, q);
+        r = __builtin_fmaf(-s, q, x);
+        q = __builtin_fmaf(r, y, q);
+        return (q != q) ? x * y : __builtin_copysignf(q, x);
+    }
+    __device__ __forceinline__ float operator()(float x) const { return fast ? quick(x) : x / s; }
+};
+
+// ---------------------------------------------------------------------------
+// bfloat16 -> binary32 (exact: bf16 is the upper half of a binary32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return as_f(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return as_f(pair & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// wave64 reductions.  DPP row operations stay inside 16-lane rows; the two
+// cross-row steps use lane shuffles.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return as_f(dpp_u<CTRL>(as_u(v)));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kMirror = 0x140;      // lane i <-> 15-i within 16
+
+// max over each 4-lane quad, result in every lane of the quad
+__device__ __forceinline__ uint32_t quad_max_u(uint32_t v) {
+    v = max(v, dpp_u<kQuadXor1>(v));
+    v = max(v, dpp_u<kQuadXor2>(v));
+    return v;
+}
+// max over each 16-lane row, result in every lane of the row
+__device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
+    v = quad_max_u(v);
+    v = max(v, dpp_u<kHalfMirror>(v));
+    v = max(v, dpp_u<kMirror>(v));
+    return v;
+}
+__device__ __forceinline__ float row16_min_f(float v) {
+    v = fminf(v, dpp_f<kQuadXor1>(v));
+    v = fminf(v, dpp_f<kQuadXor2>(v));
+    v = fminf(v, dpp_f<kHalfMirror>(v));
+    v = fminf(v, dpp_f<kMirror>(v));
+    return v;
+}
+__device__ __forceinline__ float row16_max_f(float v) {
+    v = fmaxf(v, dpp_f<kQuadXor1>(v));
+    v = fmaxf(v, dpp_f<kQuadXor2>(v));
+    v = fmaxf(v, dpp_f<kHalfMirror>(v));
+    v = fmaxf(v, dpp_f<kMirror>(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+    v = row16_max_u(v);
+    v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+    v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+__device__ __forceinline__ float wave_min_f(float v) {
+    v = row16_min_f(v);
+    v = fminf(v, __shfl_xor(v, 16));
+    v = fminf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+    v = row16_max_f(v);
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Finite min / max / non-finite accumulation over binary32 values.
+// `nf` collects max(|x| bits): it reaches 0x7F800000 iff an Inf or NaN was seen.
+// ---------------------------------------------------------------------------
+struct MinMax {
+    float mn = __builtin_inff();
+    float mx = -__builtin_inff();
+    uint32_t nf = 0;
+    __device__ __forceinline__ void add(float v) {
+        uint32_t a = as_u(v) & 0x7FFFFFFFu;
+        bool fin = a < 0x7F800000u;
+        mn = fin ? fminf(mn, v) : mn;
+        mx = fin ? fmaxf(mx, v) : mx;
+        nf = max(nf, a);
+    }
+    __device__ __forceinline__ void merge(float omn, float omx, uint32_t onf) {
+        mn = fminf(mn, omn);
+        mx = fmaxf(mx, omx);
+        nf = max(nf, onf);
+    }
+    __device__ __forceinline__ bool nonfinite() const { return nf >= 0x7F800000u; }
+};
+
+// ---------------------------------------------------------------------------
+// Integer calibration ([QAT] QuantParams::from_minmax / from_absmax), binary32.
+// ---------------------------------------------------------------------------
+struct IntRange {
+    int qmin, qmax;
+};
+__device__ __forceinline__ IntRange int_range(int bits, bool affine) {
+    // [QAT] IntDtype::q_range: restricted symmetric, full-range affine
+    if (bits == 8) return affine ? IntRange{-128, 127} : IntRange{-127, 127};
+    return affine ? IntRange{-8, 7} : IntRange{-7, 7};
+}
+
+struct IntCal {
+    float scale;
+    int zp;
+    bool degenerate;
+};
+
+// (min, max) over the finite elements; a group without finite elements arrives
+// as (+inf, -inf) and is degenerate.
+__device__ __forceinline__ IntCal calibrate(float mn, float mx, IntRange r, bool affine) {
+    IntCal c{0.0f, 0, true};
+    if (!(mn <= mx)) return c;  // no finite element
+    if (!affine) {
+        float absmax = fmaxf(fabsf(mn), fabsf(mx));
+        if (!(absmax > 0.0f)) return c;
+        float s = absmax / (float)r.qmax;
+        if (!(s > 0.0f) || !(s < __builtin_inff())) return c;
+        c.scale = s;
+        c.degenerate = false;
+        return c;
+    }
+    float rmin = fminf(mn, 0.0f);
+    float rmax = fmaxf(mx, 0.0f);
+    float range = rmax - rmin;
+    if (!(range > 0.0f)) return c;
+    float s = range / (float)(r.qmax - r.qmin);
+    if (!(s > 0.0f) || !(s < __builtin_inff())) return c;
+    float z = rintf((float)r.qmin - rmin / s);
+    z = fminf(fmaxf(z, (float)r.qmin), (float)r.qmax);
+    c.scale = s;
+    c.zp = (int)z;
+    c.degenerate = false;
+    return c;
+}
+
+// Quantize helper for one group: offset = clamp(RNE(x/s), qmin - zp, qmax - zp),
+// code = offset + zp.  NaN -> code 0 (offset -zp); scale 0 -> code 0.
+struct IntQ {
+    ExactDiv div;
+    float lo, hi;   // qmin - zp, qmax - zp as floats
+    float nan_off;  // -zp
+    bool zero;      // scale == 0
+    __device__ __forceinline__ IntQ(float scale, int zp, IntRange r)
+        : div(scale == 0.0f ? 1.0f : scale),
+          lo((float)(r.qmin - zp)),
+          hi((float)(r.qmax - zp)),
+          nan_off((float)(-zp)),
+          zero(scale == 0.0f) {}
+    // offset q - zp as an exact small integer in a float (a zero offset is +0,
+    // as the integer difference q - zp converts to +0)
+    __device__ __forceinline__ float offset(float x) const {
+        if (zero) return nan_off;  // code 0 (zp is 0 for degenerate groups)
+        float t = div(x);
+        float r = fminf(fmaxf(rintf(t), lo), hi) + 0.0f;
+        return (t != t) ? nan_off : r;
+    }
+    // offset for a group whose divisor passed the fast test and whose inputs are
+    // known finite with |x / s| bounded by the group's own range
+    __device__ __forceinline__ float offset_finite(float x) const {
+        float t = div.quick(x);
+        return fminf(fmaxf(rintf(t), lo), hi) + 0.0f;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// fp8 codec.  [QAT] module docs "fp8 quantization": E4M3 (3 mantissa bits, bias
+// 7, max 448, no Inf, NaN S.1111.111) and E5M2 (2 mantissa bits, bias 15, max
+// 57344, IEEE-like).  Rounding is the page's unified ULP rule: for a > 0 with
+// e = floor(log2 a), step = 2^(max(e, emin) - mbits), ties to even, then a
+// rounded magnitude above max saturates to max; +-Inf saturate; NaN -> 0x7F.
+//
+// Encoding arithmetic (bitwise emulation): with E the biased binary32 exponent
+// of a, clamped below at emin, k = RNE(a * 2^(mbits - e)) is the rounded
+// significand on the step grid (k in [2^mbits, 2^(mbits+1)] in a normal binade,
+// [0, 2^mbits] below emin), and the fp8 code is k + ((e + bias - 1) << mbits):
+// the carry k = 2^(mbits+1) moves into the next binade by itself, and the
+// subnormal codes are k themselves.  Codes above the largest finite code are
+// clamped to it.
+// ---------------------------------------------------------------------------
+template <int FMT>
+struct Fp8Fmt;
+template <>
+struct Fp8Fmt<0> {  // E4M3
+    static constexpr int mbits = 3, bias = 7;
+    static constexpr uint32_t max_code = 0x7E;
+    static constexpr float big = 0x1p10f;  // anything >= this saturates
+    static constexpr float rebias = 0x1p120f;  // 2^(127 - bias)
+};
+template <>
+struct Fp8Fmt<1> {  // E5M2
+    static constexpr int mbits = 2, bias = 15;
+    static constexpr uint32_t max_code = 0x7B;
+    static constexpr float big = 0x1p17f;
+    static constexpr float rebias = 0x1p112f;
+};
+
+// |y| -> 7-bit magnitude code (finite or Inf input; NaN handled by the caller)
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_mag_code(float y) {
+    using F = Fp8Fmt<FMT>;
+    constexpr uint32_t emin_biased = 127u + 1u - F::bias;  // binary32 field of 2^emin
+    float a = fminf(fabsf(y), F::big);
+    uint32_t E = max(as_u(a) >> 23, emin_biased);
+    float k = rintf(__builtin_amdgcn_ldexpf(a, (int)(127u + F::mbits) - (int)E));
+    uint32_t code = (uint32_t)k + ((E - emin_biased) << F::mbits);
+    return min(code, F::max_code);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_encode(float y) {
+    uint32_t code = fp8_mag_code<FMT>(y) | ((as_u(y) >> 24) & 0x80u);
+    return (y != y) ? 0x7Fu : code;
+}
+
+// Value of a code that is not NaN and not Inf: the 7 magnitude bits placed under
+// the binary32 exponent field give 2^(E-127) (1 + M/2^mb) (or a binary32
+// subnormal for E = 0); multiplying by 2^(127 - bias) rebiases exactly.
+template <int FMT>
+__device__ __forceinline__ float fp8_decode_finite(uint32_t b) {
+    using F = Fp8Fmt<FMT>;
+    float v = as_f((b & 0x7Fu) << (23 - F::mbits)) * F::rebias;
+    return as_f(as_u(v) | ((b & 0x80u) << 24));
+}
+
+// Value of any code (NaN patterns -> NaN, E5M2 infinities -> +-Inf)
+template <int FMT>
+__device__ __forceinline__ float fp8_decode(uint32_t b) {
+    float v = fp8_decode_finite<FMT>(b);
+    uint32_t m = b & 0x7Fu;
+    if (FMT == 0) return m == 0x7Fu ? __builtin_nanf("") : v;
+    if (m >= 0x7Cu) {
+        float inf = as_f(0x7F800000u | ((b & 0x80u) << 24));
+        return m == 0x7Cu ? inf : __builtin_nanf("");
+    }
+    return v;
+}
+
+// pack the low bytes of four words into one word (little-endian order)
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
+    return lo | hi;
+}
+// two 4-bit codes (as ints) -> one byte, first one in the high nibble
+__device__ __forceinline__ uint32_t nib2(int c0, int c1) {
+    return (((uint32_t)c0 & 0xFu) << 4) | ((uint32_t)c1 & 0xFu);
+}
+
+}  // namespace fqk

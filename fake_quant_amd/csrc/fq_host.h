@@ -1,0 +1,46 @@
+// fq_host.h -- host-side helpers of the C ABI: argument checks, launch geometry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fq.h"
+
+namespace fqh {
+
+constexpr int kBlock = 256;  // threads per workgroup (four wave64)
+
+inline bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
+
+inline bool valid_bits(int bits) { return bits == 4 || bits == 8; }
+inline bool valid_scheme(int s) { return s == FQ_SYM || s == FQ_AFFINE; }
+inline bool valid_fmt(int f) { return f == FQ_E4M3 || f == FQ_E5M2; }
+inline bool valid_dtype(int d) { return d == FQ_F32 || d == FQ_BF16; }
+
+// Compute units of the current device (cached per device id).
+int num_cus();
+
+// Status of the launch(es) just enqueued.
+inline int launched() { return hipGetLastError() == hipSuccess ? FQ_OK : FQ_E_HIP; }
+
+// Blocks for a grid-stride loop over `items` work items, `per_block` items per
+// block per pass, at most `waves_per_cu` resident blocks per compute unit.
+inline unsigned grid_for(int64_t items, int64_t per_block, int blocks_per_cu) {
+    int64_t want = (items + per_block - 1) / per_block;
+    int64_t cap = (int64_t)num_cus() * blocks_per_cu;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    return (unsigned)want;
+}
+
+// Blocks of the tensor-scope reduction (partials in the workspace).
+constexpr int kMaxReduceBlocks = 2048;
+inline unsigned reduce_blocks(int64_t n) {
+    int64_t chunks = (n + 3) / 4;
+    int64_t want = (chunks + 4 * kBlock - 1) / (4 * kBlock);
+    if (want > kMaxReduceBlocks) want = kMaxReduceBlocks;
+    if (want < 1) want = 1;
+    return (unsigned)want;
+}
+
+}  // namespace fqh

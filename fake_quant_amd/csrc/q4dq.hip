@@ -1,0 +1,263 @@
+// q4dq.hip -- 64-element 4-bit absmax blocks with 8-bit double quantization of
+// the block scales over groups of 256 blocks, and its dequantization.
+//
+// [DQ] aprender-train 0.32.0 entrenar/quant/double_quant.rs, "Double
+// quantization for QLoRA": quantize_4bit_double (super-scale = max of 256 block
+// scales with a 1e-8 floor, u8 = round(scale / super * 255)), dequantize_4bit_double
+// and reconstruct_scales (scale = u8 / 255 * super; nibble order: element i in byte
+// i/2, even i in the high nibble, two's complement).  The first-level quantizer
+// (imported by the page): blocks of 64, scale = absmax / 7, ties to even.
+//
+// One workgroup (256 threads) owns a super-block of 256 blocks = 16384 elements =
+// 64 KiB of input.  Thread t loads float4 number j*256 + t for j = 0..15, so each
+// 64-element block is one 16-lane DPP row of a wave; the block absmax is a 4-step
+// row reduction.  The whole super-block stays in registers: codes are written at
+// once, the super-scale comes from a wave + LDS maximum, and the reconstruction
+// is written from the codes kept in registers -- the input is read once.
+#include "fq_device.h"
+#include "fq_host.h"
+
+using namespace fqk;
+
+namespace {
+
+constexpr int kB = fqh::kBlock;
+constexpr int kWaves = kB / kWave;
+constexpr int kBlockElems = 64;
+constexpr int kGroup = 256;                         // block scales per super-scale
+constexpr int kSuperElems = kBlockElems * kGroup;   // 16384
+constexpr int kJ = kSuperElems / (4 * kB);          // 16 float4 per thread
+
+// code of x in a block with scale s (s > 0): clamp(RNE(x / s), -7, 7), NaN -> 0
+__device__ __forceinline__ float q4_code(const ExactDiv& d, float x) {
+    float t = d(x);
+    float r = fminf(fmaxf(rintf(t), -7.0f), 7.0f) + 0.0f;  // code 0 is +0
+    return (t != t) ? 0.0f : r;
+}
+
+// [DQ] u8 scale code: clamp(round_half_away(s / S * 255), 0, 255)
+__device__ __forceinline__ uint32_t u8_scale(float s, float S) {
+    float v = (s / S) * 255.0f;
+    v = roundf(v);
+    v = fminf(fmaxf(v, 0.0f), 255.0f);
+    return (uint32_t)v;
+}
+// [DQ] reconstruct_scales: q / 255 * super, left to right
+__device__ __forceinline__ float recon_scale(uint32_t u, float S) { return (float)u / 255.0f * S; }
+
+// Full super-block, 16-byte aligned buffers.
+__global__ __launch_bounds__(kB) void k_q4dq_full(const float* __restrict__ x, uint8_t* __restrict__ packed,
+                                                  uint8_t* __restrict__ qscale, float* __restrict__ super_scale,
+                                                  float* __restrict__ block_scale, float* __restrict__ recon,
+                                                  uint32_t* __restrict__ flags) {
+    const int64_t sb = blockIdx.x;
+    const int t = threadIdx.x;
+    const float4* xv = reinterpret_cast<const float4*>(x + sb * kSuperElems);
+    float4 v[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) v[j] = xv[j * kB + t];
+
+    __shared__ float s_scale[kGroup];
+    __shared__ uint32_t s_u8[kGroup / 4];
+    __shared__ float s_max[kWaves];
+
+    float smax = 0.0f;
+    uint32_t nf = 0;
+    float sblk[kJ];
+    uint16_t* pk = reinterpret_cast<uint16_t*>(packed + sb * (kSuperElems / 2));
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+        uint32_t a0 = as_u(v[j].x) & 0x7FFFFFFFu, a1 = as_u(v[j].y) & 0x7FFFFFFFu;
+        uint32_t a2 = as_u(v[j].z) & 0x7FFFFFFFu, a3 = as_u(v[j].w) & 0x7FFFFFFFu;
+        nf = max(nf, max(max(a0, a1), max(a2, a3)));
+        uint32_t am = max(max(a0 < 0x7F800000u ? a0 : 0u, a1 < 0x7F800000u ? a1 : 0u),
+                          max(a2 < 0x7F800000u ? a2 : 0u, a3 < 0x7F800000u ? a3 : 0u));
+        am = row16_max_u(am);
+        float s = as_f(am) / 7.0f;
+        sblk[j] = s;
+        smax = fmaxf(smax, s);
+        float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+        if (s != 0.0f) {
+            ExactDiv d(s);
+            c0 = q4_code(d, v[j].x);
+            c1 = q4_code(d, v[j].y);
+            c2 = q4_code(d, v[j].z);
+            c3 = q4_code(d, v[j].w);
+        }
+        pk[j * kB + t] = (uint16_t)(nib2((int)c0, (int)c1) | (nib2((int)c2, (int)c3) << 8));
+        v[j] = make_float4(c0, c1, c2, c3);  // keep the codes for the reconstruction
+        if ((t & 15) == 0) s_scale[j * 16 + (t >> 4)] = s;
+    }
+    // super-scale: max over the 256 block scales, floored at 1e-8
+    smax = fmaxf(smax, __shfl_xor(smax, 16));
+    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    nf = wave_max_u(nf);
+    if ((t & 63) == 0) s_max[t >> 6] = smax;
+    if (flags && (t & 63) == 0 && nf >= 0x7F800000u) atomicOr(flags, FQ_FLAG_NONFINITE);
+    __syncthreads();
+    float S = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    S = fmaxf(S, 1e-8f);
+    if (t == 0) super_scale[sb] = S;
+    if (block_scale) block_scale[sb * kGroup + t] = s_scale[t];
+    {
+        // u8 scale codes: thread t encodes block t, four per word
+        uint32_t u = u8_scale(s_scale[t], S);
+        uint32_t u1 = __shfl_down(u, 1), u2 = __shfl_down(u, 2), u3 = __shfl_down(u, 3);
+        if ((t & 3) == 0) s_u8[t >> 2] = u | (u1 << 8) | (u2 << 16) | (u3 << 24);
+    }
+    __syncthreads();
+    if (t < kGroup / 4) reinterpret_cast<uint32_t*>(qscale + sb * kGroup)[t] = s_u8[t];
+    if (!recon) return;
+    float4* rv = reinterpret_cast<float4*>(recon + sb * kSuperElems);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+        uint32_t u = u8_scale(sblk[j], S);
+        float sh = recon_scale(u, S);
+        rv[j * kB + t] = make_float4(v[j].x * sh, v[j].y * sh, v[j].z * sh, v[j].w * sh);
+    }
+}
+
+// Any super-block (partial, unaligned): element-wise, one thread per element
+// slot, same block structure (4 elements per lane, 16 lanes per block).
+__global__ __launch_bounds__(kB) void k_q4dq_any(const float* __restrict__ x, int64_t n, int64_t sb0,
+                                                 uint8_t* __restrict__ packed, uint8_t* __restrict__ qscale,
+                                                 float* __restrict__ super_scale,
+                                                 float* __restrict__ block_scale,
+                                                 float* __restrict__ recon, uint32_t* __restrict__ flags) {
+    const int64_t sb = sb0 + blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t base = sb * kSuperElems;
+    __shared__ float s_scale[kGroup];
+    __shared__ float s_max[kWaves];
+    float smax = 0.0f;
+    uint32_t nf = 0;
+    float code[kJ][4];
+    float sblk[kJ];
+    for (int j = 0; j < kJ; ++j) {
+        const int64_t e0 = base + 4 * ((int64_t)j * kB + t);
+        float xe[4];
+        uint32_t am = 0;
+        for (int e = 0; e < 4; ++e) {
+            xe[e] = (e0 + e < n) ? x[e0 + e] : 0.0f;
+            uint32_t a = as_u(xe[e]) & 0x7FFFFFFFu;
+            nf = max(nf, a);
+            am = max(am, a < 0x7F800000u ? a : 0u);
+        }
+        am = row16_max_u(am);
+        float s = as_f(am) / 7.0f;
+        sblk[j] = s;
+        smax = fmaxf(smax, s);
+        ExactDiv d(s == 0.0f ? 1.0f : s);
+        for (int e = 0; e < 4; ++e) code[j][e] = (s != 0.0f) ? q4_code(d, xe[e]) : 0.0f;
+        for (int e = 0; e < 4; e += 2) {
+            int64_t i = e0 + e;
+            if (i < n) packed[i >> 1] = (uint8_t)nib2((int)code[j][e], (i + 1 < n) ? (int)code[j][e + 1] : 0);
+        }
+        if ((t & 15) == 0) s_scale[j * 16 + (t >> 4)] = s;
+    }
+    smax = fmaxf(smax, __shfl_xor(smax, 16));
+    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    nf = wave_max_u(nf);
+    if ((t & 63) == 0) s_max[t >> 6] = smax;
+    if (flags && (t & 63) == 0 && nf >= 0x7F800000u) atomicOr(flags, FQ_FLAG_NONFINITE);
+    __syncthreads();
+    float S = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    S = fmaxf(S, 1e-8f);
+    const int64_t nb = (n + kBlockElems - 1) / kBlockElems;
+    if (t == 0) super_scale[sb] = S;
+    const int64_t b = sb * kGroup + t;
+    if (b < nb) {
+        qscale[b] = (uint8_t)u8_scale(s_scale[t], S);
+        if (block_scale) block_scale[b] = s_scale[t];
+    }
+    if (!recon) return;
+    for (int j = 0; j < kJ; ++j) {
+        const int64_t e0 = base + 4 * ((int64_t)j * kB + t);
+        float sh = recon_scale(u8_scale(sblk[j], S), S);
+        for (int e = 0; e < 4; ++e)
+            if (e0 + e < n) recon[e0 + e] = code[j][e] * sh;
+    }
+}
+
+// [DQ] dequantize_4bit_double: one workgroup per super-block.
+template <bool FULL>
+__global__ __launch_bounds__(kB) void k_q4dq_dequant(const uint8_t* __restrict__ packed,
+                                                     const uint8_t* __restrict__ qscale,
+                                                     const float* __restrict__ super_scale, int64_t n,
+                                                     int64_t sb0, float* __restrict__ out) {
+    const int64_t sb = sb0 + blockIdx.x;
+    const int t = threadIdx.x;
+    const float S = super_scale[sb];
+    const int64_t base = sb * kSuperElems;
+    const int64_t nb = (n + kBlockElems - 1) / kBlockElems;
+#pragma unroll 4
+    for (int j = 0; j < kJ; ++j) {
+        const int64_t b = sb * kGroup + j * 16 + (t >> 4);
+        const int64_t e0 = base + 4 * ((int64_t)j * kB + t);
+        if (!FULL && b >= nb) continue;
+        const float sh = recon_scale(qscale[b], S);
+        if (FULL) {
+            uint32_t w = reinterpret_cast<const uint16_t*>(packed + base / 2)[j * kB + t];
+            float c0 = (float)(((int)(w << 24)) >> 28), c1 = (float)(((int)(w << 28)) >> 28);
+            float c2 = (float)(((int)(w << 16)) >> 28), c3 = (float)(((int)(w << 20)) >> 28);
+            reinterpret_cast<float4*>(out + base)[j * kB + t] = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+        } else {
+            for (int e = 0; e < 4; ++e) {
+                int64_t i = e0 + e;
+                if (i >= n) break;
+                uint32_t byte = packed[i >> 1];
+                uint32_t nib = (i & 1) ? (byte & 0xFu) : (byte >> 4);
+                out[i] = (float)(((int)(nib << 28)) >> 28) * sh;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fq_q4dq_quantize(const float* x, int64_t n, uint8_t* packed, uint8_t* qscale,
+                     float* super_scale, float* block_scale, float* recon, uint32_t* flags,
+                     hipStream_t stream) {
+    if (!x || n < 1 || !packed || !qscale || !super_scale) return FQ_E_INVALID;
+    if (!fqh::aligned(x, 4) || !fqh::aligned(super_scale, 4) || !fqh::aligned(block_scale, 4) ||
+        !fqh::aligned(recon, 4) || !fqh::aligned(flags, 4))
+        return FQ_E_INVALID;
+    const int64_t nsb = (n + kSuperElems - 1) / kSuperElems;
+    const int64_t nfull = n / kSuperElems;
+    if (nsb > 0x7FFFFFFF) return FQ_E_INVALID;
+    const bool al = fqh::aligned(x, 16) && fqh::aligned(packed, 2) && fqh::aligned(qscale, 4) &&
+                    fqh::aligned(recon, 16);
+    int64_t done = 0;
+    if (al && nfull > 0) {
+        k_q4dq_full<<<(unsigned)nfull, kB, 0, stream>>>(x, packed, qscale, super_scale, block_scale, recon,
+                                                       flags);
+        done = nfull;
+    }
+    if (done < nsb)
+        k_q4dq_any<<<(unsigned)(nsb - done), kB, 0, stream>>>(x, n, done, packed, qscale, super_scale,
+                                                             block_scale, recon, flags);
+    return fqh::launched();
+}
+
+int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float* super_scale,
+                       int64_t n, float* out, hipStream_t stream) {
+    if (!packed || !qscale || !super_scale || n < 1 || !out) return FQ_E_INVALID;
+    if (!fqh::aligned(super_scale, 4) || !fqh::aligned(out, 4)) return FQ_E_INVALID;
+    const int64_t nsb = (n + kSuperElems - 1) / kSuperElems;
+    const int64_t nfull = n / kSuperElems;
+    if (nsb > 0x7FFFFFFF) return FQ_E_INVALID;
+    const bool al = fqh::aligned(packed, 2) && fqh::aligned(out, 16);
+    int64_t done = 0;
+    if (al && nfull > 0) {
+        k_q4dq_dequant<true><<<(unsigned)nfull, kB, 0, stream>>>(packed, qscale, super_scale, n, 0, out);
+        done = nfull;
+    }
+    if (done < nsb)
+        k_q4dq_dequant<false><<<(unsigned)(nsb - done), kB, 0, stream>>>(packed, qscale, super_scale, n, done,
+                                                                        out);
+    return fqh::launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,295 @@
+// rows.hip -- fused per-row (per-channel along axis 0 / per-token) calibration and
+// integer quantization, and the matching per-row dequantize.
+//
+// [QAT] optirs-gpu 0.3.2 src/optirs_gpu/quantization.rs, "Quantization-Aware
+// Training (QAT) primitives": per_channel_params (axis 0), QuantParams::from_minmax,
+// fake_quant_int_per_channel.  The page calibrates every channel in one pass and
+// quantizes in a second; here one workgroup owns a row, keeps it in registers
+// between the reduction and the quantize step, and reads it from HBM once.
+//
+// Workgroup: 256 threads, one row.  The row is split into 16-byte vectors (4 fp32
+// or 8 bf16); thread t holds vectors t, t + 256, t + 512, t + 768 of a slab of 1024
+// vectors.  Rows up to 4096 fp32 / 8192 bf16 are one slab and stay in registers;
+// longer rows are reduced slab by slab and re-read for the quantize step.
+#include "fq_device.h"
+#include "fq_host.h"
+
+using namespace fqk;
+
+namespace {
+
+constexpr int kB = fqh::kBlock;
+constexpr int kWaves = kB / kWave;
+constexpr int kCache = 4;              // vectors per thread per slab
+constexpr int kSlab = kCache * kB;     // vectors per slab
+
+template <int DT>
+struct Vec;
+template <>
+struct Vec<FQ_F32> {
+    static constexpr int N = 4;
+    float4 v;
+    __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+};
+template <>
+struct Vec<FQ_BF16> {
+    static constexpr int N = 8;
+    uint4 v;
+    __device__ __forceinline__ float get(int e) const {
+        uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+
+template <int DT>
+__device__ __forceinline__ float elem(const void* row, int64_t c) {
+    if (DT == FQ_F32) return reinterpret_cast<const float*>(row)[c];
+    return as_f((uint32_t)reinterpret_cast<const uint16_t*>(row)[c] << 16);
+}
+
+// Load vector vi of a row: 16-byte load when aligned, else element loads with a
+// bound check against cols (missing elements read as 0 and are marked invalid by
+// the caller through the same bound).
+template <int DT, bool AL>
+__device__ __forceinline__ Vec<DT> load_vec(const void* row, int64_t vi, int64_t cols) {
+    Vec<DT> r;
+    constexpr int N = Vec<DT>::N;
+    if constexpr (AL) {
+        if constexpr (DT == FQ_F32) r.v = reinterpret_cast<const float4*>(row)[vi];
+        else r.v = reinterpret_cast<const uint4*>(row)[vi];
+    } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+        for (int e = 0; e < N; ++e) {
+            int64_t c = vi * N + e;
+            if (c >= cols) break;
+            if constexpr (DT == FQ_F32) {
+                w[e] = as_u(reinterpret_cast<const float*>(row)[c]);
+            } else {
+                uint32_t h = reinterpret_cast<const uint16_t*>(row)[c];
+                w[e >> 1] |= (e & 1) ? (h << 16) : h;
+            }
+        }
+        *reinterpret_cast<uint4*>(&r.v) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return r;
+}
+
+template <int DT, int BITS, bool AL>
+__global__ __launch_bounds__(kB) void k_quant_rows(const void* __restrict__ x, int64_t cols, int affine,
+                                                   uint8_t* __restrict__ codes, float* __restrict__ fq,
+                                                   float* __restrict__ scale_out,
+                                                   int32_t* __restrict__ zp_out,
+                                                   uint32_t* __restrict__ flags) {
+    constexpr int N = Vec<DT>::N;
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const size_t esz = DT == FQ_F32 ? 4 : 2;
+    const char* xr = reinterpret_cast<const char*>(x) + (size_t)row * (size_t)cols * esz;
+    const int64_t nv = (cols + N - 1) / N;
+    const int nslab = (int)((nv + kSlab - 1) / kSlab);
+
+    // ---- reduction: finite min / max, non-finite marker ----
+    MinMax m;
+    Vec<DT> cache[kCache];
+    for (int s = 0; s < nslab; ++s) {
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) {
+            int64_t vi = (int64_t)s * kSlab + k * kB + t;
+            if (vi < nv) cache[k] = load_vec<DT, AL>(xr, vi, cols);
+        }
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) {
+            int64_t vi = (int64_t)s * kSlab + k * kB + t;
+            if (vi >= nv) continue;
+#pragma unroll
+            for (int e = 0; e < N; ++e)
+                if (AL || vi * N + e < cols) m.add(cache[k].get(e));
+        }
+    }
+    __shared__ float4 lds[kWaves];
+    {
+        float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
+        if (t % kWave == 0) lds[t / kWave] = r;
+        __syncthreads();
+        MinMax all;
+        for (int i = 0; i < kWaves; ++i) all.merge(lds[i].x, lds[i].y, as_u(lds[i].z));
+        m = all;
+    }
+    const bool aff = affine != 0;
+    const IntRange rg = int_range(BITS, aff);
+    const IntCal cal = calibrate(m.mn, m.mx, rg, aff);
+    if (t == 0) {
+        scale_out[row] = cal.scale;
+        zp_out[row] = cal.zp;
+        uint32_t f = (m.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+        if (flags && f) atomicOr(flags, f);
+    }
+    const IntQ q(cal.scale, cal.zp, rg);
+    // all elements finite and the divisor admitted to the exact fast quotient:
+    // no NaN / Inf / overflow can reach the rounding step
+    const bool finite_fast = !m.nonfinite() && !q.zero && q.div.fast;
+    const float sc = cal.scale;
+    const int zp = cal.zp;
+
+    // ---- quantize (last slab is still in registers) ----
+    uint8_t* crow8 = codes ? codes + (size_t)row * (size_t)cols : nullptr;
+    const int64_t pstride = (cols + 1) / 2;
+    uint8_t* crow4 = codes ? codes + (size_t)row * (size_t)pstride : nullptr;
+    float* frow = fq ? fq + (size_t)row * (size_t)cols : nullptr;
+    for (int s = nslab - 1; s >= 0; --s) {
+        if (s != nslab - 1) {
+#pragma unroll
+            for (int k = 0; k < kCache; ++k) {
+                int64_t vi = (int64_t)s * kSlab + k * kB + t;
+                if (vi < nv) cache[k] = load_vec<DT, AL>(xr, vi, cols);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kCache; ++k) {
+            int64_t vi = (int64_t)s * kSlab + k * kB + t;
+            if (vi >= nv) continue;
+            float o[N];
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                float xv = cache[k].get(e);
+                o[e] = finite_fast ? q.offset_finite(xv) : q.offset(xv);
+            }
+            if (AL) {
+                if (codes) {
+                    if (BITS == 8) {
+                        uint32_t w0 = pack4((int)o[0] + zp, (int)o[1] + zp, (int)o[2] + zp, (int)o[3] + zp);
+                        if (N == 4) {
+                            reinterpret_cast<uint32_t*>(crow8)[vi] = w0;
+                        } else {
+                            uint32_t w1 = pack4((int)o[4] + zp, (int)o[5] + zp, (int)o[6] + zp, (int)o[7] + zp);
+                            reinterpret_cast<uint2*>(crow8)[vi] = make_uint2(w0, w1);
+                        }
+                    } else {
+                        uint32_t b01 = nib2((int)o[0] + zp, (int)o[1] + zp);
+                        uint32_t b23 = nib2((int)o[2] + zp, (int)o[3] + zp);
+                        if (N == 4) {
+                            reinterpret_cast<uint16_t*>(crow4)[vi] = (uint16_t)(b01 | (b23 << 8));
+                        } else {
+                            uint32_t b45 = nib2((int)o[4] + zp, (int)o[5] + zp);
+                            uint32_t b67 = nib2((int)o[6] + zp, (int)o[7] + zp);
+                            reinterpret_cast<uint32_t*>(crow4)[vi] = b01 | (b23 << 8) | (b45 << 16) | (b67 << 24);
+                        }
+                    }
+                }
+                if (fq) {
+                    float4* fr = reinterpret_cast<float4*>(frow);
+                    fr[vi * (N / 4)] = make_float4(o[0] * sc, o[1] * sc, o[2] * sc, o[3] * sc);
+                    if (N == 8)
+                        fr[vi * 2 + 1] = make_float4(o[4] * sc, o[5] * sc, o[6] * sc, o[7] * sc);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    int64_t c = vi * N + e;
+                    if (c >= cols) break;
+                    int code = (int)o[e] + zp;
+                    if (frow) frow[c] = o[e] * sc;
+                    if (!codes) continue;
+                    if (BITS == 8) {
+                        crow8[c] = (uint8_t)code;
+                    } else if ((e & 1) == 0) {
+                        int next = (c + 1 < cols) ? (int)o[e + 1] + zp : 0;
+                        crow4[c >> 1] = (uint8_t)nib2(code, next);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Per-row dequantize: out[r, c] = (code - zp[r]) * scale[r]
+template <int BITS>
+__global__ __launch_bounds__(kB) void k_dq_rows(const uint8_t* __restrict__ codes, int64_t cols,
+                                                const float* __restrict__ scale,
+                                                const int32_t* __restrict__ zp,
+                                                float* __restrict__ out) {
+    const int64_t row = blockIdx.y;
+    const float s = scale[row];
+    const int z = zp[row];
+    const int64_t pstride = BITS == 8 ? cols : (cols + 1) / 2;
+    const uint8_t* cr = codes + (size_t)row * (size_t)pstride;
+    float* orow = out + (size_t)row * (size_t)cols;
+    for (int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x; c < cols; c += (int64_t)gridDim.x * kB) {
+        int q;
+        if (BITS == 8) {
+            q = (int)(int8_t)cr[c];
+        } else {
+            uint32_t b = cr[c >> 1];
+            uint32_t nib = (c & 1) ? (b & 0xFu) : (b >> 4);
+            q = ((int)(nib << 28)) >> 28;
+        }
+        orow[c] = (float)(q - z) * s;
+    }
+}
+
+template <int DT, int BITS>
+void launch_rows(const void* x, int64_t rows, int64_t cols, int affine, void* codes, float* fq,
+                 float* scale, int32_t* zp, uint32_t* flags, hipStream_t st) {
+    constexpr int N = Vec<DT>::N;
+    const size_t code_align = BITS == 8 ? (N == 4 ? 4 : 8) : (N == 4 ? 2 : 4);
+    const bool al = (cols % N == 0) && fqh::aligned(x, 16) && fqh::aligned(fq, 16) &&
+                    fqh::aligned(codes, code_align) && (BITS == 8 || (cols / 2) % (N / 2) == 0);
+    dim3 grid((unsigned)rows);
+    uint8_t* cd = (uint8_t*)codes;
+    if (al)
+        k_quant_rows<DT, BITS, true><<<grid, kB, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags);
+    else
+        k_quant_rows<DT, BITS, false><<<grid, kB, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fq_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int bits, int scheme,
+                  void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags,
+                  hipStream_t stream) {
+    if (!fqh::valid_bits(bits) || !fqh::valid_scheme(scheme) || !fqh::valid_dtype(dtype))
+        return FQ_E_UNSUPPORTED;
+    if (!x || rows < 1 || cols < 1 || !scale || !zero_point) return FQ_E_INVALID;
+    if (rows > 0x7FFFFFFF) return FQ_E_INVALID;
+    if (!fqh::aligned(x, dtype == FQ_F32 ? 4 : 2) || !fqh::aligned(fq, 4) || !fqh::aligned(scale, 4) ||
+        !fqh::aligned(zero_point, 4) || !fqh::aligned(flags, 4))
+        return FQ_E_INVALID;
+    const int aff = scheme == FQ_AFFINE;
+    if (dtype == FQ_F32) {
+        if (bits == 8) launch_rows<FQ_F32, 8>(x, rows, cols, aff, codes, fq, scale, zero_point, flags, stream);
+        else launch_rows<FQ_F32, 4>(x, rows, cols, aff, codes, fq, scale, zero_point, flags, stream);
+    } else {
+        if (bits == 8) launch_rows<FQ_BF16, 8>(x, rows, cols, aff, codes, fq, scale, zero_point, flags, stream);
+        else launch_rows<FQ_BF16, 4>(x, rows, cols, aff, codes, fq, scale, zero_point, flags, stream);
+    }
+    return fqh::launched();
+}
+
+int fq_dequantize_rows(const void* codes, int64_t rows, int64_t cols, int bits, const float* scale,
+                       const int32_t* zero_point, float* out, hipStream_t stream) {
+    if (!fqh::valid_bits(bits)) return FQ_E_UNSUPPORTED;
+    if (!codes || rows < 1 || cols < 1 || !scale || !zero_point || !out) return FQ_E_INVALID;
+    if (rows > 65535) {
+        // grid.y limit: process in row batches
+        for (int64_t r0 = 0; r0 < rows; r0 += 65535) {
+            int64_t nr = rows - r0 < 65535 ? rows - r0 : 65535;
+            const int64_t pstride = bits == 8 ? cols : (cols + 1) / 2;
+            int st = fq_dequantize_rows((const uint8_t*)codes + r0 * pstride, nr, cols, bits, scale + r0,
+                                        zero_point + r0, out + r0 * cols, stream);
+            if (st != FQ_OK) return st;
+        }
+        return FQ_OK;
+    }
+    if (!fqh::aligned(scale, 4) || !fqh::aligned(zero_point, 4) || !fqh::aligned(out, 4))
+        return FQ_E_INVALID;
+    unsigned gx = (unsigned)((cols + kB - 1) / kB);
+    if (gx > 64) gx = 64;
+    dim3 grid(gx, (unsigned)rows);
+    if (bits == 8) k_dq_rows<8><<<grid, kB, 0, stream>>>((const uint8_t*)codes, cols, scale, zero_point, out);
+    else k_dq_rows<4><<<grid, kB, 0, stream>>>((const uint8_t*)codes, cols, scale, zero_point, out);
+    return fqh::launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,423 @@
+// tensor.hip -- per-tensor kernels: the tensor-scope min / max / amax reduction
+// with parameter derivation on the device, integer quantize / fake-quant /
+// dequantize with one parameter set, and the straight-through-estimator backward.
+//
+// [QAT] = optirs-gpu 0.3.2 src/optirs_gpu/quantization.rs, "Quantization-Aware
+// Training (QAT) primitives": QuantParams::per_tensor_minmax, fake_quant_int,
+// real_min / real_max, fake_quant_backward.
+//
+// Layout: every kernel walks the tensor in chunks of four consecutive elements
+// (one 16-byte load of x), grid-stride, four chunks in flight per thread.  The
+// last n % 4 elements (and every chunk when a buffer is not vector-aligned) go
+// through the scalar form of the same chunk code.
+#include "fq_device.h"
+#include "fq_host.h"
+
+using namespace fqk;
+
+namespace {
+
+constexpr int kB = fqh::kBlock;
+constexpr int kWaves = kB / kWave;
+
+__device__ __forceinline__ float4 ld4(const float* p, int64_t c) {
+    return *reinterpret_cast<const float4*>(p + 4 * c);
+}
+__device__ __forceinline__ void st4(float* p, int64_t c, float4 v) {
+    *reinterpret_cast<float4*>(p + 4 * c) = v;
+}
+
+// ---------------------------------------------------------------------------
+// Tensor-scope reduction, pass 1: one partial per block.
+//   MINMAX: (finite min, finite max, max |x| bits) -- int calibration
+//   AMAX:   (-, finite amax, -)                     -- fp8 calibration
+// ---------------------------------------------------------------------------
+enum { kMinMax = 0, kAmax = 1 };
+
+template <int MODE>
+struct Acc {
+    MinMax m;
+    uint32_t amax = 0;
+    __device__ __forceinline__ void add(float v) {
+        if (MODE == kMinMax) {
+            m.add(v);
+        } else {
+            uint32_t a = as_u(v) & 0x7FFFFFFFu;
+            amax = max(amax, a < 0x7F800000u ? a : 0u);
+        }
+    }
+    __device__ __forceinline__ void add4(float4 v) {
+        add(v.x);
+        add(v.y);
+        add(v.z);
+        add(v.w);
+    }
+};
+
+template <int MODE, bool AL>
+__global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__ x, int64_t n,
+                                                       float4* __restrict__ part) {
+    Acc<MODE> acc;
+    const int64_t nfull = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kB;
+    int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
+    if (AL) {
+        for (; c + 3 * stride < nfull; c += 4 * stride) {
+            float4 v0 = ld4(x, c), v1 = ld4(x, c + stride);
+            float4 v2 = ld4(x, c + 2 * stride), v3 = ld4(x, c + 3 * stride);
+            acc.add4(v0);
+            acc.add4(v1);
+            acc.add4(v2);
+            acc.add4(v3);
+        }
+        for (; c < nfull; c += stride) acc.add4(ld4(x, c));
+    } else {
+        for (; c < nfull; c += stride)
+            for (int e = 0; e < 4; ++e) acc.add(x[4 * c + e]);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) acc.add(x[4 * nfull + threadIdx.x]);
+
+    __shared__ float4 lds[kWaves];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    float4 r;
+    if (MODE == kMinMax) {
+        r = make_float4(wave_min_f(acc.m.mn), wave_max_f(acc.m.mx), as_f(wave_max_u(acc.m.nf)), 0.f);
+    } else {
+        r = make_float4(0.f, as_f(wave_max_u(acc.amax)), 0.f, 0.f);
+    }
+    if (lane == 0) lds[w] = r;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < kWaves; ++i) {
+            float4 o = lds[i];
+            if (MODE == kMinMax) {
+                r.x = fminf(r.x, o.x);
+                r.y = fmaxf(r.y, o.y);
+                r.z = as_f(max(as_u(r.z), as_u(o.z)));
+            } else {
+                r.y = as_f(max(as_u(r.y), as_u(o.y)));
+            }
+        }
+        part[blockIdx.x] = r;
+    }
+}
+
+// Pass 2 (one block): fold the partials and derive the integer parameters
+// ([QAT] from_minmax, real_min / real_max).
+__global__ __launch_bounds__(kB) void k_params_int_final(const float4* __restrict__ part, int nparts,
+                                                         int bits, int affine,
+                                                         fq_int_params* __restrict__ params,
+                                                         uint32_t* __restrict__ flags) {
+    MinMax m;
+    for (int i = threadIdx.x; i < nparts; i += kB) {
+        float4 p = part[i];
+        m.merge(p.x, p.y, as_u(p.z));
+    }
+    __shared__ float4 lds[kWaves];
+    float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
+    if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = r;
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    for (int i = 1; i < kWaves; ++i) m.merge(lds[i].x, lds[i].y, as_u(lds[i].z));
+    m.merge(r.x, r.y, as_u(r.z));
+    IntRange rg = int_range(bits, affine != 0);
+    IntCal cal = calibrate(m.mn, m.mx, rg, affine != 0);
+    fq_int_params out;
+    out.scale = cal.scale;
+    out.zero_point = cal.zp;
+    out.real_min = (float)(rg.qmin - cal.zp) * cal.scale;
+    out.real_max = (float)(rg.qmax - cal.zp) * cal.scale;
+    *params = out;
+    uint32_t f = (m.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+    if (flags && f) atomicOr(flags, f);
+}
+
+// Pass 2 for fp8: amax over the finite elements -> scale = amax / max-normal.
+__global__ __launch_bounds__(kB) void k_fp8_scale_final(const float4* __restrict__ part, int nparts,
+                                                        float* __restrict__ s_e4m3,
+                                                        float* __restrict__ s_e5m2,
+                                                        uint32_t* __restrict__ flags) {
+    uint32_t a = 0;
+    for (int i = threadIdx.x; i < nparts; i += kB) a = max(a, as_u(part[i].y));
+    __shared__ uint32_t lds[kWaves];
+    a = wave_max_u(a);
+    if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = a;
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    for (int i = 1; i < kWaves; ++i) a = max(a, lds[i]);
+    float amax = as_f(a);
+    bool zero = false;
+    if (s_e4m3) {
+        float s = amax / 448.0f;
+        *s_e4m3 = s;
+        zero |= (s == 0.0f);
+    }
+    if (s_e5m2) {
+        float s = amax / 57344.0f;
+        *s_e5m2 = s;
+        zero |= (s == 0.0f);
+    }
+    if (flags && zero) atomicOr(flags, FQ_FLAG_DEGENERATE);
+}
+
+// ---------------------------------------------------------------------------
+// Integer quantize / fake-quant with one parameter set ([QAT] fake_quant_int)
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct IntTensorOp {
+    IntQ q;
+    float scale;
+    int zp;
+    uint8_t* codes;
+    float* fq;
+
+    // scalar form for `cnt` (1..4) elements starting at chunk c
+    __device__ void scalar_chunk(const float* x, int64_t c, int cnt) const {
+        int code[4] = {0, 0, 0, 0};
+        for (int e = 0; e < cnt; ++e) {
+            float o = q.offset(x[4 * c + e]);
+            code[e] = (int)o + zp;
+            if (fq) fq[4 * c + e] = o * scale;
+            if (codes && BITS == 8) codes[4 * c + e] = (uint8_t)code[e];
+        }
+        if (codes && BITS == 4) {
+            codes[2 * c] = (uint8_t)nib2(code[0], code[1]);
+            if (cnt > 2) codes[2 * c + 1] = (uint8_t)nib2(code[2], code[3]);
+        }
+    }
+    __device__ __forceinline__ void vector_chunk(int64_t c, float4 v) const {
+        float o0 = q.offset(v.x), o1 = q.offset(v.y), o2 = q.offset(v.z), o3 = q.offset(v.w);
+        if (codes) {
+            int c0 = (int)o0 + zp, c1 = (int)o1 + zp, c2 = (int)o2 + zp, c3 = (int)o3 + zp;
+            if (BITS == 8) {
+                reinterpret_cast<uint32_t*>(codes)[c] = pack4(c0, c1, c2, c3);
+            } else {
+                reinterpret_cast<uint16_t*>(codes)[c] = (uint16_t)(nib2(c0, c1) | (nib2(c2, c3) << 8));
+            }
+        }
+        if (fq) st4(fq, c, make_float4(o0 * scale, o1 * scale, o2 * scale, o3 * scale));
+    }
+};
+
+template <int BITS, bool AL>
+__global__ __launch_bounds__(kB) void k_fq_int_tensor(const float* __restrict__ x, int64_t n, int affine,
+                                                      const fq_int_params* __restrict__ p,
+                                                      uint8_t* __restrict__ codes,
+                                                      float* __restrict__ fq) {
+    const fq_int_params P = *p;
+    const IntRange rg = int_range(BITS, affine != 0);
+    const IntTensorOp<BITS> op{IntQ(P.scale, P.zero_point, rg), P.scale, P.zero_point, codes, fq};
+    const int64_t nfull = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kB;
+    int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
+    if (AL) {
+        for (; c + 3 * stride < nfull; c += 4 * stride) {
+            float4 v0 = ld4(x, c), v1 = ld4(x, c + stride);
+            float4 v2 = ld4(x, c + 2 * stride), v3 = ld4(x, c + 3 * stride);
+            op.vector_chunk(c, v0);
+            op.vector_chunk(c + stride, v1);
+            op.vector_chunk(c + 2 * stride, v2);
+            op.vector_chunk(c + 3 * stride, v3);
+        }
+        for (; c < nfull; c += stride) op.vector_chunk(c, ld4(x, c));
+    } else {
+        for (; c < nfull; c += stride) op.scalar_chunk(x, c, 4);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 3)) op.scalar_chunk(x, nfull, (int)(n & 3));
+}
+
+// ---------------------------------------------------------------------------
+// Integer dequantize ([QAT] dequant(q) = (q - zero_point) * scale)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int sext4(uint32_t nib) { return ((int)(nib << 28)) >> 28; }
+__device__ __forceinline__ int sext8(uint32_t b) { return ((int)(b << 24)) >> 24; }
+
+template <int BITS, bool AL>
+__global__ __launch_bounds__(kB) void k_dq_int_tensor(const uint8_t* __restrict__ codes, int64_t n,
+                                                      const fq_int_params* __restrict__ p,
+                                                      float* __restrict__ out) {
+    const float s = p->scale;
+    const int zp = p->zero_point;
+    const int64_t nfull = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kB;
+    int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
+    auto code_at = [&](int64_t i) -> int {
+        if (BITS == 8) return sext8(codes[i]);
+        uint32_t byte = codes[i >> 1];
+        return sext4((i & 1) ? (byte & 0xFu) : (byte >> 4));
+    };
+    for (; c < nfull; c += stride) {
+        int q0, q1, q2, q3;
+        if (AL && BITS == 8) {
+            uint32_t w = reinterpret_cast<const uint32_t*>(codes)[c];
+            q0 = sext8(w);
+            q1 = sext8(w >> 8);
+            q2 = sext8(w >> 16);
+            q3 = sext8(w >> 24);
+        } else if (AL) {
+            uint32_t w = reinterpret_cast<const uint16_t*>(codes)[c];
+            q0 = sext4((w >> 4) & 0xFu);
+            q1 = sext4(w & 0xFu);
+            q2 = sext4((w >> 12) & 0xFu);
+            q3 = sext4((w >> 8) & 0xFu);
+        } else {
+            q0 = code_at(4 * c);
+            q1 = code_at(4 * c + 1);
+            q2 = code_at(4 * c + 2);
+            q3 = code_at(4 * c + 3);
+        }
+        float4 v = make_float4((float)(q0 - zp) * s, (float)(q1 - zp) * s, (float)(q2 - zp) * s,
+                               (float)(q3 - zp) * s);
+        if (AL) {
+            st4(out, c, v);
+        } else {
+            out[4 * c] = v.x;
+            out[4 * c + 1] = v.y;
+            out[4 * c + 2] = v.z;
+            out[4 * c + 3] = v.w;
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        int64_t i = 4 * nfull + threadIdx.x;
+        out[i] = (float)(code_at(i) - zp) * s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// STE backward ([QAT] fake_quant_backward): pass g where lo <= x <= hi.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ste1(float g, float x, float lo, float hi) {
+    return (x >= lo && x <= hi) ? g : 0.0f;
+}
+
+template <bool AL>
+__global__ __launch_bounds__(kB) void k_ste(const float* __restrict__ g, const float* __restrict__ x,
+                                            int64_t n, const float* __restrict__ bounds,
+                                            float* __restrict__ out) {
+    const float b0 = bounds[0], b1 = bounds[1];
+    const float lo = b0 <= b1 ? b0 : b1;
+    const float hi = b0 <= b1 ? b1 : b0;
+    const int64_t nfull = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kB;
+    int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
+    if (AL) {
+        for (; c + 1 * stride < nfull; c += 2 * stride) {
+            float4 g0 = ld4(g, c), x0 = ld4(x, c), g1 = ld4(g, c + stride), x1 = ld4(x, c + stride);
+            st4(out, c, make_float4(ste1(g0.x, x0.x, lo, hi), ste1(g0.y, x0.y, lo, hi),
+                                    ste1(g0.z, x0.z, lo, hi), ste1(g0.w, x0.w, lo, hi)));
+            st4(out, c + stride,
+                make_float4(ste1(g1.x, x1.x, lo, hi), ste1(g1.y, x1.y, lo, hi),
+                            ste1(g1.z, x1.z, lo, hi), ste1(g1.w, x1.w, lo, hi)));
+        }
+        for (; c < nfull; c += stride) {
+            float4 g0 = ld4(g, c), x0 = ld4(x, c);
+            st4(out, c, make_float4(ste1(g0.x, x0.x, lo, hi), ste1(g0.y, x0.y, lo, hi),
+                                    ste1(g0.z, x0.z, lo, hi), ste1(g0.w, x0.w, lo, hi)));
+        }
+    } else {
+        for (; c < nfull; c += stride)
+            for (int e = 0; e < 4; ++e) out[4 * c + e] = ste1(g[4 * c + e], x[4 * c + e], lo, hi);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+        int64_t i = 4 * nfull + threadIdx.x;
+        out[i] = ste1(g[i], x[i], lo, hi);
+    }
+}
+
+// launch the reduction's first pass; returns the number of partials
+template <int MODE>
+unsigned launch_partial(const float* x, int64_t n, void* ws, hipStream_t st) {
+    unsigned G = fqh::reduce_blocks(n);
+    if (fqh::aligned(x, 16))
+        k_reduce_partial<MODE, true><<<G, kB, 0, st>>>(x, n, (float4*)ws);
+    else
+        k_reduce_partial<MODE, false><<<G, kB, 0, st>>>(x, n, (float4*)ws);
+    return G;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int fq_tensor_params_int(const float* x, int64_t n, int bits, int scheme, void* workspace,
+                         size_t workspace_bytes, fq_int_params* params, uint32_t* flags,
+                         hipStream_t stream) {
+    if (!fqh::valid_bits(bits) || !fqh::valid_scheme(scheme)) return FQ_E_UNSUPPORTED;
+    if (!x || n < 1 || !workspace || !params) return FQ_E_INVALID;
+    if (workspace_bytes < fq_workspace_bytes(n) || !fqh::aligned(workspace, 16)) return FQ_E_INVALID;
+    if (!fqh::aligned(params, 4) || !fqh::aligned(flags, 4) || !fqh::aligned(x, 4)) return FQ_E_INVALID;
+    unsigned G = launch_partial<kMinMax>(x, n, workspace, stream);
+    k_params_int_final<<<1, kB, 0, stream>>>((const float4*)workspace, (int)G, bits,
+                                             scheme == FQ_AFFINE, params, flags);
+    return fqh::launched();
+}
+
+int fq_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme,
+                             const fq_int_params* params, void* codes, float* fq,
+                             hipStream_t stream) {
+    if (!fqh::valid_bits(bits) || !fqh::valid_scheme(scheme)) return FQ_E_UNSUPPORTED;
+    if (!x || n < 1 || !params || (!codes && !fq)) return FQ_E_INVALID;
+    if (!fqh::aligned(params, 4) || !fqh::aligned(x, 4) || !fqh::aligned(fq, 4)) return FQ_E_INVALID;
+    const bool al = fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, bits == 8 ? 4 : 2);
+    const unsigned G = fqh::grid_for((n + 3) / 4, 4 * kB, 8);
+    uint8_t* cd = (uint8_t*)codes;
+    const int aff = scheme == FQ_AFFINE;
+    if (bits == 8) {
+        if (al) k_fq_int_tensor<8, true><<<G, kB, 0, stream>>>(x, n, aff, params, cd, fq);
+        else k_fq_int_tensor<8, false><<<G, kB, 0, stream>>>(x, n, aff, params, cd, fq);
+    } else {
+        if (al) k_fq_int_tensor<4, true><<<G, kB, 0, stream>>>(x, n, aff, params, cd, fq);
+        else k_fq_int_tensor<4, false><<<G, kB, 0, stream>>>(x, n, aff, params, cd, fq);
+    }
+    return fqh::launched();
+}
+
+int fq_dequantize_int_tensor(const void* codes, int64_t n, int bits, const fq_int_params* params,
+                             float* out, hipStream_t stream) {
+    if (!fqh::valid_bits(bits)) return FQ_E_UNSUPPORTED;
+    if (!codes || n < 1 || !params || !out) return FQ_E_INVALID;
+    if (!fqh::aligned(params, 4) || !fqh::aligned(out, 4)) return FQ_E_INVALID;
+    const bool al = fqh::aligned(out, 16) && fqh::aligned(codes, bits == 8 ? 4 : 2);
+    const unsigned G = fqh::grid_for((n + 3) / 4, kB, 8);
+    const uint8_t* cd = (const uint8_t*)codes;
+    if (bits == 8) {
+        if (al) k_dq_int_tensor<8, true><<<G, kB, 0, stream>>>(cd, n, params, out);
+        else k_dq_int_tensor<8, false><<<G, kB, 0, stream>>>(cd, n, params, out);
+    } else {
+        if (al) k_dq_int_tensor<4, true><<<G, kB, 0, stream>>>(cd, n, params, out);
+        else k_dq_int_tensor<4, false><<<G, kB, 0, stream>>>(cd, n, params, out);
+    }
+    return fqh::launched();
+}
+
+int fq_ste_backward(const float* grad, int64_t n_grad, const float* x, int64_t n_x,
+                    const float* bounds, float* grad_in, hipStream_t stream) {
+    if (!grad || !x || !bounds || !grad_in || n_x < 1 || n_grad < 1) return FQ_E_INVALID;
+    if (n_grad != n_x) return FQ_E_DIM;
+    if (!fqh::aligned(grad, 4) || !fqh::aligned(x, 4) || !fqh::aligned(bounds, 4) ||
+        !fqh::aligned(grad_in, 4))
+        return FQ_E_INVALID;
+    const bool al = fqh::aligned(grad, 16) && fqh::aligned(x, 16) && fqh::aligned(grad_in, 16);
+    const unsigned G = fqh::grid_for((n_x + 3) / 4, 2 * kB, 8);
+    if (al) k_ste<true><<<G, kB, 0, stream>>>(grad, x, n_x, bounds, grad_in);
+    else k_ste<false><<<G, kB, 0, stream>>>(grad, x, n_x, bounds, grad_in);
+    return fqh::launched();
+}
+
+int fq_fp8_tensor_scale(const float* x, int64_t n, void* workspace, size_t workspace_bytes,
+                        float* scale_e4m3, float* scale_e5m2, uint32_t* flags, hipStream_t stream) {
+    if (!x || n < 1 || !workspace || (!scale_e4m3 && !scale_e5m2)) return FQ_E_INVALID;
+    if (workspace_bytes < fq_workspace_bytes(n) || !fqh::aligned(workspace, 16)) return FQ_E_INVALID;
+    if (!fqh::aligned(x, 4) || !fqh::aligned(scale_e4m3, 4) || !fqh::aligned(scale_e5m2, 4) ||
+        !fqh::aligned(flags, 4))
+        return FQ_E_INVALID;
+    unsigned G = launch_partial<kAmax>(x, n, workspace, stream);
+    k_fp8_scale_final<<<1, kB, 0, stream>>>((const float4*)workspace, (int)G, scale_e4m3, scale_e5m2,
+                                            flags);
+    return fqh::launched();
+}
+
+}  // extern "C"

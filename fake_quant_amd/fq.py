@@ -1,0 +1,390 @@
+"""Python binding of libfq.so (include/fq.h): argument marshalling only.
+
+Every function named ``fq_*`` here calls the C entry point of the same name with
+device pointers taken from torch tensors and the current HIP stream; all the
+arithmetic runs in the library's gfx950 kernels.  A non-zero status raises
+``FqError``.  The convenience helpers at the end (``params_int`` ...) only
+allocate output tensors with torch and call the ``fq_*`` functions.
+
+There is no fallback: importing this module raises if libfq.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfq.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_DIM, E_HIP = 0, -1, -2, -3, -4
+FLAG_NONFINITE, FLAG_DEGENERATE = 1, 2
+SYM, AFFINE = 0, 1
+E4M3, E5M2 = 0, 1
+F32, BF16 = 0, 1
+
+
+class FqError(RuntimeError):
+    def __init__(self, name: str, status: int, msg: str):
+        super().__init__(f"{name}: {msg} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m fake_quant_amd.build` "
+                      "(there is no non-HIP fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "fq_version": (_INT, []),
+    "fq_status_string": (ctypes.c_char_p, [_INT]),
+    "fq_workspace_bytes": (_SZ, [_I64]),
+    "fq_q4dq_sizes": (_INT, [_I64, _P, _P, _P]),
+    "fq_tensor_params_int": (_INT, [_P, _I64, _INT, _INT, _P, _SZ, _P, _P, _P]),
+    "fq_fake_quant_int_tensor": (_INT, [_P, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "fq_dequantize_int_tensor": (_INT, [_P, _I64, _INT, _P, _P, _P]),
+    "fq_ste_backward": (_INT, [_P, _I64, _P, _I64, _P, _P, _P]),
+    "fq_quant_rows": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P]),
+    "fq_dequantize_rows": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P, _P]),
+    "fq_fp8_tensor_scale": (_INT, [_P, _I64, _P, _SZ, _P, _P, _P, _P]),
+    "fq_fp8_quantize": (_INT, [_P, _I64, _INT, _P, _P, _P, _P]),
+    "fq_fp8_dequantize": (_INT, [_P, _I64, _INT, _P, _P, _P]),
+    "fq_q4dq_quantize": (_INT, [_P, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "fq_q4dq_dequantize": (_INT, [_P, _P, _P, _I64, _P, _P]),
+    "fq_mxfp8_rows": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    """Device (or host, for tests of argument checks) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(name: str, st: int):
+    if st != OK:
+        raise FqError(name, st, _lib.fq_status_string(st).decode())
+
+
+def _need(name: str, what: str, t, nbytes: int):
+    """Host-side guard before any launch: a tensor argument must be a contiguous
+    GPU tensor holding at least the bytes the call touches (the C ABI trusts the
+    sizes it is given).  Plain integers are raw addresses and are passed as is."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_cuda:
+        raise FqError(name, E_INVALID, f"{what} is not a GPU tensor")
+    if not t.is_contiguous():
+        raise FqError(name, E_INVALID, f"{what} is not contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise FqError(name, E_INVALID, f"{what} holds {have} bytes, the call touches {nbytes}")
+
+
+def _codes_bytes(n: int, bits: int) -> int:
+    return n if bits == 8 else (n + 1) // 2
+
+
+# ---------------------------------------------------------------------------
+# C entry points (same names, same argument order; tensors in, status checked)
+# ---------------------------------------------------------------------------
+
+def fq_version() -> int:
+    return _lib.fq_version()
+
+
+def fq_workspace_bytes(n: int) -> int:
+    return _lib.fq_workspace_bytes(n)
+
+
+def fq_q4dq_sizes(n: int):
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("fq_q4dq_sizes", _lib.fq_q4dq_sizes(n, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def fq_tensor_params_int(x, n, bits, scheme, workspace, workspace_bytes, params, flags=None, stream=None):
+    nm = "fq_tensor_params_int"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "params", params, 16)
+    _need(nm, "flags", flags, 4)
+    _check("fq_tensor_params_int",
+           _lib.fq_tensor_params_int(_ptr(x), n, bits, scheme, _ptr(workspace), workspace_bytes,
+                                     _ptr(params), _ptr(flags), _stream(stream)))
+
+
+def fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes=None, fq=None, stream=None):
+    nm = "fq_fake_quant_int_tensor"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "params", params, 16)
+    _need(nm, "codes", codes, _codes_bytes(n, bits))
+    _need(nm, "fq", fq, 4 * n)
+    _check("fq_fake_quant_int_tensor",
+           _lib.fq_fake_quant_int_tensor(_ptr(x), n, bits, scheme, _ptr(params), _ptr(codes), _ptr(fq),
+                                         _stream(stream)))
+
+
+def fq_dequantize_int_tensor(codes, n, bits, params, out, stream=None):
+    nm = "fq_dequantize_int_tensor"
+    _need(nm, "codes", codes, _codes_bytes(n, bits))
+    _need(nm, "params", params, 16)
+    _need(nm, "out", out, 4 * n)
+    _check("fq_dequantize_int_tensor",
+           _lib.fq_dequantize_int_tensor(_ptr(codes), n, bits, _ptr(params), _ptr(out), _stream(stream)))
+
+
+def fq_ste_backward(grad, n_grad, x, n_x, bounds, grad_in, stream=None):
+    nm = "fq_ste_backward"
+    _need(nm, "grad", grad, 4 * n_grad)
+    _need(nm, "x", x, 4 * n_x)
+    _need(nm, "bounds", bounds, 8)
+    _need(nm, "grad_in", grad_in, 4 * n_x)
+    _check("fq_ste_backward",
+           _lib.fq_ste_backward(_ptr(grad), n_grad, _ptr(x), n_x, _ptr(bounds), _ptr(grad_in),
+                                _stream(stream)))
+
+
+def fq_quant_rows(x, dtype, rows, cols, bits, scheme, codes, fq, scale, zero_point, flags=None, stream=None):
+    nm = "fq_quant_rows"
+    _need(nm, "x", x, rows * cols * (2 if dtype == BF16 else 4))
+    _need(nm, "codes", codes, rows * _codes_bytes(cols, bits))
+    _need(nm, "fq", fq, 4 * rows * cols)
+    _need(nm, "scale", scale, 4 * rows)
+    _need(nm, "zero_point", zero_point, 4 * rows)
+    _need(nm, "flags", flags, 4)
+    _check("fq_quant_rows",
+           _lib.fq_quant_rows(_ptr(x), dtype, rows, cols, bits, scheme, _ptr(codes), _ptr(fq), _ptr(scale),
+                              _ptr(zero_point), _ptr(flags), _stream(stream)))
+
+
+def fq_dequantize_rows(codes, rows, cols, bits, scale, zero_point, out, stream=None):
+    nm = "fq_dequantize_rows"
+    _need(nm, "codes", codes, rows * _codes_bytes(cols, bits))
+    _need(nm, "scale", scale, 4 * rows)
+    _need(nm, "zero_point", zero_point, 4 * rows)
+    _need(nm, "out", out, 4 * rows * cols)
+    _check("fq_dequantize_rows",
+           _lib.fq_dequantize_rows(_ptr(codes), rows, cols, bits, _ptr(scale), _ptr(zero_point), _ptr(out),
+                                   _stream(stream)))
+
+
+def fq_fp8_tensor_scale(x, n, workspace, workspace_bytes, scale_e4m3=None, scale_e5m2=None, flags=None,
+                        stream=None):
+    nm = "fq_fp8_tensor_scale"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "scale_e4m3", scale_e4m3, 4)
+    _need(nm, "scale_e5m2", scale_e5m2, 4)
+    _need(nm, "flags", flags, 4)
+    _check("fq_fp8_tensor_scale",
+           _lib.fq_fp8_tensor_scale(_ptr(x), n, _ptr(workspace), workspace_bytes, _ptr(scale_e4m3),
+                                    _ptr(scale_e5m2), _ptr(flags), _stream(stream)))
+
+
+def fq_fp8_quantize(x, n, fmt, scale, q=None, fq=None, stream=None):
+    nm = "fq_fp8_quantize"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "scale", scale, 4)
+    _need(nm, "q", q, n)
+    _need(nm, "fq", fq, 4 * n)
+    _check("fq_fp8_quantize",
+           _lib.fq_fp8_quantize(_ptr(x), n, fmt, _ptr(scale), _ptr(q), _ptr(fq), _stream(stream)))
+
+
+def fq_fp8_dequantize(q, n, fmt, scale, out, stream=None):
+    nm = "fq_fp8_dequantize"
+    _need(nm, "q", q, n)
+    _need(nm, "scale", scale, 4)
+    _need(nm, "out", out, 4 * n)
+    _check("fq_fp8_dequantize",
+           _lib.fq_fp8_dequantize(_ptr(q), n, fmt, _ptr(scale), _ptr(out), _stream(stream)))
+
+
+def fq_q4dq_quantize(x, n, packed, qscale, super_scale, block_scale=None, recon=None, flags=None, stream=None):
+    nm = "fq_q4dq_quantize"
+    nb = (n + 63) // 64
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "packed", packed, (n + 1) // 2)
+    _need(nm, "qscale", qscale, nb)
+    _need(nm, "super_scale", super_scale, 4 * ((nb + 255) // 256))
+    _need(nm, "block_scale", block_scale, 4 * nb)
+    _need(nm, "recon", recon, 4 * n)
+    _need(nm, "flags", flags, 4)
+    _check("fq_q4dq_quantize",
+           _lib.fq_q4dq_quantize(_ptr(x), n, _ptr(packed), _ptr(qscale), _ptr(super_scale), _ptr(block_scale),
+                                 _ptr(recon), _ptr(flags), _stream(stream)))
+
+
+def fq_q4dq_dequantize(packed, qscale, super_scale, n, out, stream=None):
+    nm = "fq_q4dq_dequantize"
+    nb = (n + 63) // 64
+    _need(nm, "packed", packed, (n + 1) // 2)
+    _need(nm, "qscale", qscale, nb)
+    _need(nm, "super_scale", super_scale, 4 * ((nb + 255) // 256))
+    _need(nm, "out", out, 4 * n)
+    _check("fq_q4dq_dequantize",
+           _lib.fq_q4dq_dequantize(_ptr(packed), _ptr(qscale), _ptr(super_scale), n, _ptr(out),
+                                   _stream(stream)))
+
+
+def fq_mxfp8_rows(x, dtype, rows, cols, q, e8m0, fq=None, stream=None):
+    nm = "fq_mxfp8_rows"
+    _need(nm, "x", x, rows * cols * (2 if dtype == BF16 else 4))
+    _need(nm, "q", q, rows * cols)
+    _need(nm, "e8m0", e8m0, rows * ((cols + 31) // 32))
+    _need(nm, "fq", fq, 4 * rows * cols)
+    _check("fq_mxfp8_rows",
+           _lib.fq_mxfp8_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(e8m0), _ptr(fq), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Convenience: allocate outputs with torch on x's device, call the entry points
+# ---------------------------------------------------------------------------
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def _zeros_flags(like):
+    return torch.zeros(1, dtype=torch.int32, device=like.device)
+
+
+def params_int(x, bits=8, scheme=SYM):
+    """Per-tensor calibration -> (params int32[4] view of fq_int_params, flags)."""
+    n = x.numel()
+    wsb = fq_workspace_bytes(n)
+    ws = _empty(max(wsb // 4, 1), torch.float32, x)
+    params = _empty(4, torch.int32, x)
+    flags = _zeros_flags(x)
+    fq_tensor_params_int(x, n, bits, scheme, ws, wsb, params, flags)
+    return params, flags
+
+
+def params_fields(params):
+    """(scale, zero_point, real_min, real_max) from an int32[4] fq_int_params buffer."""
+    p = params.cpu()
+    f = p.view(torch.float32)
+    return float(f[0]), int(p[1]), float(f[2]), float(f[3])
+
+
+def fake_quant_int_tensor(x, params, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+    n = x.numel()
+    codes = _empty(n if bits == 8 else (n + 1) // 2, torch.int8 if bits == 8 else torch.uint8, x) if want_codes else None
+    fq = _empty(n, torch.float32, x) if want_fq else None
+    fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes, fq)
+    return codes, fq
+
+
+def dequantize_int_tensor(codes, n, params, bits=8):
+    out = _empty(n, torch.float32, codes)
+    fq_dequantize_int_tensor(codes, n, bits, params, out)
+    return out
+
+
+def ste_backward(grad, x, bounds):
+    out = _empty(x.numel(), torch.float32, x)
+    fq_ste_backward(grad, grad.numel(), x, x.numel(), bounds, out)
+    return out
+
+
+def quant_rows(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+    rows, cols = x.shape
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    if want_codes:
+        codes = _empty((rows, cols), torch.int8, x) if bits == 8 else _empty((rows, (cols + 1) // 2), torch.uint8, x)
+    else:
+        codes = None
+    fq = _empty((rows, cols), torch.float32, x) if want_fq else None
+    scale = _empty(rows, torch.float32, x)
+    zp = _empty(rows, torch.int32, x)
+    flags = _zeros_flags(x)
+    fq_quant_rows(x, dtype, rows, cols, bits, scheme, codes, fq, scale, zp, flags)
+    return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
+
+
+def dequantize_rows(codes, rows, cols, scale, zp, bits=8):
+    out = _empty((rows, cols), torch.float32, codes)
+    fq_dequantize_rows(codes, rows, cols, bits, scale, zp, out)
+    return out
+
+
+def fp8_tensor_scale(x):
+    n = x.numel()
+    wsb = fq_workspace_bytes(n)
+    ws = _empty(max(wsb // 4, 1), torch.float32, x)
+    s = _empty(2, torch.float32, x)
+    flags = _zeros_flags(x)
+    fq_fp8_tensor_scale(x, n, ws, wsb, s[0:1], s[1:2], flags)
+    return s, flags
+
+
+def fp8_quantize(x, fmt, scale, want_q=True, want_fq=True):
+    n = x.numel()
+    q = _empty(n, torch.uint8, x) if want_q else None
+    fq = _empty(n, torch.float32, x) if want_fq else None
+    fq_fp8_quantize(x, n, fmt, scale, q, fq)
+    return q, fq
+
+
+def fp8_dequantize(q, fmt, scale):
+    out = _empty(q.numel(), torch.float32, q)
+    fq_fp8_dequantize(q, q.numel(), fmt, scale, out)
+    return out
+
+
+def q4dq_quantize(x, want_block_scale=True, want_recon=True):
+    n = x.numel()
+    npk, nb, ns = fq_q4dq_sizes(n)
+    packed = _empty(npk, torch.uint8, x)
+    qscale = _empty(nb, torch.uint8, x)
+    sup = _empty(ns, torch.float32, x)
+    bs = _empty(nb, torch.float32, x) if want_block_scale else None
+    recon = _empty(n, torch.float32, x) if want_recon else None
+    flags = _zeros_flags(x)
+    fq_q4dq_quantize(x, n, packed, qscale, sup, bs, recon, flags)
+    return dict(packed=packed, qscale=qscale, super=sup, block_scale=bs, recon=recon, flags=flags)
+
+
+def q4dq_dequantize(packed, qscale, sup, n):
+    out = _empty(n, torch.float32, packed)
+    fq_q4dq_dequantize(packed, qscale, sup, n, out)
+    return out
+
+
+def mxfp8_rows(x, want_fq=True):
+    rows, cols = x.shape
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    q = _empty((rows, cols), torch.uint8, x)
+    e8 = _empty((rows, (cols + 31) // 32), torch.uint8, x)
+    fq = _empty((rows, cols), torch.float32, x) if want_fq else None
+    fq_mxfp8_rows(x, dtype, rows, cols, q, e8, fq)
+    return dict(q=q, e8m0=e8, fq=fq)

@@ -1,0 +1,210 @@
+/*
+ * fq.h -- C ABI of libfq.so: fake quantization (quantize / dequantize /
+ * fake-quant) of tensors on AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point enqueues hand-written HIP kernels on the caller's stream and
+ * returns at once; nothing here allocates device memory or synchronises.
+ *
+ * Conventions shared by all entry points
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  Inputs are read
+ *     only; outputs must not overlap inputs or each other.  Any alignment is
+ *     accepted (16-byte aligned buffers take the vector path).
+ *   - Layouts are dense row-major; sizes are element counts.
+ *   - Arithmetic is IEEE binary32 with one rounding per operation, true division
+ *     where the method divides, round-half-to-even for codes (round-half-away for
+ *     the 8-bit double-quant scale codes).
+ *   - Argument errors are returned synchronously, before anything is enqueued:
+ *       FQ_E_INVALID      null / empty / too-small argument (the pages' InvalidState
+ *                         for arguments: empty tensors cannot be calibrated),
+ *       FQ_E_UNSUPPORTED  width other than 4 or 8, unknown scheme / format / dtype
+ *                         (the pages' UnsupportedOperation),
+ *       FQ_E_DIM          two lengths that must agree do not (DimensionMismatch),
+ *       FQ_E_HIP          the HIP launch itself failed.
+ *   - Data-dependent conditions are NOT errors: kernels OR FQ_FLAG_* bits into
+ *     an optional device uint32_t (`flags`, may be NULL) which the caller zeroes;
+ *     the library never clears it.  NONFINITE: a calibration group held Inf or
+ *     NaN (it is then calibrated on its finite elements).  DEGENERATE: a group
+ *     had no usable range (all zero); its scale and zero-point are 0, its codes 0
+ *     and its fake-quant values +0.
+ *   - Non-finite inputs: NaN quantizes to integer code 0 and to the fp8 NaN byte
+ *     0x7F; +-Inf clamps to the range ends / saturates to +-max-normal.
+ *
+ * Sources, by page title and section:
+ *   [QAT] optirs-gpu 0.3.2 src/optirs_gpu/quantization.rs, "Quantization-Aware
+ *         Training (QAT) primitives" (module docs; QuantParams; fake_quant_int;
+ *         per_channel_params; fake_quant_fp8; fake_quant_backward).
+ *   [DQ]  aprender-train 0.32.0 entrenar/quant/double_quant.rs, "Double
+ *         quantization for QLoRA" (quantize_4bit_double, dequantize_4bit_double).
+ *   [CS]  CS349E 05_quantization_basics.py, demo 4 `block_scaled` ("e8m0").
+ *   [MAR] ferrum-kernels 0.8.0 marlin_repack.rs (zero scale gives fp8 byte 0).
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FQ_ABI_VERSION 1
+
+/* status codes (return values) */
+#define FQ_OK 0
+#define FQ_E_INVALID (-1)
+#define FQ_E_UNSUPPORTED (-2)
+#define FQ_E_DIM (-3)
+#define FQ_E_HIP (-4)
+
+/* data-dependent flag bits (OR-ed into *flags on the device) */
+#define FQ_FLAG_NONFINITE 1u
+#define FQ_FLAG_DEGENERATE 2u
+
+/* [QAT] QuantScheme: symmetric (zero-point 0, restricted range -127..127 / -7..7)
+ * or affine (full range -128..127 / -8..7, zero-point nudged so 0 is exact). */
+enum { FQ_SYM = 0, FQ_AFFINE = 1 };
+/* [QAT] Fp8Format */
+enum { FQ_E4M3 = 0, FQ_E5M2 = 1 };
+/* element type of an input tensor */
+enum { FQ_F32 = 0, FQ_BF16 = 1 };
+
+/* Per-tensor integer parameters as they sit in device memory (16 bytes).
+ * scale, zero_point: [QAT] QuantParams; real_min / real_max: [QAT]
+ * QuantParams::real_min / real_max = dequant(qmin) / dequant(qmax), the STE
+ * window.  &p->real_min is a valid `bounds` argument of fq_ste_backward. */
+typedef struct fq_int_params {
+    float scale;
+    int32_t zero_point;
+    float real_min;
+    float real_max;
+} fq_int_params;
+
+/* ABI version (FQ_ABI_VERSION) and a static string naming a status code. */
+int fq_version(void);
+const char* fq_status_string(int status);
+
+/* Bytes of device workspace that fq_tensor_params_int / fq_fp8_tensor_scale
+ * need for a tensor of n elements (partial results of the grid reduction).  The
+ * workspace is scratch owned by the caller; its contents need no initialisation
+ * and are meaningless afterwards.  Host-only; 0 for n < 1. */
+size_t fq_workspace_bytes(int64_t n);
+
+/* Sizes of the double-quantized 4-bit representation of n values ([DQ]
+ * DoubleQuantized4Bit): packed data ceil(n/2) bytes, one u8 scale per 64-element
+ * block (ceil(n/64)), one fp32 super-scale per 256 blocks.  Host-only; returns
+ * FQ_E_INVALID for n < 1 or a NULL output pointer. */
+int fq_q4dq_sizes(int64_t n, int64_t* packed_bytes, int64_t* num_blocks, int64_t* num_super);
+
+/* Per-tensor calibration ([QAT] QuantParams::per_tensor_minmax then real_min /
+ * real_max): min and max over the finite elements of x[n] (float32), then
+ *   symmetric: scale = absmax / qmax, zero_point = 0;
+ *   affine:    rmin = min(min, 0), rmax = max(max, 0),
+ *              scale = (rmax - rmin) / (qmax - qmin),
+ *              zero_point = clamp(RNE(qmin - rmin / scale), qmin, qmax).
+ * Writes one fq_int_params to `params` (device).  `bits` in {4, 8}; `scheme`
+ * FQ_SYM or FQ_AFFINE.  `workspace` of at least fq_workspace_bytes(n) bytes
+ * (workspace_bytes says how many the caller gives).  Two kernel launches. */
+int fq_tensor_params_int(const float* x, int64_t n, int bits, int scheme, void* workspace,
+                         size_t workspace_bytes, fq_int_params* params, uint32_t* flags,
+                         hipStream_t stream);
+
+/* Per-tensor integer quantize / fake-quant ([QAT] module docs "Integer
+ * quantization", fake_quant_int): q = clamp(RNE(x / scale) + zero_point, qmin,
+ * qmax) (rounded first, zero-point added as an integer), fq = (q - zero_point) *
+ * scale.  params: device fq_int_params (e.g. from fq_tensor_params_int).
+ * codes (may be NULL): bits = 8 -> int8 [n]; bits = 4 -> two codes per byte,
+ * ceil(n/2) bytes, element i in byte i/2, even i in the high nibble (the nibble
+ * order of [DQ] dequantize_4bit_double).  fq (may be NULL): float32 [n].  At
+ * least one of codes / fq.  scale == 0 gives codes 0 and fq +0. */
+int fq_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme,
+                             const fq_int_params* params, void* codes, float* fq,
+                             hipStream_t stream);
+
+/* [QAT] dequant(q) = (q - zero_point) * scale over stored codes (layout as
+ * fq_fake_quant_int_tensor's `codes`). */
+int fq_dequantize_int_tensor(const void* codes, int64_t n, int bits, const fq_int_params* params,
+                             float* out, hipStream_t stream);
+
+/* [QAT] fake_quant_backward (straight-through estimator): grad_in[i] = grad[i]
+ * if lo <= x[i] <= hi, else +0, with (lo, hi) the two device floats at `bounds`
+ * taken in either order.  n_grad must equal n_x (else FQ_E_DIM). */
+int fq_ste_backward(const float* grad, int64_t n_grad, const float* x, int64_t n_x,
+                    const float* bounds, float* grad_in, hipStream_t stream);
+
+/* Per-row (per-channel along axis 0 / per-token) fused calibration + quantize
+ * ([QAT] per_channel_params + fake_quant_int_per_channel, axis 0): every row of
+ * x[rows, cols] (dtype FQ_F32 or FQ_BF16, widened exactly) gets its own scale and
+ * zero-point from its finite min / max, as in fq_tensor_params_int, and is
+ * quantized with them in the same launch (one read of x).
+ * codes (may be NULL): bits = 8 -> int8 [rows, cols]; bits = 4 -> packed,
+ *   ceil(cols/2) bytes per row, element j of a row in byte j/2, even j high
+ *   nibble, an odd row tail leaves the low nibble 0.
+ * fq (may be NULL): float32 [rows, cols].  scale: float32 [rows];
+ * zero_point: int32 [rows] (both required). */
+int fq_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int bits, int scheme,
+                  void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags,
+                  hipStream_t stream);
+
+/* Per-row dequantize of codes stored as fq_quant_rows writes them. */
+int fq_dequantize_rows(const void* codes, int64_t rows, int64_t cols, int bits, const float* scale,
+                       const int32_t* zero_point, float* out, hipStream_t stream);
+
+/* Per-tensor fp8 scale: amax over the finite elements of x[n] (Inf and NaN are
+ * skipped), scale = amax / max-normal (448 for E4M3, 57344 for E5M2; [QAT]
+ * Fp8Format, [MAR] absmax / 448).  Either of scale_e4m3 / scale_e5m2 (device
+ * float, may be NULL, not both) is written from one pass over x.  A zero scale
+ * sets FQ_FLAG_DEGENERATE.  `workspace` as for fq_tensor_params_int. */
+int fq_fp8_tensor_scale(const float* x, int64_t n, void* workspace, size_t workspace_bytes,
+                        float* scale_e4m3, float* scale_e5m2, uint32_t* flags, hipStream_t stream);
+
+/* Saturating fp8 quantize / fake-quant with a per-tensor scale ([QAT]
+ * fake_quant_fp8 and its unified-ULP rounding, ties to even): y = x / scale,
+ * byte = cast(y) (NaN -> 0x7F, +-Inf and |y| rounding above max -> +-max, sign
+ * and -0 kept, fp8 subnormals produced), fq = decode(byte) * scale.
+ * scale: device float; 0 gives byte 0 and fq +0 ([MAR]).  q (may be NULL): u8
+ * [n]; fq (may be NULL): float32 [n]; at least one. */
+int fq_fp8_quantize(const float* x, int64_t n, int fmt, const float* scale, uint8_t* q, float* fq,
+                    hipStream_t stream);
+
+/* fp8 dequantize: out = decode(q) * scale for every byte (E5M2 infinities and
+ * all NaN patterns decode as such). */
+int fq_fp8_dequantize(const uint8_t* q, int64_t n, int fmt, const float* scale, float* out,
+                      hipStream_t stream);
+
+/* 64-element 4-bit absmax blocks with 8-bit double quantization of the block
+ * scales over groups of 256 ([DQ] quantize_4bit_double):
+ *   s_b = absmax_b / 7 over the finite elements of each 64-element block (the last
+ *         block may be partial), code = clamp(RNE(x / s_b), -7, 7) (0 if s_b = 0);
+ *   S_k = max(max of the 256 s_b of group k, 1e-8);
+ *   u_b = clamp(round_half_away(s_b / S_k * 255), 0, 255).
+ * packed: ceil(n/2) bytes (element i in byte i/2, even i high nibble);
+ * qscale: u8 [ceil(n/64)]; super_scale: float32 [ceil(n/16384)];
+ * block_scale (may be NULL): the fp32 s_b; recon (may be NULL): float32 [n] =
+ * dequantize_4bit_double of the result, code * (u_b / 255 * S_k).
+ * One launch, one read of x. */
+int fq_q4dq_quantize(const float* x, int64_t n, uint8_t* packed, uint8_t* qscale,
+                     float* super_scale, float* block_scale, float* recon, uint32_t* flags,
+                     hipStream_t stream);
+
+/* [DQ] dequantize_4bit_double: out[i] = code_i * (u_b / 255 * S_k). */
+int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float* super_scale,
+                       int64_t n, float* out, hipStream_t stream);
+
+/* 32-element fp8 E4M3 blocks with power-of-two scales along each row ([CS]
+ * block_scaled, scale kind "e8m0"): per block of 32 consecutive elements of a row
+ * (a partial block at the row end), A = finite amax (1 if 0), k = frexp exponent
+ * of A, X = 2^max(k - 1 - 8, -127); q = E4M3 cast of x / X (saturating),
+ * e8m0 = log2(X) + 127, fq = decode(q) * X.
+ * x: [rows, cols] FQ_F32 or FQ_BF16; q: u8 [rows, cols]; e8m0: u8
+ * [rows, ceil(cols/32)]; fq (may be NULL): float32 [rows, cols]. */
+int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8m0,
+                  float* fq, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

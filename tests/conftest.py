@@ -51,3 +51,18 @@ def orc():
     from oracle import oracle as o
     o.lib()
     return o
+
+
+@pytest.fixture(scope="session")
+def fqlib():
+    """The HIP binding, on a machine with a GPU (the GPU tests skip elsewhere)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fake_quant_amd import fq
+    return fq
+
+
+def log(msg):
+    """Flushed progress line naming the case about to run on the GPU."""
+    print(msg, flush=True)

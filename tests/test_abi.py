@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libfq.so loads and exports every function include/fq.h declares;
+* pure host helpers (version, status strings, workspace and double-quant sizes);
+* argument checks return their status before anything is enqueued (every call
+  here is rejected by the checks, so no HIP call is made): unsupported widths /
+  schemes / formats / dtypes (the pages' UnsupportedOperation), empty tensors and
+  null buffers (InvalidState for arguments), length mismatch (DimensionMismatch);
+* the oracle and the product share no code.
+"""
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fq.h")
+
+
+@pytest.fixture(scope="module")
+def fq():
+    lib = os.path.join(ROOT, "fake_quant_amd", "libfq.so")
+    if not os.path.exists(lib):
+        from fake_quant_amd import build
+        build.build()
+    from fake_quant_amd import fq as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fq_[a-z0-9_]+)\s*\(", text)))
+
+
+def header_define(name):
+    m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)u?\)?", open(HEADER).read())
+    return int(m.group(1))
+
+
+def test_exports_every_declared_symbol(fq):
+    decl = declared_functions()
+    assert len(decl) == 16
+    for name in decl:
+        assert hasattr(fq.lib(), name), name
+    assert sorted(fq.EXPORTS) == decl
+
+
+def test_constants_match_header(fq):
+    assert fq.fq_version() == header_define("FQ_ABI_VERSION")
+    for name, val in [("FQ_OK", fq.OK), ("FQ_E_INVALID", fq.E_INVALID), ("FQ_E_UNSUPPORTED", fq.E_UNSUPPORTED),
+                      ("FQ_E_DIM", fq.E_DIM), ("FQ_E_HIP", fq.E_HIP),
+                      ("FQ_FLAG_NONFINITE", fq.FLAG_NONFINITE), ("FQ_FLAG_DEGENERATE", fq.FLAG_DEGENERATE)]:
+        assert header_define(name) == val, name
+    for st in (0, -1, -2, -3, -4):
+        assert fq.lib().fq_status_string(st) != b"unknown status"
+    assert fq.lib().fq_status_string(7) == b"unknown status"
+
+
+def test_host_sizes(fq):
+    assert fq.fq_workspace_bytes(0) == 0
+    assert fq.fq_workspace_bytes(1) == 16
+    assert fq.fq_workspace_bytes(1 << 20) == 256 * 16
+    assert fq.fq_workspace_bytes(1 << 40) == 2048 * 16
+    assert fq.fq_q4dq_sizes(1) == (1, 1, 1)
+    assert fq.fq_q4dq_sizes(200) == (100, 4, 1)
+    assert fq.fq_q4dq_sizes(1 << 30) == (1 << 29, 1 << 24, 1 << 16)
+    assert fq.fq_q4dq_sizes(16385) == (8193, 257, 2)
+    with pytest.raises(fq.FqError):
+        fq.fq_q4dq_sizes(0)
+
+
+FAKE = 0x10000  # a non-null, well-aligned address that is never dereferenced
+
+
+def status(fn, *args):
+    return getattr(__import__("fake_quant_amd.fq", fromlist=["x"]).lib(), fn)(*args)
+
+
+def test_argument_checks(fq):
+    L = fq.lib()
+    P = FAKE
+    # unsupported widths / schemes / formats / dtypes
+    for bits in (0, 3, 16):
+        assert L.fq_quant_rows(P, 0, 4, 4, bits, 0, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+        assert L.fq_tensor_params_int(P, 8, bits, 0, P, 1 << 20, P, None, None) == fq.E_UNSUPPORTED
+        assert L.fq_fake_quant_int_tensor(P, 8, bits, 0, P, P, P, None) == fq.E_UNSUPPORTED
+        assert L.fq_dequantize_int_tensor(P, 8, bits, P, P, None) == fq.E_UNSUPPORTED
+        assert L.fq_dequantize_rows(P, 2, 2, bits, P, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_rows(P, 0, 4, 4, 8, 2, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_rows(P, 2, 4, 4, 8, 0, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_fp8_quantize(P, 8, 2, P, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_fp8_dequantize(P, 8, -1, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_mxfp8_rows(P, 5, 1, 32, P, P, P, None) == fq.E_UNSUPPORTED
+    # empty tensors and missing buffers
+    assert L.fq_tensor_params_int(P, 0, 8, 0, P, 16, P, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_int(None, 8, 8, 0, P, 16, P, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_int(P, 8, 8, 0, P, 0, P, None, None) == fq.E_INVALID  # workspace too small
+    assert L.fq_tensor_params_int(P + 4, 8, 8, 0, P + 4, 16, P, None, None) == fq.E_INVALID  # ws misaligned
+    assert L.fq_fake_quant_int_tensor(P, 8, 8, 0, P, None, None, None) == fq.E_INVALID  # no output
+    assert L.fq_fake_quant_int_tensor(P, 0, 8, 0, P, P, P, None) == fq.E_INVALID
+    assert L.fq_quant_rows(P, 0, 0, 4, 8, 0, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_rows(P, 0, 4, 0, 8, 0, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_rows(P, 0, 4, 4, 8, 0, P, P, None, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_rows(P + 1, 0, 4, 4, 8, 0, P, P, P, P, None, None) == fq.E_INVALID  # misaligned f32
+    assert L.fq_fp8_tensor_scale(P, 8, P, 1 << 20, None, None, None, None) == fq.E_INVALID
+    assert L.fq_fp8_quantize(P, 8, 0, P, None, None, None) == fq.E_INVALID
+    assert L.fq_fp8_quantize(P, 8, 0, None, P, P, None) == fq.E_INVALID
+    assert L.fq_fp8_dequantize(P, 0, 0, P, P, None) == fq.E_INVALID
+    assert L.fq_q4dq_quantize(P, 0, P, P, P, None, None, None, None) == fq.E_INVALID
+    assert L.fq_q4dq_quantize(P, 8, None, P, P, None, None, None, None) == fq.E_INVALID
+    assert L.fq_q4dq_dequantize(P, P, None, 8, P, None) == fq.E_INVALID
+    assert L.fq_mxfp8_rows(P, 1, 1, 32, None, P, None, None) == fq.E_INVALID
+    assert L.fq_mxfp8_rows(P, 1, 0, 32, P, P, None, None) == fq.E_INVALID
+    # STE: length mismatch, empty
+    assert L.fq_ste_backward(P, 3, P, 2, P, P, None) == fq.E_DIM
+    assert L.fq_ste_backward(P, 0, P, 0, P, P, None) == fq.E_INVALID
+    assert L.fq_ste_backward(None, 2, P, 2, P, P, None) == fq.E_INVALID
+
+
+def test_binding_raises_on_error(fq):
+    with pytest.raises(fq.FqError) as ei:
+        fq.fq_ste_backward(FAKE, 3, FAKE, 2, FAKE, FAKE, stream=None)
+    assert ei.value.status == fq.E_DIM
+
+
+def test_oracle_and_product_share_no_code():
+    """Neither side imports, includes or links the other."""
+    prod = []
+    for d, _, files in os.walk(os.path.join(ROOT, "fake_quant_amd")):
+        prod += [os.path.join(d, f) for f in files if f.endswith((".py", ".hip", ".h"))]
+    for p in prod:
+        text = open(p).read()
+        assert "oracle" not in re.findall(r"^\s*(?:from|import|#include)\s+\S*", text, flags=re.M).__str__(), p
+        assert "liboracle" not in text and "orc_" not in text, p
+    for p in ("oracle.c", "oracle.py"):
+        text = open(os.path.join(ROOT, "oracle", p)).read()
+        assert "fake_quant_amd" not in text and "libfq" not in text and "fq.h" not in text, p
+        assert "fqk::" not in text and "fq_device" not in text, p

@@ -1,0 +1,78 @@
+"""Host-side checks of bench.py and of the binding's pre-launch guards (CPU only:
+no kernel runs; the library's compute entry points are replaced by a recorder)."""
+import pytest
+import torch
+
+import bench
+from fake_quant_amd import fq, synthetic
+
+TINY = {
+    "tensor": dict(n=1000),
+    "rows_f32": dict(rows=8, cols=40),
+    "fp8": dict(n=3001),
+    "q4dq": dict(n=20001),
+    "rows_bf16": dict(rows=4, cols=64),
+}
+
+
+class RecordingLib:
+    """Stands in for libfq.so: host-only helpers go to the real library, compute
+    entry points are recorded and report success without launching anything."""
+
+    def __init__(self, real):
+        self.real = real
+        self.calls = []
+
+    def __getattr__(self, name):
+        if name in ("fq_workspace_bytes", "fq_q4dq_sizes", "fq_status_string", "fq_version"):
+            return getattr(self.real, name)
+
+        def rec(*args):
+            self.calls.append(name)
+            return 0
+        return rec
+
+
+def cpu_need(name, what, t, nbytes):
+    if t is None or isinstance(t, int):
+        return
+    assert t.is_contiguous(), (name, what)
+    have = t.numel() * t.element_size()
+    assert have >= nbytes, f"{name}: {what} holds {have} bytes, the call touches {nbytes}"
+
+
+def test_every_bench_op_passes_buffers_that_fit(monkeypatch):
+    monkeypatch.setattr(synthetic, "FULL", TINY)
+    recorder = RecordingLib(fq.lib())
+    monkeypatch.setattr(fq, "_lib", recorder)
+    monkeypatch.setattr(fq, "_need", cpu_need)
+    monkeypatch.setattr(fq, "_stream", lambda stream=None: None)
+    ops = bench.build_ops(fq, synthetic, torch, None, dev="cpu")
+    assert len(ops) == 16
+    for op in ops:
+        op.fn()
+    assert len(recorder.calls) == 16
+    assert sum(op.nbytes for op in ops) > 0
+
+
+def test_binding_guards_reject_bad_buffers():
+    x = torch.zeros(16)
+    with pytest.raises(fq.FqError, match="not a GPU tensor"):
+        fq.fq_fp8_quantize(x, 16, fq.E4M3, x[:1], None, x)
+    fq_need = fq._need
+    # size and contiguity checks (checked ahead of the device check on a fake view)
+    class Fake:
+        is_cuda = True
+        def __init__(self, n, contig=True):
+            self.n, self.contig = n, contig
+        def is_contiguous(self):
+            return self.contig
+        def numel(self):
+            return self.n
+        def element_size(self):
+            return 4
+    with pytest.raises(fq.FqError, match="holds 60 bytes"):
+        fq_need("f", "out", Fake(15), 64)
+    with pytest.raises(fq.FqError, match="not contiguous"):
+        fq_need("f", "out", Fake(16, contig=False), 64)
+    fq_need("f", "out", Fake(16), 64)
