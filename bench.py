@@ -291,6 +291,10 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     log(f"{len(ops)} ops per step; warmup {args.warmup}")
+    for op in ops:  # first pass one op at a time, so a failure names its op
+        log(f"first call: {op.name}")
+        op.fn()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         for op in ops:
             op.fn()
