@@ -335,10 +335,11 @@ def main():
                     avg_launch_us=round(per_op_ms[dom_i] * 1e3, 2), bytes_per_launch=dom.nbytes)
 
     cpu = None
+    n_ops = len(ops)
     if not args.no_cpu:
         from oracle import oracle as orc
         log("timing the CPU oracle on a bounded sample")
-        del ops
+        del ops, dom
         torch.cuda.empty_cache()
         cpu = cpu_baseline(orc, syn, torch, args.only)
 
@@ -360,7 +361,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "config": {"workload": workloads, "bytes_per_step": step_bytes, "ops_per_step": len(ops),
+        "config": {"workload": workloads, "bytes_per_step": step_bytes, "ops_per_step": n_ops,
                    "wall_s_timed": round(t_wall, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
