@@ -8,7 +8,9 @@
 // encodes every element as byte 0.
 //
 // Chunks of four elements: one 16-byte load of x, one 4-byte store of codes,
-// one 16-byte store of the fake-quant values; grid-stride, four chunks in flight.
+// one 16-byte store of the fake-quant values; one chunk per thread over a grid
+// covering the tensor.  The quotient mode (zero scale / exact fast quotient /
+// true division) is decided once per launch from the device-resident scale.
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -18,63 +20,76 @@ namespace {
 
 constexpr int kB = fqh::kBlock;
 
-template <int FMT>
-struct Fp8QuantOp {
-    ExactDiv div;
-    float scale;
-    bool zero;
-    __device__ __forceinline__ explicit Fp8QuantOp(float s)
-        : div(s == 0.0f ? 1.0f : s), scale(s), zero(s == 0.0f) {}
-    __device__ __forceinline__ uint32_t code(float x) const {
-        if (zero) return 0u;
-        return fp8_encode<FMT>(div(x));
-    }
-    // fake-quant value of a code produced by code(): NaN byte -> NaN
-    __device__ __forceinline__ float value(uint32_t b) const {
-        float v = fp8_decode_finite<FMT>(b) * scale;
-        return (b == 0x7Fu) ? __builtin_nanf("") : v;
-    }
-};
+// Quotient modes, chosen once per launch from the (device-resident) scale:
+// zero scale -> every byte 0; divisor in the exact-quotient window -> Markstein
+// corrections; otherwise the compiler's correctly rounded division.
+enum { kZero = 0, kQuick = 1, kTrue = 2 };
 
-template <int FMT, bool AL>
-__global__ __launch_bounds__(kB) void k_fp8_quant(const float* __restrict__ x, int64_t n,
-                                                  const float* __restrict__ scale_p,
-                                                  uint8_t* __restrict__ q, float* __restrict__ fq) {
-    const Fp8QuantOp<FMT> op(*scale_p);
+template <int FMT, int MODE>
+__device__ __forceinline__ uint32_t fp8_code(float x, const ExactDiv& d) {
+    if (MODE == kZero) return 0u;
+    return fp8_encode<FMT>(MODE == kQuick ? d.quick(x) : x / d.s);
+}
+// fake-quant value of a code produced above (the NaN byte decodes to NaN)
+template <int FMT>
+__device__ __forceinline__ float fp8_value(uint32_t b, float scale) {
+    float v = fp8_decode_finite<FMT>(b) * scale;
+    return (b == 0x7Fu) ? __builtin_nanf("") : v;
+}
+
+template <int FMT, bool AL, int MODE>
+__device__ __forceinline__ void fp8_quant_loop(const float* __restrict__ x, int64_t n, const ExactDiv& d,
+                                               float scale, uint8_t* __restrict__ q, float* __restrict__ fq) {
     const int64_t nfull = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * kB;
     int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
     auto chunk = [&](int64_t cc, float4 v) {
-        uint32_t b0 = op.code(v.x), b1 = op.code(v.y), b2 = op.code(v.z), b3 = op.code(v.w);
+        uint32_t b0 = fp8_code<FMT, MODE>(v.x, d), b1 = fp8_code<FMT, MODE>(v.y, d);
+        uint32_t b2 = fp8_code<FMT, MODE>(v.z, d), b3 = fp8_code<FMT, MODE>(v.w, d);
         if (q) reinterpret_cast<uint32_t*>(q)[cc] = pack4(b0, b1, b2, b3);
         if (fq)
-            reinterpret_cast<float4*>(fq)[cc] = make_float4(op.value(b0), op.value(b1), op.value(b2), op.value(b3));
+            reinterpret_cast<float4*>(fq)[cc] = make_float4(fp8_value<FMT>(b0, scale), fp8_value<FMT>(b1, scale),
+                                                            fp8_value<FMT>(b2, scale), fp8_value<FMT>(b3, scale));
     };
     if (AL) {
+        const float4* xv = reinterpret_cast<const float4*>(x);
         for (; c + 3 * stride < nfull; c += 4 * stride) {
-            const float4* xv = reinterpret_cast<const float4*>(x);
             float4 v0 = xv[c], v1 = xv[c + stride], v2 = xv[c + 2 * stride], v3 = xv[c + 3 * stride];
             chunk(c, v0);
             chunk(c + stride, v1);
             chunk(c + 2 * stride, v2);
             chunk(c + 3 * stride, v3);
         }
-        for (; c < nfull; c += stride) chunk(c, reinterpret_cast<const float4*>(x)[c]);
+        for (; c < nfull; c += stride) chunk(c, xv[c]);
     } else {
         for (; c < nfull; c += stride) {
             for (int e = 0; e < 4; ++e) {
-                uint32_t b = op.code(x[4 * c + e]);
+                uint32_t b = fp8_code<FMT, MODE>(x[4 * c + e], d);
                 if (q) q[4 * c + e] = (uint8_t)b;
-                if (fq) fq[4 * c + e] = op.value(b);
+                if (fq) fq[4 * c + e] = fp8_value<FMT>(b, scale);
             }
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
         int64_t i = 4 * nfull + threadIdx.x;
-        uint32_t b = op.code(x[i]);
+        uint32_t b = fp8_code<FMT, MODE>(x[i], d);
         if (q) q[i] = (uint8_t)b;
-        if (fq) fq[i] = op.value(b);
+        if (fq) fq[i] = fp8_value<FMT>(b, scale);
     }
+}
+
+template <int FMT, bool AL>
+__global__ __launch_bounds__(kB) void k_fp8_quant(const float* __restrict__ x, int64_t n,
+                                                  const float* __restrict__ scale_p,
+                                                  uint8_t* __restrict__ q, float* __restrict__ fq) {
+    const float s = *scale_p;
+    const ExactDiv d(s == 0.0f ? 1.0f : s);
+    if (s == 0.0f)
+        fp8_quant_loop<FMT, AL, kZero>(x, n, d, s, q, fq);
+    else if (d.fast)
+        fp8_quant_loop<FMT, AL, kQuick>(x, n, d, s, q, fq);
+    else
+        fp8_quant_loop<FMT, AL, kTrue>(x, n, d, s, q, fq);
 }
 
 template <int FMT, bool AL>
@@ -85,6 +100,21 @@ __global__ __launch_bounds__(kB) void k_fp8_dequant(const uint8_t* __restrict__ 
     const int64_t nfull = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * kB;
     int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
+    if (AL) {
+        const uint32_t* qw = reinterpret_cast<const uint32_t*>(q);
+        float4* ov = reinterpret_cast<float4*>(out);
+        auto dec4 = [&](uint32_t w) {
+            return make_float4(fp8_decode<FMT>(w & 0xFFu) * s, fp8_decode<FMT>((w >> 8) & 0xFFu) * s,
+                               fp8_decode<FMT>((w >> 16) & 0xFFu) * s, fp8_decode<FMT>(w >> 24) * s);
+        };
+        for (; c + 3 * stride < nfull; c += 4 * stride) {
+            uint32_t w0 = qw[c], w1 = qw[c + stride], w2 = qw[c + 2 * stride], w3 = qw[c + 3 * stride];
+            ov[c] = dec4(w0);
+            ov[c + stride] = dec4(w1);
+            ov[c + 2 * stride] = dec4(w2);
+            ov[c + 3 * stride] = dec4(w3);
+        }
+    }
     for (; c < nfull; c += stride) {
         uint32_t w;
         if (AL) {
@@ -113,7 +143,7 @@ __global__ __launch_bounds__(kB) void k_fp8_dequant(const uint8_t* __restrict__ 
 template <int FMT>
 void launch_quant(const float* x, int64_t n, const float* scale, uint8_t* q, float* fq, hipStream_t st) {
     const bool al = fqh::aligned(x, 16) && fqh::aligned(q, 4) && fqh::aligned(fq, 16);
-    const unsigned G = fqh::grid_for((n + 3) / 4, 4 * kB, 8);
+    const unsigned G = fqh::grid_all((n + 3) / 4, kB);
     if (al) k_fp8_quant<FMT, true><<<G, kB, 0, st>>>(x, n, scale, q, fq);
     else k_fp8_quant<FMT, false><<<G, kB, 0, st>>>(x, n, scale, q, fq);
 }
@@ -121,7 +151,7 @@ void launch_quant(const float* x, int64_t n, const float* scale, uint8_t* q, flo
 template <int FMT>
 void launch_dequant(const uint8_t* q, int64_t n, const float* scale, float* out, hipStream_t st) {
     const bool al = fqh::aligned(q, 4) && fqh::aligned(out, 16);
-    const unsigned G = fqh::grid_for((n + 3) / 4, kB, 8);
+    const unsigned G = fqh::grid_all((n + 3) / 4, kB);
     if (al) k_fp8_dequant<FMT, true><<<G, kB, 0, st>>>(q, n, scale, out);
     else k_fp8_dequant<FMT, false><<<G, kB, 0, st>>>(q, n, scale, out);
 }

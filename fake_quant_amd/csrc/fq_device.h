@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fqk {
 
 constexpr int kWave = 64;
@@ -61,6 +63,41 @@ struct ExactDiv {
     __device__ __forceinline__ float operator()(float x) const { return fast ? quick(x) : x / s; }
 };
 
+// The two Markstein corrections alone, for callers that know x is finite and
+// |x/s| is bounded by the group's own range (no overflow, no NaN): 5 operations.
+// A zero x may come back as +0; callers that need the sign of zero use ExactDiv.
+__device__ __forceinline__ float quick_div(float x, float s, float y) {
+    float q = x * y;
+    float r = __builtin_fmaf(-s, q, x);
+    q = __builtin_fmaf(r, y, q);
+    r = __builtin_fmaf(-s, q, x);
+    return __builtin_fmaf(r, y, q);
+}
+__device__ __forceinline__ bool fast_divisor(float s) { return (s >= 0x1p-60f) && (s <= 0x1p60f); }
+
+// Adding 1.5 * 2^23 to a binary32 v with |v| < 2^22 leaves round-half-even(v) in
+// the low mantissa bits: the sum's ulp is 1 and the constant is even, so
+// RNE(v + kMagic) = RNE(v) + kMagic exactly; (sum - kMagic) is RNE(v) as a float
+// (+0 for a zero) and the low bits of the sum's pattern hold RNE(v) in two's
+// complement.
+constexpr float kMagic = 12582912.0f;
+constexpr uint32_t kMagicBits = 0x4B400000u;
+
+// compile-time loop: f(std::integral_constant<int, I>{}) for I in [0, N)
+template <int I, int N>
+struct StaticFor {
+    template <class F>
+    __device__ __forceinline__ static void run(F&& f) {
+        f(std::integral_constant<int, I>{});
+        StaticFor<I + 1, N>::run(f);
+    }
+};
+template <int N>
+struct StaticFor<N, N> {
+    template <class F>
+    __device__ __forceinline__ static void run(F&&) {}
+};
+
 // ---------------------------------------------------------------------------
 // bfloat16 -> binary32 (exact: bf16 is the upper half of a binary32)
 // ---------------------------------------------------------------------------
@@ -78,6 +115,15 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return as_f(dpp_u<CTRL>(as_u(v)));
+}
+// lane J of each 16-lane row, broadcast to the whole row (DPP row_newbcast)
+template <int J>
+__device__ __forceinline__ float row_bcast_f(float v) {
+    return dpp_f<0x150 + J>(v);
+}
+template <int J>
+__device__ __forceinline__ uint32_t row_bcast_u(uint32_t v) {
+    return dpp_u<0x150 + J>(v);
 }
 constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
@@ -217,6 +263,15 @@ struct IntQ {
     __device__ __forceinline__ float offset(float x) const {
         if (zero) return nan_off;  // code 0 (zp is 0 for degenerate groups)
         float t = div(x);
+        float r = fminf(fmaxf(rintf(t), lo), hi) + 0.0f;
+        return (t != t) ? nan_off : r;
+    }
+    // offset with the quotient mode fixed at compile time: 0 = zero scale,
+    // 1 = divisor in the exact-quotient window, 2 = true division
+    template <int MODE>
+    __device__ __forceinline__ float offset_m(float x) const {
+        if (MODE == 0) return nan_off;
+        float t = MODE == 1 ? div.quick(x) : x / div.s;
         float r = fminf(fmaxf(rintf(t), lo), hi) + 0.0f;
         return (t != t) ? nan_off : r;
     }

@@ -33,11 +33,27 @@ inline unsigned grid_for(int64_t items, int64_t per_block, int blocks_per_cu) {
     return (unsigned)want;
 }
 
-// Blocks of the tensor-scope reduction (partials in the workspace).
-constexpr int kMaxReduceBlocks = 2048;
+// One work item per thread over the whole index space: on MI355X many short
+// workgroups that sweep memory in order stream faster than a capped grid with a
+// grid-stride loop.  Grids beyond 2^31 - 1 blocks fall back to the kernels'
+// grid-stride loop.
+inline unsigned grid_all(int64_t items, int64_t per_block) {
+    int64_t want = (items + per_block - 1) / per_block;
+    if (want > 0x7FFFFFFF) want = 0x7FFFFFFF;
+    if (want < 1) want = 1;
+    return (unsigned)want;
+}
+
+// Tensor-scope reduction: the tensor is cut into tiles of kReduceTile
+// consecutive 16-byte chunks (four per thread); block b reduces tiles b, b + G,
+// ... into one partial in the workspace, with G at most kMaxReduceBlocks.
+constexpr int kReduceChunks = 4;
+constexpr int64_t kReduceTile = (int64_t)kReduceChunks * kBlock;
+constexpr int64_t kMaxReduceBlocks = 16384;
+constexpr int kFinalThreads = 1024;
 inline unsigned reduce_blocks(int64_t n) {
     int64_t chunks = (n + 3) / 4;
-    int64_t want = (chunks + 4 * kBlock - 1) / (4 * kBlock);
+    int64_t want = (chunks + kReduceTile - 1) / kReduceTile;
     if (want > kMaxReduceBlocks) want = kMaxReduceBlocks;
     if (want < 1) want = 1;
     return (unsigned)want;

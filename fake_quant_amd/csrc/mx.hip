@@ -11,7 +11,7 @@
 //
 // Vector path (cols a multiple of 32, aligned buffers): a block is 64 bytes of
 // bf16 = four 16-byte lane loads (a DPP quad) or 128 bytes of fp32 = eight lanes;
-// grid-stride over 16-byte vectors of the flattened tensor.
+// one 16-byte vector per thread over a grid covering the flattened tensor.
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -125,7 +125,7 @@ int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t*
                     fqh::aligned(fq, 16);
     if (al) {
         const int64_t nvec = rows * cols / N;
-        const unsigned G = fqh::grid_for(nvec, 4 * kB, 8);
+        const unsigned G = fqh::grid_all(nvec, kB);
         if (dtype == FQ_F32) k_mx_vec<FQ_F32><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
         else k_mx_vec<FQ_BF16><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
     } else {

@@ -26,7 +26,11 @@ constexpr int kWaves = kB / kWave;
 constexpr int kBlockElems = 64;
 constexpr int kGroup = 256;                         // block scales per super-scale
 constexpr int kSuperElems = kBlockElems * kGroup;   // 16384
-constexpr int kJ = kSuperElems / (4 * kB);          // 16 float4 per thread
+constexpr int kJ = kSuperElems / (4 * kB);          // 16 float4 per thread (generic kernels)
+#ifndef FQ_Q4_THREADS
+#define FQ_Q4_THREADS 1024
+#endif
+constexpr int kQ4Threads = FQ_Q4_THREADS;            // threads per super-block (full kernel)
 
 // code of x in a block with scale s (s > 0): clamp(RNE(x / s), -7, 7), NaN -> 0
 __device__ __forceinline__ float q4_code(const ExactDiv& d, float x) {
@@ -46,75 +50,139 @@ __device__ __forceinline__ uint32_t u8_scale(float s, float S) {
 __device__ __forceinline__ float recon_scale(uint32_t u, float S) { return (float)u / 255.0f * S; }
 
 // Full super-block, 16-byte aligned buffers.
-__global__ __launch_bounds__(kB) void k_q4dq_full(const float* __restrict__ x, uint8_t* __restrict__ packed,
-                                                  uint8_t* __restrict__ qscale, float* __restrict__ super_scale,
-                                                  float* __restrict__ block_scale, float* __restrict__ recon,
-                                                  uint32_t* __restrict__ flags) {
+//
+// Per thread: 16 float4 (elements of 16 different blocks).  Per 64-element
+// block (a 16-lane row at step j): the absmax is a DPP row maximum; the block's
+// scale s = absmax / 7 and its reciprocal are computed once, by the row's lane j,
+// and broadcast back to the row with DPP row_newbcast -- one pair of true
+// divisions per lane per super-block instead of one per float4.  Codes are
+// RNE(fl(x / s)) clamped to +-7 (kMagic rounding); the packed nibbles stay in
+// registers for the reconstruction written after the super-scale is known.
+// A wave holding Inf / NaN takes the general per-element rule (finite absmax,
+// NaN -> 0, +-Inf -> +-7).
+__device__ __forceinline__ uint32_t abs_bits(float v) { return as_u(v) & 0x7FFFFFFFu; }
+__device__ __forceinline__ uint32_t fin_bits(float v) {
+    uint32_t a = abs_bits(v);
+    return a < 0x7F800000u ? a : 0u;
+}
+// two nibbles from two magic-rounded floats (low 4 bits of their patterns)
+__device__ __forceinline__ uint32_t nib_pair(float f0, float f1) {
+    return __builtin_amdgcn_ubfe(as_u(f0), 0, 4) << 4 | __builtin_amdgcn_ubfe(as_u(f1), 0, 4);
+}
+// general code of one element, as an int in [-7, 7]
+__device__ __forceinline__ int q4_general(float x, float s, float y, bool fast) {
+    if (s == 0.0f) return 0;
+    ExactDiv d(s);
+    d.y = y;
+    d.fast = fast;
+    return (int)q4_code(d, x);
+}
+
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, uint8_t* __restrict__ packed,
+                                                   uint8_t* __restrict__ qscale, float* __restrict__ super_scale,
+                                                   float* __restrict__ block_scale, float* __restrict__ recon,
+                                                   uint32_t* __restrict__ flags) {
+    constexpr int J = kSuperElems / (4 * TPB);  // float4 per thread
+    constexpr int RW = TPB / 16;                // 16-lane rows per workgroup
+    constexpr int NW = TPB / kWave;             // waves per workgroup
     const int64_t sb = blockIdx.x;
     const int t = threadIdx.x;
+    const int lrow = t & 15;  // position inside the 16-lane row
     const float4* xv = reinterpret_cast<const float4*>(x + sb * kSuperElems);
-    float4 v[kJ];
+    float4 v[J];
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) v[j] = xv[j * kB + t];
+    for (int j = 0; j < J; ++j) v[j] = xv[j * TPB + t];
 
     __shared__ float s_scale[kGroup];
     __shared__ uint32_t s_u8[kGroup / 4];
-    __shared__ float s_max[kWaves];
+    __shared__ float s_max[NW];
 
-    float smax = 0.0f;
-    uint32_t nf = 0;
-    float sblk[kJ];
-    uint16_t* pk = reinterpret_cast<uint16_t*>(packed + sb * (kSuperElems / 2));
+    // Block absmax bits (raw: Inf / NaN included); lane lrow (< J) of each row
+    // keeps the maximum of block j = lrow of that row.  The wave's non-finite
+    // marker picks the finite-only recomputation.
+    uint32_t nf = 0, my_am = 0;
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-        uint32_t a0 = as_u(v[j].x) & 0x7FFFFFFFu, a1 = as_u(v[j].y) & 0x7FFFFFFFu;
-        uint32_t a2 = as_u(v[j].z) & 0x7FFFFFFFu, a3 = as_u(v[j].w) & 0x7FFFFFFFu;
-        nf = max(nf, max(max(a0, a1), max(a2, a3)));
-        uint32_t am = max(max(a0 < 0x7F800000u ? a0 : 0u, a1 < 0x7F800000u ? a1 : 0u),
-                          max(a2 < 0x7F800000u ? a2 : 0u, a3 < 0x7F800000u ? a3 : 0u));
-        am = row16_max_u(am);
-        float s = as_f(am) / 7.0f;
-        sblk[j] = s;
-        smax = fmaxf(smax, s);
-        float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
-        if (s != 0.0f) {
-            ExactDiv d(s);
-            c0 = q4_code(d, v[j].x);
-            c1 = q4_code(d, v[j].y);
-            c2 = q4_code(d, v[j].z);
-            c3 = q4_code(d, v[j].w);
-        }
-        pk[j * kB + t] = (uint16_t)(nib2((int)c0, (int)c1) | (nib2((int)c2, (int)c3) << 8));
-        v[j] = make_float4(c0, c1, c2, c3);  // keep the codes for the reconstruction
-        if ((t & 15) == 0) s_scale[j * 16 + (t >> 4)] = s;
+    for (int j = 0; j < J; ++j) {
+        uint32_t m = max(max(abs_bits(v[j].x), abs_bits(v[j].y)), max(abs_bits(v[j].z), abs_bits(v[j].w)));
+        nf = max(nf, m);
+        m = row16_max_u(m);
+        my_am = (lrow == j) ? m : my_am;
     }
+    const bool wave_nf = __any(nf >= 0x7F800000u);
+    if (wave_nf) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            uint32_t m = max(max(fin_bits(v[j].x), fin_bits(v[j].y)), max(fin_bits(v[j].z), fin_bits(v[j].w)));
+            m = row16_max_u(m);
+            my_am = (lrow == j) ? m : my_am;
+        }
+    }
+    const float my_s = as_f(my_am) / 7.0f;  // lanes lrow >= J hold 0 (neutral below)
+    const float my_y = 1.0f / (my_s == 0.0f ? 1.0f : my_s);
+    const bool all_fast = __all(lrow >= J || fast_divisor(my_s)) && !wave_nf;
+
+    uint32_t pc[J];  // packed codes of each float4 (16 bits)
+    uint16_t* pk = reinterpret_cast<uint16_t*>(packed + sb * (kSuperElems / 2));
+    if (all_fast) {
+        StaticFor<0, J>::run([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const float s = row_bcast_f<j>(my_s);
+            const float y = row_bcast_f<j>(my_y);
+            const float f0 = fminf(fmaxf(quick_div(v[j].x, s, y), -7.0f), 7.0f) + kMagic;
+            const float f1 = fminf(fmaxf(quick_div(v[j].y, s, y), -7.0f), 7.0f) + kMagic;
+            const float f2 = fminf(fmaxf(quick_div(v[j].z, s, y), -7.0f), 7.0f) + kMagic;
+            const float f3 = fminf(fmaxf(quick_div(v[j].w, s, y), -7.0f), 7.0f) + kMagic;
+            const uint32_t w = nib_pair(f0, f1) | (nib_pair(f2, f3) << 8);
+            pk[j * TPB + t] = (uint16_t)w;
+            pc[j] = w;
+        });
+    } else {
+        StaticFor<0, J>::run([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const float s = row_bcast_f<j>(my_s);
+            const float y = row_bcast_f<j>(my_y);
+            const bool fast = fast_divisor(s);
+            const uint32_t w = nib2(q4_general(v[j].x, s, y, fast), q4_general(v[j].y, s, y, fast)) |
+                               (nib2(q4_general(v[j].z, s, y, fast), q4_general(v[j].w, s, y, fast)) << 8);
+            pk[j * TPB + t] = (uint16_t)w;
+            pc[j] = w;
+        });
+    }
+
     // super-scale: max over the 256 block scales, floored at 1e-8
-    smax = fmaxf(smax, __shfl_xor(smax, 16));
-    smax = fmaxf(smax, __shfl_xor(smax, 32));
-    nf = wave_max_u(nf);
-    if ((t & 63) == 0) s_max[t >> 6] = smax;
-    if (flags && (t & 63) == 0 && nf >= 0x7F800000u) atomicOr(flags, FQ_FLAG_NONFINITE);
+    const float wmax = wave_max_f(my_s);
+    if ((t & 63) == 0) s_max[t >> 6] = wmax;
+    if (flags && (t & 63) == 0 && wave_nf) atomicOr(flags, FQ_FLAG_NONFINITE);
+    if (lrow < J) s_scale[lrow * RW + (t >> 4)] = my_s;  // block (j = lrow, this row)
     __syncthreads();
-    float S = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    float S = s_max[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) S = fmaxf(S, s_max[i]);
     S = fmaxf(S, 1e-8f);
     if (t == 0) super_scale[sb] = S;
-    if (block_scale) block_scale[sb * kGroup + t] = s_scale[t];
-    {
+    if (t < kGroup) {
+        if (block_scale) block_scale[sb * kGroup + t] = s_scale[t];
         // u8 scale codes: thread t encodes block t, four per word
         uint32_t u = u8_scale(s_scale[t], S);
         uint32_t u1 = __shfl_down(u, 1), u2 = __shfl_down(u, 2), u3 = __shfl_down(u, 3);
         if ((t & 3) == 0) s_u8[t >> 2] = u | (u1 << 8) | (u2 << 16) | (u3 << 24);
     }
+    const float my_sh = recon_scale(u8_scale(my_s, S), S);
     __syncthreads();
     if (t < kGroup / 4) reinterpret_cast<uint32_t*>(qscale + sb * kGroup)[t] = s_u8[t];
     if (!recon) return;
     float4* rv = reinterpret_cast<float4*>(recon + sb * kSuperElems);
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-        uint32_t u = u8_scale(sblk[j], S);
-        float sh = recon_scale(u, S);
-        rv[j * kB + t] = make_float4(v[j].x * sh, v[j].y * sh, v[j].z * sh, v[j].w * sh);
-    }
+    StaticFor<0, J>::run([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        const float sh = row_bcast_f<j>(my_sh);
+        const uint32_t w = pc[j];
+        const float c0 = (float)(int)__builtin_amdgcn_sbfe((int)w, 4, 4);
+        const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w, 0, 4);
+        const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w, 12, 4);
+        const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w, 8, 4);
+        rv[j * TPB + t] = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+    });
 }
 
 // Any super-block (partial, unaligned): element-wise, one thread per element
@@ -179,36 +247,58 @@ __global__ __launch_bounds__(kB) void k_q4dq_any(const float* __restrict__ x, in
     }
 }
 
-// [DQ] dequantize_4bit_double: one workgroup per super-block.
-template <bool FULL>
-__global__ __launch_bounds__(kB) void k_q4dq_dequant(const uint8_t* __restrict__ packed,
-                                                     const uint8_t* __restrict__ qscale,
-                                                     const float* __restrict__ super_scale, int64_t n,
-                                                     int64_t sb0, float* __restrict__ out) {
+// [DQ] dequantize_4bit_double, full super-block: thread t reconstructs block t's
+// scale into LDS, every packed word is loaded up front, then each float4 is
+// decoded with its block's scale.
+template <int TPB>
+__global__ __launch_bounds__(TPB) void k_q4dq_dequant_full(const uint8_t* __restrict__ packed,
+                                                           const uint8_t* __restrict__ qscale,
+                                                           const float* __restrict__ super_scale,
+                                                           float* __restrict__ out) {
+    constexpr int J = kSuperElems / (4 * TPB);
+    constexpr int RW = TPB / 16;
+    const int64_t sb = blockIdx.x;
+    const int t = threadIdx.x;
+    __shared__ float s_sh[kGroup];
+    const uint16_t* pk = reinterpret_cast<const uint16_t*>(packed + sb * (kSuperElems / 2));
+    uint32_t w[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) w[j] = pk[j * TPB + t];
+    if (t < kGroup) s_sh[t] = recon_scale(qscale[sb * kGroup + t], super_scale[sb]);
+    __syncthreads();
+    float4* o = reinterpret_cast<float4*>(out + sb * kSuperElems);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const float sh = s_sh[j * RW + (t >> 4)];
+        const float c0 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 4, 4);
+        const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 0, 4);
+        const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 12, 4);
+        const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 8, 4);
+        o[j * TPB + t] = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+    }
+}
+
+// [DQ] dequantize_4bit_double, any super-block (partial or unaligned).
+__global__ __launch_bounds__(kB) void k_q4dq_dequant_any(const uint8_t* __restrict__ packed,
+                                                         const uint8_t* __restrict__ qscale,
+                                                         const float* __restrict__ super_scale, int64_t n,
+                                                         int64_t sb0, float* __restrict__ out) {
     const int64_t sb = sb0 + blockIdx.x;
     const int t = threadIdx.x;
     const float S = super_scale[sb];
     const int64_t base = sb * kSuperElems;
     const int64_t nb = (n + kBlockElems - 1) / kBlockElems;
-#pragma unroll 4
     for (int j = 0; j < kJ; ++j) {
         const int64_t b = sb * kGroup + j * 16 + (t >> 4);
-        const int64_t e0 = base + 4 * ((int64_t)j * kB + t);
-        if (!FULL && b >= nb) continue;
+        if (b >= nb) continue;
         const float sh = recon_scale(qscale[b], S);
-        if (FULL) {
-            uint32_t w = reinterpret_cast<const uint16_t*>(packed + base / 2)[j * kB + t];
-            float c0 = (float)(((int)(w << 24)) >> 28), c1 = (float)(((int)(w << 28)) >> 28);
-            float c2 = (float)(((int)(w << 16)) >> 28), c3 = (float)(((int)(w << 20)) >> 28);
-            reinterpret_cast<float4*>(out + base)[j * kB + t] = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
-        } else {
-            for (int e = 0; e < 4; ++e) {
-                int64_t i = e0 + e;
-                if (i >= n) break;
-                uint32_t byte = packed[i >> 1];
-                uint32_t nib = (i & 1) ? (byte & 0xFu) : (byte >> 4);
-                out[i] = (float)(((int)(nib << 28)) >> 28) * sh;
-            }
+        const int64_t e0 = base + 4 * ((int64_t)j * kB + t);
+        for (int e = 0; e < 4; ++e) {
+            int64_t i = e0 + e;
+            if (i >= n) break;
+            uint32_t byte = packed[i >> 1];
+            uint32_t nib = (i & 1) ? (byte & 0xFu) : (byte >> 4);
+            out[i] = (float)(((int)(nib << 28)) >> 28) * sh;
         }
     }
 }
@@ -231,8 +321,8 @@ int fq_q4dq_quantize(const float* x, int64_t n, uint8_t* packed, uint8_t* qscale
                     fqh::aligned(recon, 16);
     int64_t done = 0;
     if (al && nfull > 0) {
-        k_q4dq_full<<<(unsigned)nfull, kB, 0, stream>>>(x, packed, qscale, super_scale, block_scale, recon,
-                                                       flags);
+        k_q4dq_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, 0, stream>>>(x, packed, qscale, super_scale,
+                                                                           block_scale, recon, flags);
         done = nfull;
     }
     if (done < nsb)
@@ -251,12 +341,12 @@ int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float
     const bool al = fqh::aligned(packed, 2) && fqh::aligned(out, 16);
     int64_t done = 0;
     if (al && nfull > 0) {
-        k_q4dq_dequant<true><<<(unsigned)nfull, kB, 0, stream>>>(packed, qscale, super_scale, n, 0, out);
+        k_q4dq_dequant_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, 0, stream>>>(packed, qscale, super_scale,
+                                                                                   out);
         done = nfull;
     }
     if (done < nsb)
-        k_q4dq_dequant<false><<<(unsigned)(nsb - done), kB, 0, stream>>>(packed, qscale, super_scale, n, done,
-                                                                        out);
+        k_q4dq_dequant_any<<<(unsigned)(nsb - done), kB, 0, stream>>>(packed, qscale, super_scale, n, done, out);
     return fqh::launched();
 }
 

@@ -7,10 +7,17 @@
 // quantizes in a second; here one workgroup owns a row, keeps it in registers
 // between the reduction and the quantize step, and reads it from HBM once.
 //
-// Workgroup: 256 threads, one row.  The row is split into 16-byte vectors (4 fp32
-// or 8 bf16); thread t holds vectors t, t + 256, t + 512, t + 768 of a slab of 1024
-// vectors.  Rows up to 4096 fp32 / 8192 bf16 are one slab and stay in registers;
-// longer rows are reduced slab by slab and re-read for the quantize step.
+// Three launch shapes, chosen by the row length in 16-byte vectors (4 fp32 or
+// 8 bf16) and the buffers' alignment:
+//   k_rows_wg    aligned rows of 257..1024 vectors: a 512-thread workgroup per
+//                row, one or two vectors per thread (the fastest shape measured
+//                for 4096-float / 8192-bf16 rows);
+//   k_rows_wave  other aligned rows: one wave per row, up to 16 vectors per lane
+//                per slab, longer rows slab by slab;
+//   k_quant_rows ragged or unaligned rows: 256-thread workgroup per row with
+//                element loads.
+// Every shape keeps a slab of the row in registers between the reduction and the
+// quantize step.
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -202,6 +209,283 @@ __global__ __launch_bounds__(kB) void k_quant_rows(const void* __restrict__ x, i
     }
 }
 
+// ---------------------------------------------------------------------------
+// Aligned rows: one wave per row.  Lane l holds 16-byte vectors l + 64 k,
+// k < KV, of a slab of 64 * KV vectors (a 4096-float / 8192-bf16 row is one slab
+// at KV = 16: 64 registers of data per lane).  No barrier: the row reduction is
+// DPP + lane shuffles, the parameters are wave-uniform.
+// Fast path (row all finite, divisor in the exact-quotient window):
+//   t = fl(x / s) (two Markstein corrections), tc = clamp(t, qmin - zp, qmax - zp),
+//   f = tc + kMagic rounds tc half-even; code = low bits of (pattern(f) + zp);
+//   fake-quant = (f - kMagic) * s.
+// Rows holding Inf / NaN are calibrated on their finite elements and quantized
+// with the general per-element rule (NaN -> 0, +-Inf clamp).
+// ---------------------------------------------------------------------------
+template <int DT, bool NEED>
+__device__ __forceinline__ void minmax_vec(const Vec<DT>& v, float& mn, float& mx, bool& bad) {
+    constexpr int N = Vec<DT>::N;
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+        float a = v.get(e), b = v.get(e + 1), c = v.get(e + 2), d = v.get(e + 3);
+        mn = fminf(fminf(mn, a), fminf(b, fminf(c, d)));
+        mx = fmaxf(fmaxf(mx, a), fmaxf(b, fmaxf(c, d)));
+        if (NEED) bad = bad | (a != a) | (b != b) | (c != c) | (d != d);
+    }
+}
+
+template <int BITS, int N>
+__device__ __forceinline__ void store_codes(uint8_t* crow, int64_t vi, const uint32_t (&cb)[N]) {
+    if (BITS == 8) {
+        uint32_t w0 = pack4(cb[0], cb[1], cb[2], cb[3]);
+        if (N == 4) {
+            reinterpret_cast<uint32_t*>(crow)[vi] = w0;
+        } else {
+            uint32_t w1 = pack4(cb[4 % N], cb[5 % N], cb[6 % N], cb[7 % N]);
+            reinterpret_cast<uint2*>(crow)[vi] = make_uint2(w0, w1);
+        }
+    } else {
+        uint32_t b01 = ((cb[0] & 0xFu) << 4) | (cb[1] & 0xFu);
+        uint32_t b23 = ((cb[2] & 0xFu) << 4) | (cb[3] & 0xFu);
+        if (N == 4) {
+            reinterpret_cast<uint16_t*>(crow)[vi] = (uint16_t)(b01 | (b23 << 8));
+        } else {
+            uint32_t b45 = ((cb[4 % N] & 0xFu) << 4) | (cb[5 % N] & 0xFu);
+            uint32_t b67 = ((cb[6 % N] & 0xFu) << 4) | (cb[7 % N] & 0xFu);
+            reinterpret_cast<uint32_t*>(crow)[vi] = b01 | (b23 << 8) | (b45 << 16) | (b67 << 24);
+        }
+    }
+}
+
+template <int DT, int BITS, int KV>
+__global__ __launch_bounds__(kB) void k_rows_wave(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                  int affine, uint8_t* __restrict__ codes,
+                                                  float* __restrict__ fq, float* __restrict__ scale_out,
+                                                  int32_t* __restrict__ zp_out, uint32_t* __restrict__ flags) {
+    constexpr int N = Vec<DT>::N;
+    constexpr int kSlabW = kWave * KV;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wave
+    const size_t esz = DT == FQ_F32 ? 4 : 2;
+    const char* xr = reinterpret_cast<const char*>(x) + (size_t)row * (size_t)cols * esz;
+    const int64_t nv = cols / N;
+    const int nslab = (int)((nv + kSlabW - 1) / kSlabW);
+
+    Vec<DT> cache[KV];
+    auto load_slab = [&](int s) {
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+            const int64_t vi = (int64_t)s * kSlabW + k * kWave + lane;
+            if (vi < nv) cache[k] = load_vec<DT, true>(xr, vi, cols);
+        }
+    };
+
+    // ---- reduction (NaN is ignored by min / max; +-Inf and NaN are detected) ----
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    bool bad = false;
+    for (int s = 0; s < nslab; ++s) {
+        load_slab(s);
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+            const int64_t vi = (int64_t)s * kSlabW + k * kWave + lane;
+            if (vi < nv) minmax_vec<DT, true>(cache[k], mn, mx, bad);
+        }
+    }
+    mn = wave_min_f(mn);
+    mx = wave_max_f(mx);
+    const bool nonfinite = __any(bad) || mn == -__builtin_inff() || mx == __builtin_inff();
+    if (nonfinite) {
+        MinMax m;
+        for (int s = nslab - 1; s >= 0; --s) {
+            if (s != nslab - 1) load_slab(s);
+#pragma unroll
+            for (int k = 0; k < KV; ++k) {
+                const int64_t vi = (int64_t)s * kSlabW + k * kWave + lane;
+                if (vi >= nv) continue;
+#pragma unroll
+                for (int e = 0; e < N; ++e) m.add(cache[k].get(e));
+            }
+        }
+        mn = wave_min_f(m.mn);
+        mx = wave_max_f(m.mx);
+        if (nslab > 1) load_slab(nslab - 1);
+    }
+    const bool aff = affine != 0;
+    const IntRange rg = int_range(BITS, aff);
+    const IntCal cal = calibrate(mn, mx, rg, aff);
+    if (lane == 0) {
+        scale_out[row] = cal.scale;
+        zp_out[row] = cal.zp;
+        uint32_t f = (nonfinite ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+        if (flags && f) atomicOr(flags, f);
+    }
+    const float sc = cal.scale;
+    const int zp = cal.zp;
+    const bool fast = !nonfinite && !cal.degenerate && fast_divisor(sc);
+    const IntQ q(sc, zp, rg);
+    const float y = q.div.y;
+    const float lo = q.lo, hi = q.hi;
+
+    uint8_t* crow = codes ? codes + (size_t)row * (size_t)(BITS == 8 ? cols : cols / 2) : nullptr;
+    float* frow = fq ? fq + (size_t)row * (size_t)cols : nullptr;
+    for (int s = nslab - 1; s >= 0; --s) {
+        if (s != nslab - 1) load_slab(s);
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+            const int64_t vi = (int64_t)s * kSlabW + k * kWave + lane;
+            if (vi >= nv) continue;
+            uint32_t cb[N];
+            float fv[N];
+            if (fast) {
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const float tc = fminf(fmaxf(quick_div(cache[k].get(e), sc, y), lo), hi);
+                    const float f = tc + kMagic;
+                    cb[e] = as_u(f) + (uint32_t)zp;
+                    fv[e] = (f - kMagic) * sc;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const float o = q.offset(cache[k].get(e));
+                    cb[e] = (uint32_t)((int)o + zp);
+                    fv[e] = o * sc;
+                }
+            }
+            if (crow) store_codes<BITS, N>(crow, vi, cb);
+            if (frow) {
+                float4* fr = reinterpret_cast<float4*>(frow);
+                fr[vi * (N / 4)] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+                if (N == 8) fr[vi * 2 + 1] = make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Aligned rows that fit one workgroup: T threads, V vectors of 16 bytes per
+// thread (vi = k * T + t), the row reduction through DPP + LDS.  Same fast and
+// general quantize paths as k_rows_wave.
+// ---------------------------------------------------------------------------
+template <int DT, int BITS, int T, int V>
+__global__ __launch_bounds__(T) void k_rows_wg(const void* __restrict__ x, int64_t cols, int affine,
+                                               uint8_t* __restrict__ codes, float* __restrict__ fq,
+                                               float* __restrict__ scale_out, int32_t* __restrict__ zp_out,
+                                               uint32_t* __restrict__ flags) {
+    constexpr int N = Vec<DT>::N;
+    constexpr int NW = T / kWave;
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const size_t esz = DT == FQ_F32 ? 4 : 2;
+    const char* xr = reinterpret_cast<const char*>(x) + (size_t)row * (size_t)cols * esz;
+    const int64_t nv = cols / N;
+
+    Vec<DT> cache[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int64_t vi = (int64_t)k * T + t;
+        if (vi < nv) cache[k] = load_vec<DT, true>(xr, vi, cols);
+    }
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < V; ++k)
+        if ((int64_t)k * T + t < nv) minmax_vec<DT, true>(cache[k], mn, mx, bad);
+
+    __shared__ float s_mn[NW], s_mx[NW];
+    __shared__ uint32_t s_bad[NW];
+    const int w = t / kWave;
+    {
+        const float wmn = wave_min_f(mn), wmx = wave_max_f(mx);
+        const bool wbad = __any(bad);
+        if ((t & (kWave - 1)) == 0) {
+            s_mn[w] = wmn;
+            s_mx[w] = wmx;
+            s_bad[w] = wbad;
+        }
+    }
+    __syncthreads();
+    mn = s_mn[0];
+    mx = s_mx[0];
+    bool any_bad = s_bad[0] != 0;
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+        mn = fminf(mn, s_mn[i]);
+        mx = fmaxf(mx, s_mx[i]);
+        any_bad = any_bad || s_bad[i] != 0;
+    }
+    const bool nonfinite = any_bad || mn == -__builtin_inff() || mx == __builtin_inff();
+    if (nonfinite) {
+        MinMax m;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            if ((int64_t)k * T + t >= nv) continue;
+#pragma unroll
+            for (int e = 0; e < N; ++e) m.add(cache[k].get(e));
+        }
+        const float wmn = wave_min_f(m.mn), wmx = wave_max_f(m.mx);
+        __syncthreads();
+        if ((t & (kWave - 1)) == 0) {
+            s_mn[w] = wmn;
+            s_mx[w] = wmx;
+        }
+        __syncthreads();
+        mn = s_mn[0];
+        mx = s_mx[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) {
+            mn = fminf(mn, s_mn[i]);
+            mx = fmaxf(mx, s_mx[i]);
+        }
+    }
+    const bool aff = affine != 0;
+    const IntRange rg = int_range(BITS, aff);
+    const IntCal cal = calibrate(mn, mx, rg, aff);
+    if (t == 0) {
+        scale_out[row] = cal.scale;
+        zp_out[row] = cal.zp;
+        uint32_t f = (nonfinite ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+        if (flags && f) atomicOr(flags, f);
+    }
+    const float sc = cal.scale;
+    const int zp = cal.zp;
+    const bool fast = !nonfinite && !cal.degenerate && fast_divisor(sc);
+    const IntQ q(sc, zp, rg);
+    const float y = q.div.y;
+    const float lo = q.lo, hi = q.hi;
+    uint8_t* crow = codes ? codes + (size_t)row * (size_t)(BITS == 8 ? cols : cols / 2) : nullptr;
+    float* frow = fq ? fq + (size_t)row * (size_t)cols : nullptr;
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const int64_t vi = (int64_t)k * T + t;
+        if (vi >= nv) continue;
+        uint32_t cb[N];
+        float fv[N];
+        if (fast) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                const float tc = fminf(fmaxf(quick_div(cache[k].get(e), sc, y), lo), hi);
+                const float f = tc + kMagic;
+                cb[e] = as_u(f) + (uint32_t)zp;
+                fv[e] = (f - kMagic) * sc;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                const float o = q.offset(cache[k].get(e));
+                cb[e] = (uint32_t)((int)o + zp);
+                fv[e] = o * sc;
+            }
+        }
+        if (crow) store_codes<BITS, N>(crow, vi, cb);
+        if (frow) {
+            float4* fr = reinterpret_cast<float4*>(frow);
+            fr[vi * (N / 4)] = make_float4(fv[0], fv[1], fv[2], fv[3]);
+            if (N == 8) fr[vi * 2 + 1] = make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]);
+        }
+    }
+}
+
 // Per-row dequantize: out[r, c] = (code - zp[r]) * scale[r]
 template <int BITS>
 __global__ __launch_bounds__(kB) void k_dq_rows(const uint8_t* __restrict__ codes, int64_t cols,
@@ -234,12 +518,37 @@ void launch_rows(const void* x, int64_t rows, int64_t cols, int affine, void* co
     const size_t code_align = BITS == 8 ? (N == 4 ? 4 : 8) : (N == 4 ? 2 : 4);
     const bool al = (cols % N == 0) && fqh::aligned(x, 16) && fqh::aligned(fq, 16) &&
                     fqh::aligned(codes, code_align) && (BITS == 8 || (cols / 2) % (N / 2) == 0);
-    dim3 grid((unsigned)rows);
     uint8_t* cd = (uint8_t*)codes;
-    if (al)
-        k_quant_rows<DT, BITS, true><<<grid, kB, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags);
+    if (!al) {
+        k_quant_rows<DT, BITS, false><<<dim3((unsigned)rows), kB, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags);
+        return;
+    }
+    const int64_t nv = cols / N;
+#ifndef FQ_ROWS_WG_THREADS
+#define FQ_ROWS_WG_THREADS 512
+#endif
+    constexpr int TW = FQ_ROWS_WG_THREADS;  // threads per row in the workgroup-per-row kernel
+    if (TW > 0 && nv > TW / 2 && nv <= TW) {
+        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 1><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
+            x, cols, affine, cd, fq, scale, zp, flags);
+        return;
+    }
+    if (TW > 0 && nv > TW && nv <= 2 * TW) {
+        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 2><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
+            x, cols, affine, cd, fq, scale, zp, flags);
+        return;
+    }
+    const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));
+    if (nv <= 64)
+        k_rows_wave<DT, BITS, 1><<<grid, kB, 0, st>>>(x, rows, cols, affine, cd, fq, scale, zp, flags);
+    else if (nv <= 128)
+        k_rows_wave<DT, BITS, 2><<<grid, kB, 0, st>>>(x, rows, cols, affine, cd, fq, scale, zp, flags);
+    else if (nv <= 256)
+        k_rows_wave<DT, BITS, 4><<<grid, kB, 0, st>>>(x, rows, cols, affine, cd, fq, scale, zp, flags);
+    else if (nv <= 512)
+        k_rows_wave<DT, BITS, 8><<<grid, kB, 0, st>>>(x, rows, cols, affine, cd, fq, scale, zp, flags);
     else
-        k_quant_rows<DT, BITS, false><<<grid, kB, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags);
+        k_rows_wave<DT, BITS, 16><<<grid, kB, 0, st>>>(x, rows, cols, affine, cd, fq, scale, zp, flags);
 }
 
 }  // namespace

@@ -6,10 +6,11 @@
 // Training (QAT) primitives": QuantParams::per_tensor_minmax, fake_quant_int,
 // real_min / real_max, fake_quant_backward.
 //
-// Layout: every kernel walks the tensor in chunks of four consecutive elements
-// (one 16-byte load of x), grid-stride, four chunks in flight per thread.  The
-// last n % 4 elements (and every chunk when a buffer is not vector-aligned) go
-// through the scalar form of the same chunk code.
+// Layout: the element-wise kernels walk the tensor in chunks of four consecutive
+// elements (one 16-byte load of x), one chunk per thread over a grid that covers
+// the whole tensor (many short workgroups sweeping memory in order stream best on
+// MI355X).  The last n % 4 elements (and every chunk when a buffer is not
+// vector-aligned) go through the scalar form of the same chunk code.
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -31,60 +32,98 @@ __device__ __forceinline__ void st4(float* p, int64_t c, float4 v) {
 // Tensor-scope reduction, pass 1: one partial per block.
 //   MINMAX: (finite min, finite max, max |x| bits) -- int calibration
 //   AMAX:   (-, finite amax, -)                     -- fp8 calibration
+// A block reduces tiles of 1024 consecutive 16-byte chunks (thread t takes
+// chunks t, t + 256, t + 512, t + 768 of a tile: four loads in flight, each load
+// instruction covering 4 KiB), tiles b, b + G, ... for block b of G.
+// MINMAX runs unfiltered min / max first (NaN is ignored by them); a thread that
+// met a NaN or an infinity redoes its own chunks with the finite filter.
 // ---------------------------------------------------------------------------
 enum { kMinMax = 0, kAmax = 1 };
+constexpr int kRU = fqh::kReduceChunks;
 
-template <int MODE>
-struct Acc {
-    MinMax m;
-    uint32_t amax = 0;
-    __device__ __forceinline__ void add(float v) {
-        if (MODE == kMinMax) {
-            m.add(v);
-        } else {
-            uint32_t a = as_u(v) & 0x7FFFFFFFu;
-            amax = max(amax, a < 0x7F800000u ? a : 0u);
-        }
-    }
-    __device__ __forceinline__ void add4(float4 v) {
-        add(v.x);
-        add(v.y);
-        add(v.z);
-        add(v.w);
-    }
-};
+__device__ __forceinline__ uint32_t fin_abs_bits(float v) {
+    uint32_t a = as_u(v) & 0x7FFFFFFFu;
+    return a < 0x7F800000u ? a : 0u;
+}
 
 template <int MODE, bool AL>
 __global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__ x, int64_t n,
                                                        float4* __restrict__ part) {
-    Acc<MODE> acc;
     const int64_t nfull = n >> 2;
-    const int64_t stride = (int64_t)gridDim.x * kB;
-    int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
-    if (AL) {
-        for (; c + 3 * stride < nfull; c += 4 * stride) {
-            float4 v0 = ld4(x, c), v1 = ld4(x, c + stride);
-            float4 v2 = ld4(x, c + 2 * stride), v3 = ld4(x, c + 3 * stride);
-            acc.add4(v0);
-            acc.add4(v1);
-            acc.add4(v2);
-            acc.add4(v3);
+    const int64_t ntiles = (nfull + fqh::kReduceTile - 1) / fqh::kReduceTile;
+    const bool tail = blockIdx.x == 0 && threadIdx.x < (n & 3);
+    auto ld = [&](int64_t c) -> float4 {
+        if (AL) return ld4(x, c);
+        return make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+    };
+    float4 r;
+    if (MODE == kAmax) {
+        uint32_t acc[kRU];
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) acc[u] = 0;
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            const int64_t c0 = tile * fqh::kReduceTile + threadIdx.x;
+            float4 v[kRU];
+#pragma unroll
+            for (int u = 0; u < kRU; ++u)
+                v[u] = (c0 + u * kB < nfull) ? ld(c0 + u * kB) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < kRU; ++u)
+                acc[u] = max(acc[u], max(max(fin_abs_bits(v[u].x), fin_abs_bits(v[u].y)),
+                                         max(fin_abs_bits(v[u].z), fin_abs_bits(v[u].w))));
         }
-        for (; c < nfull; c += stride) acc.add4(ld4(x, c));
+        if (tail) acc[0] = max(acc[0], fin_abs_bits(x[4 * nfull + threadIdx.x]));
+#pragma unroll
+        for (int u = 1; u < kRU; ++u) acc[0] = max(acc[0], acc[u]);
+        r = make_float4(0.f, as_f(wave_max_u(acc[0])), 0.f, 0.f);
     } else {
-        for (; c < nfull; c += stride)
-            for (int e = 0; e < 4; ++e) acc.add(x[4 * c + e]);
+        float mn[kRU], mx[kRU];
+        bool bad = false;
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) {
+            mn[u] = __builtin_inff();
+            mx[u] = -__builtin_inff();
+        }
+        for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+            const int64_t c0 = tile * fqh::kReduceTile + threadIdx.x;
+            float4 v[kRU];
+#pragma unroll
+            for (int u = 0; u < kRU; ++u)
+                v[u] = (c0 + u * kB < nfull) ? ld(c0 + u * kB) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < kRU; ++u) {
+                if (c0 + u * kB >= nfull) continue;
+                mn[u] = fminf(fminf(mn[u], v[u].x), fminf(v[u].y, fminf(v[u].z, v[u].w)));
+                mx[u] = fmaxf(fmaxf(mx[u], v[u].x), fmaxf(v[u].y, fmaxf(v[u].z, v[u].w)));
+                bad = bad | (v[u].x != v[u].x) | (v[u].y != v[u].y) | (v[u].z != v[u].z) | (v[u].w != v[u].w);
+            }
+        }
+        MinMax m;
+        if (tail) m.add(x[4 * nfull + threadIdx.x]);
+#pragma unroll
+        for (int u = 0; u < kRU; ++u) m.merge(mn[u], mx[u], 0u);
+        if (bad || m.mn == -__builtin_inff() || m.mx == __builtin_inff()) {
+            // this thread saw a non-finite value: redo its chunks with the filter
+            MinMax f;
+            for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+                const int64_t c0 = tile * fqh::kReduceTile + threadIdx.x;
+                for (int u = 0; u < kRU; ++u) {
+                    if (c0 + u * kB >= nfull) continue;
+                    float4 v = ld(c0 + u * kB);
+                    f.add(v.x);
+                    f.add(v.y);
+                    f.add(v.z);
+                    f.add(v.w);
+                }
+            }
+            if (tail) f.add(x[4 * nfull + threadIdx.x]);
+            m = f;
+        }
+        r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
     }
-    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) acc.add(x[4 * nfull + threadIdx.x]);
 
     __shared__ float4 lds[kWaves];
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    float4 r;
-    if (MODE == kMinMax) {
-        r = make_float4(wave_min_f(acc.m.mn), wave_max_f(acc.m.mx), as_f(wave_max_u(acc.m.nf)), 0.f);
-    } else {
-        r = make_float4(0.f, as_f(wave_max_u(acc.amax)), 0.f, 0.f);
-    }
     if (lane == 0) lds[w] = r;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -104,21 +143,24 @@ __global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__
 
 // Pass 2 (one block): fold the partials and derive the integer parameters
 // ([QAT] from_minmax, real_min / real_max).
-__global__ __launch_bounds__(kB) void k_params_int_final(const float4* __restrict__ part, int nparts,
+constexpr int kFT = fqh::kFinalThreads;
+constexpr int kFW = kFT / kWave;
+
+__global__ __launch_bounds__(kFT) void k_params_int_final(const float4* __restrict__ part, int nparts,
                                                          int bits, int affine,
                                                          fq_int_params* __restrict__ params,
                                                          uint32_t* __restrict__ flags) {
     MinMax m;
-    for (int i = threadIdx.x; i < nparts; i += kB) {
+    for (int i = threadIdx.x; i < nparts; i += kFT) {
         float4 p = part[i];
         m.merge(p.x, p.y, as_u(p.z));
     }
-    __shared__ float4 lds[kWaves];
+    __shared__ float4 lds[kFW];
     float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = r;
     __syncthreads();
     if (threadIdx.x != 0) return;
-    for (int i = 1; i < kWaves; ++i) m.merge(lds[i].x, lds[i].y, as_u(lds[i].z));
+    for (int i = 1; i < kFW; ++i) m.merge(lds[i].x, lds[i].y, as_u(lds[i].z));
     m.merge(r.x, r.y, as_u(r.z));
     IntRange rg = int_range(bits, affine != 0);
     IntCal cal = calibrate(m.mn, m.mx, rg, affine != 0);
@@ -133,18 +175,18 @@ __global__ __launch_bounds__(kB) void k_params_int_final(const float4* __restric
 }
 
 // Pass 2 for fp8: amax over the finite elements -> scale = amax / max-normal.
-__global__ __launch_bounds__(kB) void k_fp8_scale_final(const float4* __restrict__ part, int nparts,
+__global__ __launch_bounds__(kFT) void k_fp8_scale_final(const float4* __restrict__ part, int nparts,
                                                         float* __restrict__ s_e4m3,
                                                         float* __restrict__ s_e5m2,
                                                         uint32_t* __restrict__ flags) {
     uint32_t a = 0;
-    for (int i = threadIdx.x; i < nparts; i += kB) a = max(a, as_u(part[i].y));
-    __shared__ uint32_t lds[kWaves];
+    for (int i = threadIdx.x; i < nparts; i += kFT) a = max(a, as_u(part[i].y));
+    __shared__ uint32_t lds[kFW];
     a = wave_max_u(a);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = a;
     __syncthreads();
     if (threadIdx.x != 0) return;
-    for (int i = 1; i < kWaves; ++i) a = max(a, lds[i]);
+    for (int i = 1; i < kFW; ++i) a = max(a, lds[i]);
     float amax = as_f(a);
     bool zero = false;
     if (s_e4m3) {
@@ -163,7 +205,7 @@ __global__ __launch_bounds__(kB) void k_fp8_scale_final(const float4* __restrict
 // ---------------------------------------------------------------------------
 // Integer quantize / fake-quant with one parameter set ([QAT] fake_quant_int)
 // ---------------------------------------------------------------------------
-template <int BITS>
+template <int BITS, int MODE>
 struct IntTensorOp {
     IntQ q;
     float scale;
@@ -175,7 +217,7 @@ struct IntTensorOp {
     __device__ void scalar_chunk(const float* x, int64_t c, int cnt) const {
         int code[4] = {0, 0, 0, 0};
         for (int e = 0; e < cnt; ++e) {
-            float o = q.offset(x[4 * c + e]);
+            float o = q.template offset_m<MODE>(x[4 * c + e]);
             code[e] = (int)o + zp;
             if (fq) fq[4 * c + e] = o * scale;
             if (codes && BITS == 8) codes[4 * c + e] = (uint8_t)code[e];
@@ -186,7 +228,8 @@ struct IntTensorOp {
         }
     }
     __device__ __forceinline__ void vector_chunk(int64_t c, float4 v) const {
-        float o0 = q.offset(v.x), o1 = q.offset(v.y), o2 = q.offset(v.z), o3 = q.offset(v.w);
+        float o0 = q.template offset_m<MODE>(v.x), o1 = q.template offset_m<MODE>(v.y);
+        float o2 = q.template offset_m<MODE>(v.z), o3 = q.template offset_m<MODE>(v.w);
         if (codes) {
             int c0 = (int)o0 + zp, c1 = (int)o1 + zp, c2 = (int)o2 + zp, c3 = (int)o3 + zp;
             if (BITS == 8) {
@@ -199,14 +242,9 @@ struct IntTensorOp {
     }
 };
 
-template <int BITS, bool AL>
-__global__ __launch_bounds__(kB) void k_fq_int_tensor(const float* __restrict__ x, int64_t n, int affine,
-                                                      const fq_int_params* __restrict__ p,
-                                                      uint8_t* __restrict__ codes,
-                                                      float* __restrict__ fq) {
-    const fq_int_params P = *p;
-    const IntRange rg = int_range(BITS, affine != 0);
-    const IntTensorOp<BITS> op{IntQ(P.scale, P.zero_point, rg), P.scale, P.zero_point, codes, fq};
+template <int BITS, int MODE, bool AL>
+__device__ __forceinline__ void fq_int_loop(const IntTensorOp<BITS, MODE>& op, const float* __restrict__ x,
+                                            int64_t n) {
     const int64_t nfull = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * kB;
     int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
@@ -224,6 +262,24 @@ __global__ __launch_bounds__(kB) void k_fq_int_tensor(const float* __restrict__ 
         for (; c < nfull; c += stride) op.scalar_chunk(x, c, 4);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 3)) op.scalar_chunk(x, nfull, (int)(n & 3));
+}
+
+template <int BITS, bool AL>
+__global__ __launch_bounds__(kB) void k_fq_int_tensor(const float* __restrict__ x, int64_t n, int affine,
+                                                      const fq_int_params* __restrict__ p,
+                                                      uint8_t* __restrict__ codes,
+                                                      float* __restrict__ fq) {
+    const fq_int_params P = *p;
+    const IntRange rg = int_range(BITS, affine != 0);
+    const IntQ q(P.scale, P.zero_point, rg);
+    // one uniform decision per launch: the per-element code then carries no branch
+    if (q.zero) {
+        fq_int_loop<BITS, 0, AL>(IntTensorOp<BITS, 0>{q, P.scale, P.zero_point, codes, fq}, x, n);
+    } else if (q.div.fast) {
+        fq_int_loop<BITS, 1, AL>(IntTensorOp<BITS, 1>{q, P.scale, P.zero_point, codes, fq}, x, n);
+    } else {
+        fq_int_loop<BITS, 2, AL>(IntTensorOp<BITS, 2>{q, P.scale, P.zero_point, codes, fq}, x, n);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -350,7 +406,7 @@ int fq_tensor_params_int(const float* x, int64_t n, int bits, int scheme, void* 
     if (workspace_bytes < fq_workspace_bytes(n) || !fqh::aligned(workspace, 16)) return FQ_E_INVALID;
     if (!fqh::aligned(params, 4) || !fqh::aligned(flags, 4) || !fqh::aligned(x, 4)) return FQ_E_INVALID;
     unsigned G = launch_partial<kMinMax>(x, n, workspace, stream);
-    k_params_int_final<<<1, kB, 0, stream>>>((const float4*)workspace, (int)G, bits,
+    k_params_int_final<<<1, kFT, 0, stream>>>((const float4*)workspace, (int)G, bits,
                                              scheme == FQ_AFFINE, params, flags);
     return fqh::launched();
 }
@@ -362,7 +418,7 @@ int fq_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme,
     if (!x || n < 1 || !params || (!codes && !fq)) return FQ_E_INVALID;
     if (!fqh::aligned(params, 4) || !fqh::aligned(x, 4) || !fqh::aligned(fq, 4)) return FQ_E_INVALID;
     const bool al = fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, bits == 8 ? 4 : 2);
-    const unsigned G = fqh::grid_for((n + 3) / 4, 4 * kB, 8);
+    const unsigned G = fqh::grid_all((n + 3) / 4, kB);
     uint8_t* cd = (uint8_t*)codes;
     const int aff = scheme == FQ_AFFINE;
     if (bits == 8) {
@@ -381,7 +437,7 @@ int fq_dequantize_int_tensor(const void* codes, int64_t n, int bits, const fq_in
     if (!codes || n < 1 || !params || !out) return FQ_E_INVALID;
     if (!fqh::aligned(params, 4) || !fqh::aligned(out, 4)) return FQ_E_INVALID;
     const bool al = fqh::aligned(out, 16) && fqh::aligned(codes, bits == 8 ? 4 : 2);
-    const unsigned G = fqh::grid_for((n + 3) / 4, kB, 8);
+    const unsigned G = fqh::grid_all((n + 3) / 4, kB);
     const uint8_t* cd = (const uint8_t*)codes;
     if (bits == 8) {
         if (al) k_dq_int_tensor<8, true><<<G, kB, 0, stream>>>(cd, n, params, out);
@@ -401,7 +457,7 @@ int fq_ste_backward(const float* grad, int64_t n_grad, const float* x, int64_t n
         !fqh::aligned(grad_in, 4))
         return FQ_E_INVALID;
     const bool al = fqh::aligned(grad, 16) && fqh::aligned(x, 16) && fqh::aligned(grad_in, 16);
-    const unsigned G = fqh::grid_for((n_x + 3) / 4, 2 * kB, 8);
+    const unsigned G = fqh::grid_all((n_x + 3) / 4, kB);
     if (al) k_ste<true><<<G, kB, 0, stream>>>(grad, x, n_x, bounds, grad_in);
     else k_ste<false><<<G, kB, 0, stream>>>(grad, x, n_x, bounds, grad_in);
     return fqh::launched();
@@ -415,7 +471,7 @@ int fq_fp8_tensor_scale(const float* x, int64_t n, void* workspace, size_t works
         !fqh::aligned(flags, 4))
         return FQ_E_INVALID;
     unsigned G = launch_partial<kAmax>(x, n, workspace, stream);
-    k_fp8_scale_final<<<1, kB, 0, stream>>>((const float4*)workspace, (int)G, scale_e4m3, scale_e5m2,
+    k_fp8_scale_final<<<1, kFT, 0, stream>>>((const float4*)workspace, (int)G, scale_e4m3, scale_e5m2,
                                             flags);
     return fqh::launched();
 }
