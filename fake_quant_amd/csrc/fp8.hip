@@ -44,12 +44,19 @@ __device__ __forceinline__ void fp8_quant_loop(const float* __restrict__ x, int6
     const int64_t stride = (int64_t)gridDim.x * kB;
     int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
     auto chunk = [&](int64_t cc, float4 v) {
-        uint32_t b0 = fp8_code<FMT, MODE>(v.x, d), b1 = fp8_code<FMT, MODE>(v.y, d);
-        uint32_t b2 = fp8_code<FMT, MODE>(v.z, d), b3 = fp8_code<FMT, MODE>(v.w, d);
-        if (q) reinterpret_cast<uint32_t*>(q)[cc] = pack4(b0, b1, b2, b3);
+        uint32_t w = 0;
+        if (MODE != kZero) {
+            const float y0 = MODE == kQuick ? d.quick(v.x) : v.x / d.s;
+            const float y1 = MODE == kQuick ? d.quick(v.y) : v.y / d.s;
+            const float y2 = MODE == kQuick ? d.quick(v.z) : v.z / d.s;
+            const float y3 = MODE == kQuick ? d.quick(v.w) : v.w / d.s;
+            w = fp8_encode4_hw<FMT>(y0, y1, y2, y3);
+        }
+        if (q) reinterpret_cast<uint32_t*>(q)[cc] = w;
         if (fq)
-            reinterpret_cast<float4*>(fq)[cc] = make_float4(fp8_value<FMT>(b0, scale), fp8_value<FMT>(b1, scale),
-                                                            fp8_value<FMT>(b2, scale), fp8_value<FMT>(b3, scale));
+            reinterpret_cast<float4*>(fq)[cc] =
+                make_float4(fp8_value<FMT>(w & 0xFFu, scale), fp8_value<FMT>((w >> 8) & 0xFFu, scale),
+                            fp8_value<FMT>((w >> 16) & 0xFFu, scale), fp8_value<FMT>(w >> 24, scale));
     };
     if (AL) {
         const float4* xv = reinterpret_cast<const float4*>(x);

@@ -333,6 +333,36 @@ __device__ __forceinline__ uint32_t fp8_encode(float y) {
     return (y != y) ? 0x7Fu : code;
 }
 
+// The same cast on the CDNA4 conversion unit, four values per call, packed
+// little-endian.  v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32 round to nearest even on
+// the E4M3 / E5M2 grid; an exhaustive comparison over all 2^32 binary32 inputs
+// with fp8_encode above found them equal for every |y| <= max-normal (zeros and
+// binary32 subnormals included), while larger magnitudes and infinities come
+// out as NaN / Inf codes and a NaN comes out as a negative NaN byte.  So the
+// input is clamped to [-max, max] first (saturation, sign of zero kept) and NaN
+// inputs are patched to 0x7F afterwards.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_encode4_hw(float y0, float y1, float y2, float y3) {
+    constexpr float M = FMT == 0 ? 448.0f : 57344.0f;
+    const float c0 = fminf(fmaxf(y0, -M), M), c1 = fminf(fmaxf(y1, -M), M);
+    const float c2 = fminf(fmaxf(y2, -M), M), c3 = fminf(fmaxf(y3, -M), M);
+    int w;
+    if (FMT == 0) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c0, c1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, c3, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c0, c1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(c2, c3, w, true);
+    }
+    uint32_t u = (uint32_t)w;
+    if ((y0 != y0) | (y1 != y1) | (y2 != y2) | (y3 != y3)) {
+        const uint32_t m = ((y0 != y0) ? 0xFFu : 0u) | ((y1 != y1) ? 0xFF00u : 0u) |
+                           ((y2 != y2) ? 0xFF0000u : 0u) | ((y3 != y3) ? 0xFF000000u : 0u);
+        u = (u & ~m) | (0x7F7F7F7Fu & m);
+    }
+    return u;
+}
+
 // Value of a code that is not NaN and not Inf: the 7 magnitude bits placed under
 // the binary32 exponent field give 2^(E-127) (1 + M/2^mb) (or a binary32
 // subnormal for E = 0); multiplying by 2^(127 - bias) rebiases exactly.

@@ -63,13 +63,20 @@ __global__ __launch_bounds__(kB) void k_mx_vec(const void* __restrict__ x, int64
         am = quad_max_u(am);
         if (L == 8) am = max(am, dpp_u<kHalfMirror>(am));
         const int xe_exp = mx_exp(am);
+        uint32_t w[N / 4];
+#pragma unroll
+        for (int e = 0; e < N; e += 4)
+            w[e / 4] = fp8_encode4_hw<0>(__builtin_amdgcn_ldexpf(xe[e], -xe_exp),
+                                         __builtin_amdgcn_ldexpf(xe[e + 1], -xe_exp),
+                                         __builtin_amdgcn_ldexpf(xe[e + 2], -xe_exp),
+                                         __builtin_amdgcn_ldexpf(xe[e + 3], -xe_exp));
         uint32_t b[N];
 #pragma unroll
-        for (int e = 0; e < N; ++e) b[e] = fp8_encode<0>(__builtin_amdgcn_ldexpf(xe[e], -xe_exp));
+        for (int e = 0; e < N; ++e) b[e] = (w[e / 4] >> (8 * (e % 4))) & 0xFFu;
         if (DT == FQ_F32) {
-            reinterpret_cast<uint32_t*>(q)[gv] = pack4(b[0], b[1], b[2], b[3]);
+            reinterpret_cast<uint32_t*>(q)[gv] = w[0];
         } else {
-            reinterpret_cast<uint2*>(q)[gv] = make_uint2(pack4(b[0], b[1], b[2], b[3]), pack4(b[4], b[5], b[6], b[7]));
+            reinterpret_cast<uint2*>(q)[gv] = make_uint2(w[0], w[(N / 4) - 1]);
         }
         if ((gv % L) == 0) e8[gv / L] = (uint8_t)(xe_exp + 127);
         if (fq) {
