@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fake-quant hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu] [--copy-ref]
 
 One step runs every operation of the path once, each on the full-size synthetic
 input of its workload (all inputs resident in HBM before timing starts):
@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective GB/s of quantize/fake-quant kernels; % of MI355X HBM peak"
 PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_SUMMARY = "bench_step_all_workloads_hbm_traffic.txt"
 
 
 def log(msg):
@@ -51,7 +52,28 @@ def parse():
     ap.add_argument("--only", nargs="*", default=None,
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="only run COPY_REF_LAUNCHES plain device copies of COPY_REF_BYTES each (the known-size "
+                         "reference that scales HBM counter readings) and exit")
     return ap.parse_args()
+
+
+COPY_REF_BYTES = 1 << 30
+COPY_REF_LAUNCHES = 3
+
+
+def copy_reference(torch):
+    """Plain torch copies of a known size: each launch reads and writes exactly
+    COPY_REF_BYTES, so the FETCH_SIZE / WRITE_SIZE counters read for it give the
+    factor from counter units to bytes."""
+    src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for i in range(COPY_REF_LAUNCHES):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy {i} of {COPY_REF_BYTES} bytes done")
+    print(json.dumps({"copy_ref_bytes": COPY_REF_BYTES, "launches": COPY_REF_LAUNCHES}))
 
 
 class Op:
@@ -174,6 +196,11 @@ def build_ops(fq, syn, torch, only, dev="cuda"):
     return ops
 
 
+# The oracle runs over the first 1/CPU_SAMPLE_DIV of each large workload (the
+# whole step at 1: about 12 s of single-threaded CPU work).
+CPU_SAMPLE_DIV = 1
+
+
 def cpu_baseline(orc, syn, torch, only):
     """The oracle, single-threaded, on a bounded sample of every workload."""
     import numpy as np
@@ -201,7 +228,7 @@ def cpu_baseline(orc, syn, torch, only):
         parts.append("tensor: all 2^20")
     if want("rows_f32"):
         r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
-        rs = r // 4
+        rs = r // CPU_SAMPLE_DIV
         w = syn.rows_f32_inputs(r, c, device=dev)[:rs].cpu().numpy()
         for bits in (8, 4):
             for scheme in (orc.SYM, orc.AFFINE):
@@ -210,7 +237,7 @@ def cpu_baseline(orc, syn, torch, only):
         parts.append(f"rows_f32: {rs} of {r} rows")
     if want("fp8"):
         n = syn.FULL["fp8"]["n"]
-        m = n // 4
+        m = n // CPU_SAMPLE_DIV
         x = syn.fp8_inputs(n, device=dev)[:m].cpu().numpy()
         amax = [0.0]
         timed(lambda: amax.__setitem__(0, orc.amax_finite(x)), 4 * m)
@@ -222,7 +249,7 @@ def cpu_baseline(orc, syn, torch, only):
         parts.append(f"fp8: first {m} of {n} elements")
     if want("q4dq"):
         n = syn.FULL["q4dq"]["n"]
-        m = n // 4
+        m = n // CPU_SAMPLE_DIV
         x = syn.q4dq_inputs(n, device=dev)[:m].cpu().numpy()
         res = {}
         npk, nb, ns = (m + 1) // 2, (m + 63) // 64, (m + 16383) // 16384
@@ -232,7 +259,7 @@ def cpu_baseline(orc, syn, torch, only):
         parts.append(f"q4dq: first {m} of {n} elements")
     if want("rows_bf16"):
         r, c = syn.FULL["rows_bf16"]["rows"], syn.FULL["rows_bf16"]["cols"]
-        rs = r // 4
+        rs = r // CPU_SAMPLE_DIV
         a = syn.bf16_bits(syn.rows_bf16_inputs(r, c, device=dev)[:rs])
         timed(lambda: orc.quant_rows(a, 8, orc.AFFINE, dtype=orc.BF16, want_fq=False), 3 * rs * c + 8 * rs)
         timed(lambda: orc.mxfp8_rows(a, dtype=orc.BF16, want_fq=False), 3 * rs * c + rs * c // 32)
@@ -243,9 +270,10 @@ def cpu_baseline(orc, syn, torch, only):
 
 
 def traffic_record(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"{kernel}_traffic.txt")
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, scaled by the
+    copy reference) from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, TRAFFIC_SUMMARY)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -256,7 +284,7 @@ def traffic_record(kernel):
     if rec.get("source_sha256") != sources_sha():
         return None
     try:
-        return float(rec["hbm_bytes_per_launch"])
+        return float(rec[f"hbm_bytes_per_launch[{kernel}]"])
     except (KeyError, ValueError):
         return None
 
@@ -265,6 +293,8 @@ def sources_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fake_quant_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not f.endswith((".hip", ".h")):
+            continue
         h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
@@ -286,6 +316,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_ref:
+        copy_reference(torch)
+        return
     log("drawing inputs and allocating outputs")
     ops = build_ops(fq, syn, torch, args.only)
     stream = torch.cuda.current_stream()
