@@ -5,19 +5,32 @@
 
 namespace fqh {
 
-int num_cus() {
-    static std::atomic<int> cache[64];
+namespace {
+// Per-device cache of one device attribute (fallback when the query fails).
+int cached_attr(std::atomic<int>* cache, hipDeviceAttribute_t attr, int fallback) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    if (dev >= 64) dev = 63;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
+    if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+}  // namespace
+
+int num_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    return cached_attr(cache, hipDeviceAttributeMultiprocessorCount, 256);
+}
+
+int lds_per_cu() {
+    static std::atomic<int> cache[kMaxDevices];
+    return cached_attr(cache, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, 160 * 1024);
+}
+
+int lds_per_block() {
+    static std::atomic<int> cache[kMaxDevices];
+    return cached_attr(cache, hipDeviceAttributeMaxSharedMemoryPerBlock, 64 * 1024);
 }
 
 }  // namespace fqh

@@ -19,6 +19,13 @@ using namespace fqk;
 namespace {
 
 constexpr int kB = fqh::kBlock;
+// Resident workgroups per compute unit (0: as many as the wave slots allow).
+#ifndef FQ_OCC_FP8Q
+#define FQ_OCC_FP8Q 0
+#endif
+#ifndef FQ_OCC_FP8DQ
+#define FQ_OCC_FP8DQ 0
+#endif
 
 // Quotient modes, chosen once per launch from the (device-resident) scale:
 // zero scale -> every byte 0; divisor in the exact-quotient window -> Markstein
@@ -54,9 +61,9 @@ __device__ __forceinline__ void fp8_quant_loop(const float* __restrict__ x, int6
         }
         if (q) reinterpret_cast<uint32_t*>(q)[cc] = w;
         if (fq)
-            reinterpret_cast<float4*>(fq)[cc] =
+            store_nt(reinterpret_cast<float4*>(fq) + cc,
                 make_float4(fp8_value<FMT>(w & 0xFFu, scale), fp8_value<FMT>((w >> 8) & 0xFFu, scale),
-                            fp8_value<FMT>((w >> 16) & 0xFFu, scale), fp8_value<FMT>(w >> 24, scale));
+                            fp8_value<FMT>((w >> 16) & 0xFFu, scale), fp8_value<FMT>(w >> 24, scale)));
     };
     if (AL) {
         const float4* xv = reinterpret_cast<const float4*>(x);
@@ -116,10 +123,10 @@ __global__ __launch_bounds__(kB) void k_fp8_dequant(const uint8_t* __restrict__ 
         };
         for (; c + 3 * stride < nfull; c += 4 * stride) {
             uint32_t w0 = qw[c], w1 = qw[c + stride], w2 = qw[c + 2 * stride], w3 = qw[c + 3 * stride];
-            ov[c] = dec4(w0);
-            ov[c + stride] = dec4(w1);
-            ov[c + 2 * stride] = dec4(w2);
-            ov[c + 3 * stride] = dec4(w3);
+            store_nt(ov + c, dec4(w0));
+            store_nt(ov + c + stride, dec4(w1));
+            store_nt(ov + c + 2 * stride, dec4(w2));
+            store_nt(ov + c + 3 * stride, dec4(w3));
         }
     }
     for (; c < nfull; c += stride) {
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(kB) void k_fp8_dequant(const uint8_t* __restrict__ 
         float4 v = make_float4(fp8_decode<FMT>(w & 0xFFu) * s, fp8_decode<FMT>((w >> 8) & 0xFFu) * s,
                                fp8_decode<FMT>((w >> 16) & 0xFFu) * s, fp8_decode<FMT>(w >> 24) * s);
         if (AL) {
-            reinterpret_cast<float4*>(out)[c] = v;
+            store_nt(reinterpret_cast<float4*>(out) + c, v);
         } else {
             out[4 * c] = v.x;
             out[4 * c + 1] = v.y;
@@ -151,16 +158,18 @@ template <int FMT>
 void launch_quant(const float* x, int64_t n, const float* scale, uint8_t* q, float* fq, hipStream_t st) {
     const bool al = fqh::aligned(x, 16) && fqh::aligned(q, 4) && fqh::aligned(fq, 16);
     const unsigned G = fqh::grid_all((n + 3) / 4, kB);
-    if (al) k_fp8_quant<FMT, true><<<G, kB, 0, st>>>(x, n, scale, q, fq);
-    else k_fp8_quant<FMT, false><<<G, kB, 0, st>>>(x, n, scale, q, fq);
+    const size_t lds = fqh::lds_cap(FQ_OCC_FP8Q, 0);
+    if (al) k_fp8_quant<FMT, true><<<G, kB, lds, st>>>(x, n, scale, q, fq);
+    else k_fp8_quant<FMT, false><<<G, kB, lds, st>>>(x, n, scale, q, fq);
 }
 
 template <int FMT>
 void launch_dequant(const uint8_t* q, int64_t n, const float* scale, float* out, hipStream_t st) {
     const bool al = fqh::aligned(q, 4) && fqh::aligned(out, 16);
     const unsigned G = fqh::grid_all((n + 3) / 4, kB);
-    if (al) k_fp8_dequant<FMT, true><<<G, kB, 0, st>>>(q, n, scale, out);
-    else k_fp8_dequant<FMT, false><<<G, kB, 0, st>>>(q, n, scale, out);
+    const size_t lds = fqh::lds_cap(FQ_OCC_FP8DQ, 0);
+    if (al) k_fp8_dequant<FMT, true><<<G, kB, lds, st>>>(q, n, scale, out);
+    else k_fp8_dequant<FMT, false><<<G, kB, lds, st>>>(q, n, scale, out);
 }
 
 }  // namespace

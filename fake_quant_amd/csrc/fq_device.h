@@ -177,6 +177,17 @@ __device__ __forceinline__ float wave_max_f(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// Stores of outputs that no later step of the same kernel reads: with the
+// nontemporal hint they stream to HBM instead of settling in the Infinity Cache
+// as dirty lines that the next kernel's traffic would have to write back first.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(float4* p, float4 v) {
+    f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(p));
+}
+
+// ---------------------------------------------------------------------------
 // Finite min / max / non-finite accumulation over binary32 values.
 // `nf` collects max(|x| bits): it reaches 0x7F800000 iff an Inf or NaN was seen.
 // ---------------------------------------------------------------------------

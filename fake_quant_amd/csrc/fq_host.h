@@ -17,8 +17,32 @@ inline bool valid_scheme(int s) { return s == FQ_SYM || s == FQ_AFFINE; }
 inline bool valid_fmt(int f) { return f == FQ_E4M3 || f == FQ_E5M2; }
 inline bool valid_dtype(int d) { return d == FQ_F32 || d == FQ_BF16; }
 
+constexpr int kMaxDevices = 64;  // per-device caches; ids beyond share slot 0
+
 // Compute units of the current device (cached per device id).
 int num_cus();
+// LDS bytes per compute unit / largest LDS allocation of one workgroup.
+int lds_per_cu();
+int lds_per_block();
+
+// Dynamic LDS bytes that keep at most `wgs` workgroups of a kernel resident on a
+// compute unit (0: no cap).  The streaming kernels here move more bytes per
+// second with fewer workgroups in flight than the wave slots allow: the HBM then
+// sees a narrower window of addresses at a time.  The allocation sits midway
+// between LDS/(wgs + 1) and LDS/wgs, so the kernel's own static LDS (at most
+// `static_bytes`, which must stay below the margin) and the allocation
+// granularity cannot move it out of that window; if the device cannot express
+// the cap the kernel runs uncapped.
+inline size_t lds_cap(int wgs, int static_bytes) {
+    if (wgs <= 0) return 0;
+    const int64_t C = lds_per_cu();
+    const int64_t lo = C / (wgs + 1), hi = C / wgs;
+    int64_t mid = (lo + hi) / 2 / 256 * 256;
+    if (mid + static_bytes + 2048 > hi || mid <= lo + static_bytes) return 0;
+    int64_t pad = mid - static_bytes;
+    if (pad + static_bytes > lds_per_block()) return 0;
+    return (size_t)pad;
+}
 
 // Status of the launch(es) just enqueued.
 inline int launched() { return hipGetLastError() == hipSuccess ? FQ_OK : FQ_E_HIP; }
@@ -45,10 +69,15 @@ inline unsigned grid_all(int64_t items, int64_t per_block) {
 }
 
 // Tensor-scope reduction: the tensor is cut into tiles of kReduceTile
-// consecutive 16-byte chunks (four per thread); block b reduces tiles b, b + G,
-// ... into one partial in the workspace, with G at most kMaxReduceBlocks.
+// consecutive 16-byte chunks (four per thread of a kReduceThreads block); block b
+// reduces tiles b, b + G, ... into one partial in the workspace, with G at most
+// kMaxReduceBlocks.
+#ifndef FQ_REDUCE_THREADS
+#define FQ_REDUCE_THREADS 256
+#endif
+constexpr int kReduceThreads = FQ_REDUCE_THREADS;
 constexpr int kReduceChunks = 4;
-constexpr int64_t kReduceTile = (int64_t)kReduceChunks * kBlock;
+constexpr int64_t kReduceTile = (int64_t)kReduceChunks * kReduceThreads;
 constexpr int64_t kMaxReduceBlocks = 16384;
 constexpr int kFinalThreads = 1024;
 inline unsigned reduce_blocks(int64_t n) {

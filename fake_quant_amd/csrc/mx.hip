@@ -22,6 +22,10 @@ namespace {
 constexpr int kB = fqh::kBlock;
 constexpr int kMx = 32;
 constexpr int kE4M3Emax = 8;
+// Resident workgroups per compute unit of the vector kernel (0: no cap).
+#ifndef FQ_OCC_MX
+#define FQ_OCC_MX 0
+#endif
 
 // exponent of X for a block whose finite amax has bits `am`
 __device__ __forceinline__ int mx_exp(uint32_t am) {
@@ -81,11 +85,11 @@ __global__ __launch_bounds__(kB) void k_mx_vec(const void* __restrict__ x, int64
         if ((gv % L) == 0) e8[gv / L] = (uint8_t)(xe_exp + 127);
         if (fq) {
             float4* fv = reinterpret_cast<float4*>(fq) + gv * (N / 4);
-            fv[0] = make_float4(mx_value(b[0], xe_exp), mx_value(b[1], xe_exp), mx_value(b[2], xe_exp),
-                                mx_value(b[3], xe_exp));
+            store_nt(fv, make_float4(mx_value(b[0], xe_exp), mx_value(b[1], xe_exp), mx_value(b[2], xe_exp),
+                                     mx_value(b[3], xe_exp)));
             if (N == 8)
-                fv[1] = make_float4(mx_value(b[4], xe_exp), mx_value(b[5], xe_exp), mx_value(b[6], xe_exp),
-                                    mx_value(b[7], xe_exp));
+                store_nt(fv + 1, make_float4(mx_value(b[4], xe_exp), mx_value(b[5], xe_exp),
+                                             mx_value(b[6], xe_exp), mx_value(b[7], xe_exp)));
         }
     }
 }
@@ -133,8 +137,9 @@ int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t*
     if (al) {
         const int64_t nvec = rows * cols / N;
         const unsigned G = fqh::grid_all(nvec, kB);
-        if (dtype == FQ_F32) k_mx_vec<FQ_F32><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
-        else k_mx_vec<FQ_BF16><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
+        const size_t lds = fqh::lds_cap(FQ_OCC_MX, 0);
+        if (dtype == FQ_F32) k_mx_vec<FQ_F32><<<G, kB, lds, stream>>>(x, nvec, q, e8m0, fq);
+        else k_mx_vec<FQ_BF16><<<G, kB, lds, stream>>>(x, nvec, q, e8m0, fq);
     } else {
         const int64_t total = rows * ((cols + kMx - 1) / kMx);
         const unsigned G = fqh::grid_for(total, kB, 8);

@@ -30,7 +30,20 @@ constexpr int kJ = kSuperElems / (4 * kB);          // 16 float4 per thread (gen
 #ifndef FQ_Q4_THREADS
 #define FQ_Q4_THREADS 1024
 #endif
-constexpr int kQ4Threads = FQ_Q4_THREADS;            // threads per super-block (full kernel)
+constexpr int kQ4Threads = FQ_Q4_THREADS;            // threads per super-block (full kernels)
+// Resident workgroups per compute unit for the full-super-block kernels (one:
+// measured fastest on MI355X for both directions), and an upper bound of their
+// static LDS.
+#ifndef FQ_OCC_Q4
+#define FQ_OCC_Q4 1
+#endif
+#ifndef FQ_OCC_Q4DQ
+#define FQ_OCC_Q4DQ 1
+#endif
+constexpr int kOccQuant = FQ_OCC_Q4;
+constexpr int kOccDequant = FQ_OCC_Q4DQ;
+constexpr int kQuantLds = 2048;
+constexpr int kDequantLds = 1024;
 
 // code of x in a block with scale s (s > 0): clamp(RNE(x / s), -7, 7), NaN -> 0
 __device__ __forceinline__ float q4_code(const ExactDiv& d, float x) {
@@ -181,7 +194,7 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
         const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w, 0, 4);
         const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w, 12, 4);
         const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w, 8, 4);
-        rv[j * TPB + t] = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+        store_nt(rv + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
     });
 }
 
@@ -274,7 +287,7 @@ __global__ __launch_bounds__(TPB) void k_q4dq_dequant_full(const uint8_t* __rest
         const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 0, 4);
         const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 12, 4);
         const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 8, 4);
-        o[j * TPB + t] = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+        store_nt(o + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
     }
 }
 
@@ -321,8 +334,8 @@ int fq_q4dq_quantize(const float* x, int64_t n, uint8_t* packed, uint8_t* qscale
                     fqh::aligned(recon, 16);
     int64_t done = 0;
     if (al && nfull > 0) {
-        k_q4dq_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, 0, stream>>>(x, packed, qscale, super_scale,
-                                                                           block_scale, recon, flags);
+        k_q4dq_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, fqh::lds_cap(kOccQuant, kQuantLds), stream>>>(
+            x, packed, qscale, super_scale, block_scale, recon, flags);
         done = nfull;
     }
     if (done < nsb)
@@ -341,8 +354,8 @@ int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float
     const bool al = fqh::aligned(packed, 2) && fqh::aligned(out, 16);
     int64_t done = 0;
     if (al && nfull > 0) {
-        k_q4dq_dequant_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, 0, stream>>>(packed, qscale, super_scale,
-                                                                                   out);
+        k_q4dq_dequant_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, fqh::lds_cap(kOccDequant, kDequantLds), stream>>>(
+            packed, qscale, super_scale, out);
         done = nfull;
     }
     if (done < nsb)

@@ -355,8 +355,8 @@ __global__ __launch_bounds__(kB) void k_rows_wave(const void* __restrict__ x, in
             if (crow) store_codes<BITS, N>(crow, vi, cb);
             if (frow) {
                 float4* fr = reinterpret_cast<float4*>(frow);
-                fr[vi * (N / 4)] = make_float4(fv[0], fv[1], fv[2], fv[3]);
-                if (N == 8) fr[vi * 2 + 1] = make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]);
+                store_nt(fr + vi * (N / 4), make_float4(fv[0], fv[1], fv[2], fv[3]));
+                if (N == 8) store_nt(fr + vi * 2 + 1, make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]));
             }
         }
     }
@@ -480,8 +480,8 @@ __global__ __launch_bounds__(T) void k_rows_wg(const void* __restrict__ x, int64
         if (crow) store_codes<BITS, N>(crow, vi, cb);
         if (frow) {
             float4* fr = reinterpret_cast<float4*>(frow);
-            fr[vi * (N / 4)] = make_float4(fv[0], fv[1], fv[2], fv[3]);
-            if (N == 8) fr[vi * 2 + 1] = make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]);
+            store_nt(fr + vi * (N / 4), make_float4(fv[0], fv[1], fv[2], fv[3]));
+            if (N == 8) store_nt(fr + vi * 2 + 1, make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]));
         }
     }
 }
@@ -528,13 +528,17 @@ void launch_rows(const void* x, int64_t rows, int64_t cols, int affine, void* co
 #define FQ_ROWS_WG_THREADS 512
 #endif
     constexpr int TW = FQ_ROWS_WG_THREADS;  // threads per row in the workgroup-per-row kernel
+#ifndef FQ_OCC_ROWS
+#define FQ_OCC_ROWS 0
+#endif
+    const size_t lds = fqh::lds_cap(FQ_OCC_ROWS, 1024);  // resident rows per compute unit (0: no cap)
     if (TW > 0 && nv > TW / 2 && nv <= TW) {
-        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 1><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
+        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 1><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), lds, st>>>(
             x, cols, affine, cd, fq, scale, zp, flags);
         return;
     }
     if (TW > 0 && nv > TW && nv <= 2 * TW) {
-        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 2><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
+        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 2><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), lds, st>>>(
             x, cols, affine, cd, fq, scale, zp, flags);
         return;
     }

@@ -25,21 +25,23 @@ __device__ __forceinline__ float4 ld4(const float* p, int64_t c) {
     return *reinterpret_cast<const float4*>(p + 4 * c);
 }
 __device__ __forceinline__ void st4(float* p, int64_t c, float4 v) {
-    *reinterpret_cast<float4*>(p + 4 * c) = v;
+    store_nt(reinterpret_cast<float4*>(p + 4 * c), v);
 }
 
 // ---------------------------------------------------------------------------
 // Tensor-scope reduction, pass 1: one partial per block.
 //   MINMAX: (finite min, finite max, max |x| bits) -- int calibration
 //   AMAX:   (-, finite amax, -)                     -- fp8 calibration
-// A block reduces tiles of 1024 consecutive 16-byte chunks (thread t takes
-// chunks t, t + 256, t + 512, t + 768 of a tile: four loads in flight, each load
-// instruction covering 4 KiB), tiles b, b + G, ... for block b of G.
+// A block of kRT threads reduces tiles of 4 * kRT consecutive 16-byte chunks
+// (thread t takes chunks t, t + kRT, t + 2 kRT, t + 3 kRT of a tile: four loads in
+// flight, each load instruction covering 1 KiB per wave), tiles b, b + G, ... for
+// block b of G.
 // MINMAX runs unfiltered min / max first (NaN is ignored by them); a thread that
 // met a NaN or an infinity redoes its own chunks with the finite filter.
 // ---------------------------------------------------------------------------
 enum { kMinMax = 0, kAmax = 1 };
 constexpr int kRU = fqh::kReduceChunks;
+constexpr int kRT = fqh::kReduceThreads;
 
 __device__ __forceinline__ uint32_t fin_abs_bits(float v) {
     uint32_t a = as_u(v) & 0x7FFFFFFFu;
@@ -47,7 +49,7 @@ __device__ __forceinline__ uint32_t fin_abs_bits(float v) {
 }
 
 template <int MODE, bool AL>
-__global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__ x, int64_t n,
+__global__ __launch_bounds__(kRT) void k_reduce_partial(const float* __restrict__ x, int64_t n,
                                                        float4* __restrict__ part) {
     const int64_t nfull = n >> 2;
     const int64_t ntiles = (nfull + fqh::kReduceTile - 1) / fqh::kReduceTile;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__
             float4 v[kRU];
 #pragma unroll
             for (int u = 0; u < kRU; ++u)
-                v[u] = (c0 + u * kB < nfull) ? ld(c0 + u * kB) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[u] = (c0 + u * kRT < nfull) ? ld(c0 + u * kRT) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < kRU; ++u)
                 acc[u] = max(acc[u], max(max(fin_abs_bits(v[u].x), fin_abs_bits(v[u].y)),
@@ -89,10 +91,10 @@ __global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__
             float4 v[kRU];
 #pragma unroll
             for (int u = 0; u < kRU; ++u)
-                v[u] = (c0 + u * kB < nfull) ? ld(c0 + u * kB) : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[u] = (c0 + u * kRT < nfull) ? ld(c0 + u * kRT) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < kRU; ++u) {
-                if (c0 + u * kB >= nfull) continue;
+                if (c0 + u * kRT >= nfull) continue;
                 mn[u] = fminf(fminf(mn[u], v[u].x), fminf(v[u].y, fminf(v[u].z, v[u].w)));
                 mx[u] = fmaxf(fmaxf(mx[u], v[u].x), fmaxf(v[u].y, fmaxf(v[u].z, v[u].w)));
                 bad = bad | (v[u].x != v[u].x) | (v[u].y != v[u].y) | (v[u].z != v[u].z) | (v[u].w != v[u].w);
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__
             for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
                 const int64_t c0 = tile * fqh::kReduceTile + threadIdx.x;
                 for (int u = 0; u < kRU; ++u) {
-                    if (c0 + u * kB >= nfull) continue;
-                    float4 v = ld(c0 + u * kB);
+                    if (c0 + u * kRT >= nfull) continue;
+                    float4 v = ld(c0 + u * kRT);
                     f.add(v.x);
                     f.add(v.y);
                     f.add(v.z);
@@ -122,12 +124,12 @@ __global__ __launch_bounds__(kB) void k_reduce_partial(const float* __restrict__
         r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
     }
 
-    __shared__ float4 lds[kWaves];
+    __shared__ float4 lds[kRT / kWave];
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
     if (lane == 0) lds[w] = r;
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int i = 1; i < kWaves; ++i) {
+        for (int i = 1; i < kRT / kWave; ++i) {
             float4 o = lds[i];
             if (MODE == kMinMax) {
                 r.x = fminf(r.x, o.x);
@@ -151,9 +153,13 @@ __global__ __launch_bounds__(kFT) void k_params_int_final(const float4* __restri
                                                          fq_int_params* __restrict__ params,
                                                          uint32_t* __restrict__ flags) {
     MinMax m;
-    for (int i = threadIdx.x; i < nparts; i += kFT) {
-        float4 p = part[i];
-        m.merge(p.x, p.y, as_u(p.z));
+    for (int i0 = threadIdx.x; i0 < nparts; i0 += 4 * kFT) {
+        float4 p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            p[u] = i0 + u * kFT < nparts ? part[i0 + u * kFT] : make_float4(__builtin_inff(), -__builtin_inff(), 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m.merge(p[u].x, p[u].y, as_u(p[u].z));
     }
     __shared__ float4 lds[kFW];
     float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
@@ -180,7 +186,12 @@ __global__ __launch_bounds__(kFT) void k_fp8_scale_final(const float4* __restric
                                                         float* __restrict__ s_e5m2,
                                                         uint32_t* __restrict__ flags) {
     uint32_t a = 0;
-    for (int i = threadIdx.x; i < nparts; i += kFT) a = max(a, as_u(part[i].y));
+    for (int i0 = threadIdx.x; i0 < nparts; i0 += 4 * kFT) {
+        uint32_t p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) p[u] = i0 + u * kFT < nparts ? as_u(part[i0 + u * kFT].y) : 0u;
+        a = max(max(a, max(p[0], p[1])), max(p[2], p[3]));
+    }
     __shared__ uint32_t lds[kFW];
     a = wave_max_u(a);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = a;
@@ -384,10 +395,14 @@ __global__ __launch_bounds__(kB) void k_ste(const float* __restrict__ g, const f
 template <int MODE>
 unsigned launch_partial(const float* x, int64_t n, void* ws, hipStream_t st) {
     unsigned G = fqh::reduce_blocks(n);
+#ifndef FQ_OCC_RED
+#define FQ_OCC_RED 0
+#endif
+    const size_t lds = fqh::lds_cap(FQ_OCC_RED, 256);  // resident blocks per compute unit (0: no cap)
     if (fqh::aligned(x, 16))
-        k_reduce_partial<MODE, true><<<G, kB, 0, st>>>(x, n, (float4*)ws);
+        k_reduce_partial<MODE, true><<<G, kRT, lds, st>>>(x, n, (float4*)ws);
     else
-        k_reduce_partial<MODE, false><<<G, kB, 0, st>>>(x, n, (float4*)ws);
+        k_reduce_partial<MODE, false><<<G, kRT, lds, st>>>(x, n, (float4*)ws);
     return G;
 }
 
