@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fake-quant hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu] [--copy-ref]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu] [--no-cold] [--copy-ref]
 
 One step runs every operation of the path once, each on the full-size synthetic
 input of its workload (all inputs resident in HBM before timing starts):
@@ -19,8 +19,11 @@ input of its workload (all inputs resident in HBM before timing starts):
 
 `value` = algorithmic bytes of the step (each contract input read once, each
 output written once) / measured step time, in GB/s; `roofline` is the dominant
-kernel's achieved bandwidth against the 8 TB/s HBM peak; `cpu_baseline` is the
-CPU oracle on a bounded sample of the same work.  Prints one JSON line.
+kernel's achieved bandwidth against the 8 TB/s HBM peak; `kernels` gives every
+op's share of the timed steps; `per_op_cold_warm` times each op on its own with
+its inputs evicted from the caches (cold) and back to back (warm);
+`copy_f32_ceiling` is a plain device copy timed the same ways; `cpu_baseline`
+is the CPU oracle on a bounded sample of the same work.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -52,6 +55,7 @@ def parse():
     ap.add_argument("--only", nargs="*", default=None,
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only run COPY_REF_LAUNCHES plain device copies of COPY_REF_BYTES each (the known-size "
                          "reference that scales HBM counter readings) and exit")
@@ -201,6 +205,65 @@ def build_ops(fq, syn, torch, only, dev="cuda"):
 CPU_SAMPLE_DIV = 1
 
 
+FLUSH_BYTES = 1 << 30
+COLD_REPS, WARM_REPS, PRE_REPS = 20, 20, 5
+
+
+def _median_min(ms):
+    ms = sorted(ms)
+    return ms[len(ms) // 2], ms[0]
+
+
+def _timed_reps(fn, reps, torch, stream, before=None):
+    """HIP events around each of `reps` launches of fn (after `before`, if given),
+    enqueued back to back and read after one synchronisation."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        if before is not None:
+            before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def cold_warm(ops, fq, torch, stream):
+    """Every op on its own, cold (a 1 GiB read of scratch before each repetition
+    evicts its inputs from L2 and the Infinity Cache) and warm (back to back);
+    median and minimum over the repetitions.  Also the plain-copy ceiling."""
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flush = lambda: fq.fqb_flush(scratch, FLUSH_BYTES, sink)
+    res = {}
+    for op in ops:
+        for _ in range(PRE_REPS):
+            op.fn()
+        warm = _timed_reps(op.fn, WARM_REPS, torch, stream)
+        cold = _timed_reps(op.fn, COLD_REPS, torch, stream, before=flush)
+        (cm, cmin), (wm, wmin) = _median_min(cold), _median_min(warm)
+        res[op.name] = dict(cold_us=round(cm * 1e3, 2), cold_us_min=round(cmin * 1e3, 2),
+                            cold_gbs=round(op.nbytes / (cm * 1e-3) / 1e9, 1),
+                            cold_frac=round(op.nbytes / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            warm_us=round(wm * 1e3, 2), warm_us_min=round(wmin * 1e3, 2),
+                            warm_gbs=round(op.nbytes / (wm * 1e-3) / 1e9, 1),
+                            warm_frac=round(op.nbytes / (wm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    n = COPY_REF_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy = lambda: fq.fqb_copy_f32(src, dst, n)
+    for _ in range(PRE_REPS):
+        copy()
+    nbytes = 2 * COPY_REF_BYTES
+    (cm, _), (wm, _) = (_median_min(_timed_reps(copy, COLD_REPS, torch, stream, before=flush)),
+                        _median_min(_timed_reps(copy, WARM_REPS, torch, stream)))
+    ceiling = dict(kernel="fqb_copy_f32", bytes=nbytes, cold_gbs=round(nbytes / (cm * 1e-3) / 1e9, 1),
+                   warm_gbs=round(nbytes / (wm * 1e-3) / 1e9, 1),
+                   cold_frac=round(nbytes / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    del scratch, src, dst
+    return res, ceiling
+
+
 def cpu_baseline(orc, syn, torch, only):
     """The oracle, single-threaded, on a bounded sample of every workload."""
     import numpy as np
@@ -281,7 +344,7 @@ def traffic_record(kernel):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("source_sha256") != sources_sha():
+    if rec.get("source_sha256") != sources_sha(kernel):
         return None
     try:
         return float(rec[f"hbm_bytes_per_launch[{kernel}]"])
@@ -289,14 +352,20 @@ def traffic_record(kernel):
         return None
 
 
-def sources_sha():
+def sources_sha(kernel):
+    """sha256 over the sources `kernel` is built from: the .hip file(s) that
+    define it, every header of the package and the public header."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fake_quant_amd", "csrc")
+    files = []
     for f in sorted(os.listdir(csrc)):
-        if not f.endswith((".hip", ".h")):
-            continue
-        h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        p = os.path.join(csrc, f)
+        if f.endswith(".h") or (f.endswith(".hip") and kernel.encode() in open(p, "rb").read()):
+            files.append(p)
+    files.append(os.path.join(ROOT, "include", "fq.h"))
+    for p in files:
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
     return h.hexdigest()
 
 
@@ -367,6 +436,11 @@ def main():
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_record(dom.kernel),
                     avg_launch_us=round(per_op_ms[dom_i] * 1e3, 2), bytes_per_launch=dom.nbytes)
 
+    per_op, copy_ceiling = None, None
+    if not args.no_cold:
+        log("per-op cold / warm timings and the copy ceiling")
+        per_op, copy_ceiling = cold_warm(ops, fq, torch, stream)
+
     cpu = None
     n_ops = len(ops)
     if not args.no_cpu:
@@ -399,6 +473,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "per_op_cold_warm": per_op,
+        "copy_f32_ceiling": copy_ceiling,
     }
     print(json.dumps(out), flush=True)
 

@@ -67,6 +67,18 @@ for _name, (_res, _args) in _SIGS.items():
 
 EXPORTS = tuple(_SIGS)
 
+# Measurement helpers of the benchmark (include/fq_bench.h), not steps of the method.
+_BENCH_SIGS = {
+    "fqb_flush": (_INT, [_P, _SZ, _P, _P]),
+    "fqb_copy_f32": (_INT, [_P, _P, _I64, _P]),
+}
+for _name, (_res, _args) in _BENCH_SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+BENCH_EXPORTS = tuple(_BENCH_SIGS)
+
 
 def lib():
     return _lib
@@ -388,3 +400,19 @@ def mxfp8_rows(x, want_fq=True):
     fq = _empty((rows, cols), torch.float32, x) if want_fq else None
     fq_mxfp8_rows(x, dtype, rows, cols, q, e8, fq)
     return dict(q=q, e8m0=e8, fq=fq)
+
+
+# ---------------------------------------------------------------------------
+# Measurement helpers (include/fq_bench.h)
+# ---------------------------------------------------------------------------
+
+def fqb_flush(scratch, nbytes, sink, stream=None):
+    _need("fqb_flush", "scratch", scratch, nbytes)
+    _need("fqb_flush", "sink", sink, 4)
+    _check("fqb_flush", _lib.fqb_flush(_ptr(scratch), nbytes, _ptr(sink), _stream(stream)))
+
+
+def fqb_copy_f32(x, y, n, stream=None):
+    _need("fqb_copy_f32", "x", x, 4 * n)
+    _need("fqb_copy_f32", "y", y, 4 * n)
+    _check("fqb_copy_f32", _lib.fqb_copy_f32(_ptr(x), _ptr(y), n, _stream(stream)))

@@ -16,6 +16,7 @@ import pytest
 from conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "fq.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "fq_bench.h")
 
 
 @pytest.fixture(scope="module")
@@ -28,10 +29,10 @@ def fq():
     return mod
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER, prefix="fq_"):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fq_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(rf"\b({prefix}[a-z0-9_]+)\s*\(", text)))
 
 
 def header_define(name):
@@ -45,6 +46,22 @@ def test_exports_every_declared_symbol(fq):
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
+
+
+def test_exports_bench_helpers(fq):
+    decl = declared_functions(BENCH_HEADER, "fqb_")
+    assert decl == ["fqb_copy_f32", "fqb_flush"]
+    for name in decl:
+        assert hasattr(fq.lib(), name), name
+    assert sorted(fq.BENCH_EXPORTS) == decl
+    L = fq.lib()
+    P = FAKE
+    assert L.fqb_flush(None, 1 << 20, P, None) == fq.E_INVALID
+    assert L.fqb_flush(P, 8, P, None) == fq.E_INVALID
+    assert L.fqb_flush(P + 4, 1 << 20, P, None) == fq.E_INVALID
+    assert L.fqb_copy_f32(P, P + 4096, 6, None) == fq.E_INVALID
+    assert L.fqb_copy_f32(P + 4, P + 4096, 8, None) == fq.E_INVALID
+    assert L.fqb_copy_f32(P, None, 8, None) == fq.E_INVALID
 
 
 def test_constants_match_header(fq):
