@@ -19,13 +19,6 @@ using namespace fqk;
 namespace {
 
 constexpr int kB = fqh::kBlock;
-// Resident workgroups per compute unit (0: as many as the wave slots allow).
-#ifndef FQ_OCC_FP8Q
-#define FQ_OCC_FP8Q 0
-#endif
-#ifndef FQ_OCC_FP8DQ
-#define FQ_OCC_FP8DQ 0
-#endif
 
 // Quotient modes, chosen once per launch from the (device-resident) scale:
 // zero scale -> every byte 0; divisor in the exact-quotient window -> Markstein
@@ -106,70 +99,65 @@ __global__ __launch_bounds__(kB) void k_fp8_quant(const float* __restrict__ x, i
         fp8_quant_loop<FMT, AL, kTrue>(x, n, d, s, q, fq);
 }
 
-template <int FMT, bool AL>
-__global__ __launch_bounds__(kB) void k_fp8_dequant(const uint8_t* __restrict__ q, int64_t n,
-                                                    const float* __restrict__ scale_p,
-                                                    float* __restrict__ out) {
+// Dequantize, any alignment: one chunk of four codes per thread-iteration, byte
+// loads and element stores.
+template <int FMT>
+__global__ __launch_bounds__(kB) void k_fp8_dequant_any(const uint8_t* __restrict__ q, int64_t n,
+                                                        const float* __restrict__ scale_p,
+                                                        float* __restrict__ out) {
+    const float s = *scale_p;
+    const int64_t stride = (int64_t)gridDim.x * kB;
+    for (int64_t i = (int64_t)blockIdx.x * kB + threadIdx.x; i < n; i += stride)
+        out[i] = fp8_decode<FMT>(q[i]) * s;
+}
+
+// Aligned dequantize, U chunks of four codes per lane: wave w of the grid owns
+// chunks [64 U w, 64 U (w + 1)); its lane l takes chunks 64 U w + 64 u + l, so
+// every load and store instruction of the wave is one contiguous run and a wave
+// has U loads in flight before its first store (U = 2 measured fastest with the
+// codes cold in HBM: one 4-byte load per lane leaves too few reads in flight).
+template <int FMT, int U>
+__global__ __launch_bounds__(kB) void k_fp8_dequant_w(const uint32_t* __restrict__ qw, int64_t n,
+                                                      const float* __restrict__ scale_p,
+                                                      float4* __restrict__ out) {
     const float s = *scale_p;
     const int64_t nfull = n >> 2;
-    const int64_t stride = (int64_t)gridDim.x * kB;
-    int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
-    if (AL) {
-        const uint32_t* qw = reinterpret_cast<const uint32_t*>(q);
-        float4* ov = reinterpret_cast<float4*>(out);
-        auto dec4 = [&](uint32_t w) {
-            return make_float4(fp8_decode<FMT>(w & 0xFFu) * s, fp8_decode<FMT>((w >> 8) & 0xFFu) * s,
-                               fp8_decode<FMT>((w >> 16) & 0xFFu) * s, fp8_decode<FMT>(w >> 24) * s);
-        };
-        for (; c + 3 * stride < nfull; c += 4 * stride) {
-            uint32_t w0 = qw[c], w1 = qw[c + stride], w2 = qw[c + 2 * stride], w3 = qw[c + 3 * stride];
-            store_nt(ov + c, dec4(w0));
-            store_nt(ov + c + stride, dec4(w1));
-            store_nt(ov + c + 2 * stride, dec4(w2));
-            store_nt(ov + c + 3 * stride, dec4(w3));
-        }
-    }
-    for (; c < nfull; c += stride) {
-        uint32_t w;
-        if (AL) {
-            w = reinterpret_cast<const uint32_t*>(q)[c];
-        } else {
-            w = (uint32_t)q[4 * c] | ((uint32_t)q[4 * c + 1] << 8) | ((uint32_t)q[4 * c + 2] << 16) |
-                ((uint32_t)q[4 * c + 3] << 24);
-        }
-        float4 v = make_float4(fp8_decode<FMT>(w & 0xFFu) * s, fp8_decode<FMT>((w >> 8) & 0xFFu) * s,
-                               fp8_decode<FMT>((w >> 16) & 0xFFu) * s, fp8_decode<FMT>(w >> 24) * s);
-        if (AL) {
-            store_nt(reinterpret_cast<float4*>(out) + c, v);
-        } else {
-            out[4 * c] = v.x;
-            out[4 * c + 1] = v.y;
-            out[4 * c + 2] = v.z;
-            out[4 * c + 3] = v.w;
-        }
-    }
+    const int64_t base = ((int64_t)blockIdx.x * (kB / kWave) + threadIdx.x / kWave) * (kWave * U) + threadIdx.x % kWave;
+    uint32_t w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = base + u * kWave < nfull ? qw[base + u * kWave] : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (base + u * kWave < nfull)
+            store_nt(out + base + u * kWave,
+                     make_float4(fp8_decode<FMT>(w[u] & 0xFFu) * s, fp8_decode<FMT>((w[u] >> 8) & 0xFFu) * s,
+                                 fp8_decode<FMT>((w[u] >> 16) & 0xFFu) * s, fp8_decode<FMT>(w[u] >> 24) * s));
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-        int64_t i = 4 * nfull + threadIdx.x;
-        out[i] = fp8_decode<FMT>(q[i]) * s;
+        const int64_t i = 4 * nfull + threadIdx.x;
+        reinterpret_cast<float*>(out)[i] = fp8_decode<FMT>(reinterpret_cast<const uint8_t*>(qw)[i]) * s;
     }
 }
+
+constexpr int kDqU = 2;
 
 template <int FMT>
 void launch_quant(const float* x, int64_t n, const float* scale, uint8_t* q, float* fq, hipStream_t st) {
     const bool al = fqh::aligned(x, 16) && fqh::aligned(q, 4) && fqh::aligned(fq, 16);
     const unsigned G = fqh::grid_all((n + 3) / 4, kB);
-    const size_t lds = fqh::lds_cap(FQ_OCC_FP8Q, 0);
-    if (al) k_fp8_quant<FMT, true><<<G, kB, lds, st>>>(x, n, scale, q, fq);
-    else k_fp8_quant<FMT, false><<<G, kB, lds, st>>>(x, n, scale, q, fq);
+    if (al) k_fp8_quant<FMT, true><<<G, kB, 0, st>>>(x, n, scale, q, fq);
+    else k_fp8_quant<FMT, false><<<G, kB, 0, st>>>(x, n, scale, q, fq);
 }
 
 template <int FMT>
 void launch_dequant(const uint8_t* q, int64_t n, const float* scale, float* out, hipStream_t st) {
-    const bool al = fqh::aligned(q, 4) && fqh::aligned(out, 16);
-    const unsigned G = fqh::grid_all((n + 3) / 4, kB);
-    const size_t lds = fqh::lds_cap(FQ_OCC_FP8DQ, 0);
-    if (al) k_fp8_dequant<FMT, true><<<G, kB, lds, st>>>(q, n, scale, out);
-    else k_fp8_dequant<FMT, false><<<G, kB, lds, st>>>(q, n, scale, out);
+    const int64_t blocks = (n / 4 + 1 + (int64_t)kB * kDqU - 1) / ((int64_t)kB * kDqU);
+    if (fqh::aligned(q, 4) && fqh::aligned(out, 16) && blocks <= 0x7FFFFFFF) {
+        const unsigned G = fqh::grid_all(n / 4 + 1, (int64_t)kB * kDqU);
+        k_fp8_dequant_w<FMT, kDqU><<<G, kB, 0, st>>>(reinterpret_cast<const uint32_t*>(q), n, scale,
+                                                     reinterpret_cast<float4*>(out));
+    } else {
+        k_fp8_dequant_any<FMT><<<fqh::grid_for(n, kB, 8), kB, 0, st>>>(q, n, scale, out);
+    }
 }
 
 }  // namespace

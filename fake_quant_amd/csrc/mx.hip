@@ -22,10 +22,7 @@ namespace {
 constexpr int kB = fqh::kBlock;
 constexpr int kMx = 32;
 constexpr int kE4M3Emax = 8;
-// Resident workgroups per compute unit of the vector kernel (0: no cap).
-#ifndef FQ_OCC_MX
-#define FQ_OCC_MX 0
-#endif
+
 
 // exponent of X for a block whose finite amax has bits `am`
 __device__ __forceinline__ int mx_exp(uint32_t am) {
@@ -137,9 +134,8 @@ int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t*
     if (al) {
         const int64_t nvec = rows * cols / N;
         const unsigned G = fqh::grid_all(nvec, kB);
-        const size_t lds = fqh::lds_cap(FQ_OCC_MX, 0);
-        if (dtype == FQ_F32) k_mx_vec<FQ_F32><<<G, kB, lds, stream>>>(x, nvec, q, e8m0, fq);
-        else k_mx_vec<FQ_BF16><<<G, kB, lds, stream>>>(x, nvec, q, e8m0, fq);
+        if (dtype == FQ_F32) k_mx_vec<FQ_F32><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
+        else k_mx_vec<FQ_BF16><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
     } else {
         const int64_t total = rows * ((cols + kMx - 1) / kMx);
         const unsigned G = fqh::grid_for(total, kB, 8);

@@ -528,17 +528,13 @@ void launch_rows(const void* x, int64_t rows, int64_t cols, int affine, void* co
 #define FQ_ROWS_WG_THREADS 512
 #endif
     constexpr int TW = FQ_ROWS_WG_THREADS;  // threads per row in the workgroup-per-row kernel
-#ifndef FQ_OCC_ROWS
-#define FQ_OCC_ROWS 0
-#endif
-    const size_t lds = fqh::lds_cap(FQ_OCC_ROWS, 1024);  // resident rows per compute unit (0: no cap)
     if (TW > 0 && nv > TW / 2 && nv <= TW) {
-        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 1><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), lds, st>>>(
+        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 1><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
             x, cols, affine, cd, fq, scale, zp, flags);
         return;
     }
     if (TW > 0 && nv > TW && nv <= 2 * TW) {
-        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 2><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), lds, st>>>(
+        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 2><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
             x, cols, affine, cd, fq, scale, zp, flags);
         return;
     }

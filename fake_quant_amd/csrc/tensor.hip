@@ -147,20 +147,23 @@ __global__ __launch_bounds__(kRT) void k_reduce_partial(const float* __restrict_
 // ([QAT] from_minmax, real_min / real_max).
 constexpr int kFT = fqh::kFinalThreads;
 constexpr int kFW = kFT / kWave;
+constexpr int kFinalLoads = (int)(fqh::kMaxReduceBlocks / kFT);  // partials per thread of pass 2
+static_assert(fqh::kMaxReduceBlocks % kFT == 0, "pass 2 covers every partial");
 
 __global__ __launch_bounds__(kFT) void k_params_int_final(const float4* __restrict__ part, int nparts,
                                                          int bits, int affine,
                                                          fq_int_params* __restrict__ params,
                                                          uint32_t* __restrict__ flags) {
+    // every partial this thread folds is loaded at once (one memory round trip)
     MinMax m;
-    for (int i0 = threadIdx.x; i0 < nparts; i0 += 4 * kFT) {
-        float4 p[4];
+    float4 p[kFinalLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            p[u] = i0 + u * kFT < nparts ? part[i0 + u * kFT] : make_float4(__builtin_inff(), -__builtin_inff(), 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) m.merge(p[u].x, p[u].y, as_u(p[u].z));
+    for (int u = 0; u < kFinalLoads; ++u) {
+        const int i = threadIdx.x + u * kFT;
+        p[u] = i < nparts ? part[i] : make_float4(__builtin_inff(), -__builtin_inff(), 0.f, 0.f);
     }
+#pragma unroll
+    for (int u = 0; u < kFinalLoads; ++u) m.merge(p[u].x, p[u].y, as_u(p[u].z));
     __shared__ float4 lds[kFW];
     float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = r;
@@ -185,13 +188,15 @@ __global__ __launch_bounds__(kFT) void k_fp8_scale_final(const float4* __restric
                                                         float* __restrict__ s_e4m3,
                                                         float* __restrict__ s_e5m2,
                                                         uint32_t* __restrict__ flags) {
-    uint32_t a = 0;
-    for (int i0 = threadIdx.x; i0 < nparts; i0 += 4 * kFT) {
-        uint32_t p[4];
+    uint32_t p[kFinalLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) p[u] = i0 + u * kFT < nparts ? as_u(part[i0 + u * kFT].y) : 0u;
-        a = max(max(a, max(p[0], p[1])), max(p[2], p[3]));
+    for (int u = 0; u < kFinalLoads; ++u) {
+        const int i = threadIdx.x + u * kFT;
+        p[u] = i < nparts ? as_u(part[i].y) : 0u;
     }
+    uint32_t a = 0;
+#pragma unroll
+    for (int u = 0; u < kFinalLoads; ++u) a = max(a, p[u]);
     __shared__ uint32_t lds[kFW];
     a = wave_max_u(a);
     if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = a;
@@ -395,14 +400,10 @@ __global__ __launch_bounds__(kB) void k_ste(const float* __restrict__ g, const f
 template <int MODE>
 unsigned launch_partial(const float* x, int64_t n, void* ws, hipStream_t st) {
     unsigned G = fqh::reduce_blocks(n);
-#ifndef FQ_OCC_RED
-#define FQ_OCC_RED 0
-#endif
-    const size_t lds = fqh::lds_cap(FQ_OCC_RED, 256);  // resident blocks per compute unit (0: no cap)
     if (fqh::aligned(x, 16))
-        k_reduce_partial<MODE, true><<<G, kRT, lds, st>>>(x, n, (float4*)ws);
+        k_reduce_partial<MODE, true><<<G, kRT, 0, st>>>(x, n, (float4*)ws);
     else
-        k_reduce_partial<MODE, false><<<G, kRT, lds, st>>>(x, n, (float4*)ws);
+        k_reduce_partial<MODE, false><<<G, kRT, 0, st>>>(x, n, (float4*)ws);
     return G;
 }
 
