@@ -176,6 +176,44 @@ __device__ __forceinline__ float wave_max_f(float v) {
     return v;
 }
 
+// Order-preserving signed key of a binary32 that is not NaN (-0 sorts just
+// below +0); the map is its own inverse.  Integer min / max fold into DPP
+// instructions (v_max_i32_dpp), float ones need separate moves.
+__device__ __forceinline__ int32_t fkey(float f) {
+    const int32_t i = (int32_t)as_u(f);
+    return i ^ ((i >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float fkey_value(int32_t k) { return as_f((uint32_t)(k ^ ((k >> 31) & 0x7FFFFFFF))); }
+
+// DPP move that leaves lanes of rows outside ROWS unchanged
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int32_t dpp_keep_i(int32_t v) {
+    return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row into the next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+// max / min over the whole wave as a wave-uniform value: 16-lane rows by DPP,
+// then rows folded with the row broadcasts into lane 63
+__device__ __forceinline__ int32_t wave_max_i(int32_t v) {
+    v = max(v, (int32_t)dpp_u<kQuadXor1>((uint32_t)v));
+    v = max(v, (int32_t)dpp_u<kQuadXor2>((uint32_t)v));
+    v = max(v, (int32_t)dpp_u<kHalfMirror>((uint32_t)v));
+    v = max(v, (int32_t)dpp_u<kMirror>((uint32_t)v));
+    v = max(v, dpp_keep_i<kRowBcast15, 0xA>(v));
+    v = max(v, dpp_keep_i<kRowBcast31, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int32_t wave_min_i(int32_t v) {
+    v = min(v, (int32_t)dpp_u<kQuadXor1>((uint32_t)v));
+    v = min(v, (int32_t)dpp_u<kQuadXor2>((uint32_t)v));
+    v = min(v, (int32_t)dpp_u<kHalfMirror>((uint32_t)v));
+    v = min(v, (int32_t)dpp_u<kMirror>((uint32_t)v));
+    v = min(v, dpp_keep_i<kRowBcast15, 0xA>(v));
+    v = min(v, dpp_keep_i<kRowBcast31, 0xC>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // ---------------------------------------------------------------------------
 // Stores of outputs that no later step of the same kernel reads: with the
 // nontemporal hint they stream to HBM instead of settling in the Infinity Cache

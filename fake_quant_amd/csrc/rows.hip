@@ -9,15 +9,17 @@
 //
 // Three launch shapes, chosen by the row length in 16-byte vectors (4 fp32 or
 // 8 bf16) and the buffers' alignment:
-//   k_rows_wg    aligned rows of 257..1024 vectors: a 512-thread workgroup per
-//                row, one or two vectors per thread (the fastest shape measured
-//                for 4096-float / 8192-bf16 rows);
+//   k_rows_wg    aligned rows of 257 .. 4 TW vectors: a workgroup of TW threads
+//                per row (512 for fp32, 256 for bf16), up to four vectors per
+//                thread;
 //   k_rows_wave  other aligned rows: one wave per row, up to 16 vectors per lane
 //                per slab, longer rows slab by slab;
 //   k_quant_rows ragged or unaligned rows: 256-thread workgroup per row with
 //                element loads.
 // Every shape keeps a slab of the row in registers between the reduction and the
 // quantize step.
+#include <type_traits>
+
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -233,6 +235,20 @@ __device__ __forceinline__ void minmax_vec(const Vec<DT>& v, float& mn, float& m
     }
 }
 
+// min / max of a vector with NaN propagation (IEEE 754-2019 minimum / maximum,
+// v_minimum3_f32 / v_maximum3_f32): a NaN anywhere makes both results NaN, an
+// infinity shows as itself, so a finite result proves the vector finite.
+template <int DT>
+__device__ __forceinline__ void minmax_nan(const Vec<DT>& v, float& mn, float& mx) {
+    constexpr int N = Vec<DT>::N;
+#pragma unroll
+    for (int e = 0; e < N; e += 2) {
+        const float a = v.get(e), b = v.get(e + 1);
+        mn = __builtin_elementwise_minimum(mn, __builtin_elementwise_minimum(a, b));
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(a, b));
+    }
+}
+
 template <int BITS, int N>
 __device__ __forceinline__ void store_codes(uint8_t* crow, int64_t vi, const uint32_t (&cb)[N]) {
     if (BITS == 8) {
@@ -364,8 +380,11 @@ __global__ __launch_bounds__(kB) void k_rows_wave(const void* __restrict__ x, in
 
 // ---------------------------------------------------------------------------
 // Aligned rows that fit one workgroup: T threads, V vectors of 16 bytes per
-// thread (vi = k * T + t), the row reduction through DPP + LDS.  Same fast and
-// general quantize paths as k_rows_wave.
+// thread (vi = k * T + t).  The row min / max is NaN-propagating per thread
+// (v_minimum3 / v_maximum3) and reduced as order-preserving integer keys (DPP
+// within the wave, LDS across waves), so one test on the result tells a finite
+// row from one that needs the finite-only recomputation.  Same fast and general
+// quantize paths as k_rows_wave; the fast clamp is one v_med3_f32.
 // ---------------------------------------------------------------------------
 template <int DT, int BITS, int T, int V>
 __global__ __launch_bounds__(T) void k_rows_wg(const void* __restrict__ x, int64_t cols, int affine,
@@ -386,36 +405,35 @@ __global__ __launch_bounds__(T) void k_rows_wg(const void* __restrict__ x, int64
         const int64_t vi = (int64_t)k * T + t;
         if (vi < nv) cache[k] = load_vec<DT, true>(xr, vi, cols);
     }
+    // Row min / max: NaN-propagating per thread, then as order-preserving integer
+    // keys across the wave (DPP) and the workgroup (LDS).  A thread that met a
+    // NaN reports the extreme keys, which decode to NaN.
     float mn = __builtin_inff(), mx = -__builtin_inff();
-    bool bad = false;
 #pragma unroll
     for (int k = 0; k < V; ++k)
-        if ((int64_t)k * T + t < nv) minmax_vec<DT, true>(cache[k], mn, mx, bad);
+        if ((int64_t)k * T + t < nv) minmax_nan<DT>(cache[k], mn, mx);
+    const bool tnan = mn != mn;
+    int32_t kmn = wave_min_i(tnan ? INT32_MIN : fkey(mn));
+    int32_t kmx = wave_max_i(tnan ? INT32_MAX : fkey(mx));
 
+    __shared__ int32_t s_key[2 * NW];
     __shared__ float s_mn[NW], s_mx[NW];
-    __shared__ uint32_t s_bad[NW];
     const int w = t / kWave;
-    {
-        const float wmn = wave_min_f(mn), wmx = wave_max_f(mx);
-        const bool wbad = __any(bad);
-        if ((t & (kWave - 1)) == 0) {
-            s_mn[w] = wmn;
-            s_mx[w] = wmx;
-            s_bad[w] = wbad;
-        }
+    if ((t & (kWave - 1)) == 0) {
+        s_key[w] = kmn;
+        s_key[NW + w] = kmx;
     }
     __syncthreads();
-    mn = s_mn[0];
-    mx = s_mx[0];
-    bool any_bad = s_bad[0] != 0;
 #pragma unroll
-    for (int i = 1; i < NW; ++i) {
-        mn = fminf(mn, s_mn[i]);
-        mx = fmaxf(mx, s_mx[i]);
-        any_bad = any_bad || s_bad[i] != 0;
+    for (int i = 0; i < NW; ++i) {
+        kmn = min(kmn, s_key[i]);
+        kmx = max(kmx, s_key[NW + i]);
     }
-    const bool nonfinite = any_bad || mn == -__builtin_inff() || mx == __builtin_inff();
+    mn = fkey_value(kmn);
+    mx = fkey_value(kmx);
+    const bool nonfinite = !(__builtin_fabsf(mn) < __builtin_inff()) || !(__builtin_fabsf(mx) < __builtin_inff());
     if (nonfinite) {
+        // calibrate on the finite elements only
         MinMax m;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -424,7 +442,6 @@ __global__ __launch_bounds__(T) void k_rows_wg(const void* __restrict__ x, int64
             for (int e = 0; e < N; ++e) m.add(cache[k].get(e));
         }
         const float wmn = wave_min_f(m.mn), wmx = wave_max_f(m.mx);
-        __syncthreads();
         if ((t & (kWave - 1)) == 0) {
             s_mn[w] = wmn;
             s_mx[w] = wmx;
@@ -455,35 +472,43 @@ __global__ __launch_bounds__(T) void k_rows_wg(const void* __restrict__ x, int64
     const float lo = q.lo, hi = q.hi;
     uint8_t* crow = codes ? codes + (size_t)row * (size_t)(BITS == 8 ? cols : cols / 2) : nullptr;
     float* frow = fq ? fq + (size_t)row * (size_t)cols : nullptr;
+    // the fast loop is instantiated with and without the fake-quant output, so a
+    // codes-only call spends nothing on fake-quant values
+    auto quantize = [&](auto want_fq) {
+        constexpr bool WF = decltype(want_fq)::value;
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-        const int64_t vi = (int64_t)k * T + t;
-        if (vi >= nv) continue;
-        uint32_t cb[N];
-        float fv[N];
-        if (fast) {
+        for (int k = 0; k < V; ++k) {
+            const int64_t vi = (int64_t)k * T + t;
+            if (vi >= nv) continue;
+            uint32_t cb[N];
+            float fv[N];
+            if (fast) {
 #pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const float tc = fminf(fmaxf(quick_div(cache[k].get(e), sc, y), lo), hi);
-                const float f = tc + kMagic;
-                cb[e] = as_u(f) + (uint32_t)zp;
-                fv[e] = (f - kMagic) * sc;
+                for (int e = 0; e < N; ++e) {
+                    // the row is finite here, so the clamp is one v_med3_f32
+                    const float tc = __builtin_amdgcn_fmed3f(quick_div(cache[k].get(e), sc, y), lo, hi);
+                    const float f = tc + kMagic;
+                    cb[e] = as_u(f) + (uint32_t)zp;
+                    if (WF) fv[e] = (f - kMagic) * sc;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    const float o = q.offset(cache[k].get(e));
+                    cb[e] = (uint32_t)((int)o + zp);
+                    if (WF) fv[e] = o * sc;
+                }
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const float o = q.offset(cache[k].get(e));
-                cb[e] = (uint32_t)((int)o + zp);
-                fv[e] = o * sc;
+            if (crow) store_codes<BITS, N>(crow, vi, cb);
+            if (WF) {
+                float4* fr = reinterpret_cast<float4*>(frow);
+                store_nt(fr + vi * (N / 4), make_float4(fv[0], fv[1], fv[2], fv[3]));
+                if (N == 8) store_nt(fr + vi * 2 + 1, make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]));
             }
         }
-        if (crow) store_codes<BITS, N>(crow, vi, cb);
-        if (frow) {
-            float4* fr = reinterpret_cast<float4*>(frow);
-            store_nt(fr + vi * (N / 4), make_float4(fv[0], fv[1], fv[2], fv[3]));
-            if (N == 8) store_nt(fr + vi * 2 + 1, make_float4(fv[4 % N], fv[5 % N], fv[6 % N], fv[7 % N]));
-        }
-    }
+    };
+    if (frow) quantize(std::true_type{});
+    else quantize(std::false_type{});
 }
 
 // Per-row dequantize: out[r, c] = (code - zp[r]) * scale[r]
@@ -524,18 +549,19 @@ void launch_rows(const void* x, int64_t rows, int64_t cols, int affine, void* co
         return;
     }
     const int64_t nv = cols / N;
-#ifndef FQ_ROWS_WG_THREADS
-#define FQ_ROWS_WG_THREADS 512
-#endif
-    constexpr int TW = FQ_ROWS_WG_THREADS;  // threads per row in the workgroup-per-row kernel
-    if (TW > 0 && nv > TW / 2 && nv <= TW) {
-        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 1><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
-            x, cols, affine, cd, fq, scale, zp, flags);
-        return;
-    }
-    if (TW > 0 && nv > TW && nv <= 2 * TW) {
-        k_rows_wg<DT, BITS, (TW > 0 ? TW : 256), 2><<<dim3((unsigned)rows), (TW > 0 ? TW : 256), 0, st>>>(
-            x, cols, affine, cd, fq, scale, zp, flags);
+    // threads per row in the workgroup-per-row kernel: bf16 rows carry eight
+    // elements per vector and are bound by arithmetic, so fewer threads with four
+    // vectors each spread the per-row work thinner; fp32 rows stream faster with
+    // 512 threads of two vectors (both measured on 8192-bf16 / 4096-fp32 rows).
+    constexpr int TW = DT == FQ_BF16 ? 256 : 512;
+    if (nv > 256 && nv <= 4 * TW) {
+        const dim3 g((unsigned)rows);
+        switch ((nv + TW - 1) / TW) {
+            case 1: k_rows_wg<DT, BITS, TW, 1><<<g, TW, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags); break;
+            case 2: k_rows_wg<DT, BITS, TW, 2><<<g, TW, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags); break;
+            case 3: k_rows_wg<DT, BITS, TW, 3><<<g, TW, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags); break;
+            default: k_rows_wg<DT, BITS, TW, 4><<<g, TW, 0, st>>>(x, cols, affine, cd, fq, scale, zp, flags); break;
+        }
         return;
     }
     const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));

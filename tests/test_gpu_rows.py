@@ -57,7 +57,12 @@ def test_activation_rows_full_size_sampled(fqlib, orc):
     assert int(r["zp"].min().item()) == -128 and int(r["zp"].max().item()) == -128
 
 
-SHAPES = [(1, 1), (3, 5), (7, 127), (2, 4095), (5, 4097), (3, 9001), (4, 12288), (9, 3), (2, 64)]
+# ragged and aligned lengths; the aligned ones hit every launch shape: a wave
+# per row (<= 256 vectors, > 4 workgroup widths) and a workgroup per row with
+# one to four vectors per thread (fp32: 1200, 2056, 6000, 8192 columns; bf16:
+# 2056, 4096, 6000, 8192 columns)
+SHAPES = [(1, 1), (3, 5), (7, 127), (2, 4095), (5, 4097), (3, 9001), (4, 12288), (9, 3), (2, 64),
+          (3, 1200), (3, 2056), (2, 4096), (3, 6000), (2, 8192)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -85,12 +90,17 @@ def test_unaligned_views(fqlib, orc):
         check_rows(fqlib, orc, v, bits, scheme, what="offset view")
 
 
-def test_special_rows(fqlib, orc):
+@pytest.mark.parametrize("cols", [300, 1200, 4096, 6000, 8192])
+def test_special_rows(fqlib, orc, cols):
+    """Zero, NaN, Inf, tiny, huge, one-signed and -0 rows through every launch
+    shape (a wave per row at 300 columns, a workgroup per row above)."""
     rng = np.random.default_rng(1)
-    x = (rng.standard_normal((10, 300)) * np.exp(rng.normal(-3, 0.5, (10, 1)))).astype(np.float32)
+    x = (rng.standard_normal((10, cols)) * np.exp(rng.normal(-3, 0.5, (10, 1)))).astype(np.float32)
     x[0] = 0.0
     x[1, 5] = np.nan
+    x[1, -3] = np.nan           # also in the last vector a thread holds
     x[2, 7] = np.inf
+    x[2, -1] = -np.inf
     x[3] = np.nan
     x[4] *= np.float32(1e-33)   # tiny scale -> exact-division fallback
     x[5] = np.abs(x[5]) + 1.0   # all positive
@@ -101,8 +111,8 @@ def test_special_rows(fqlib, orc):
     xt = torch.from_numpy(x).cuda()
     for bits in (8, 4):
         for scheme in (0, 1):
-            check_rows(fqlib, orc, xt, bits, scheme, what="special rows")
-            check_rows(fqlib, orc, xt.to(torch.bfloat16), bits, scheme, what="special rows bf16")
+            check_rows(fqlib, orc, xt, bits, scheme, what=f"special rows {cols}")
+            check_rows(fqlib, orc, xt.to(torch.bfloat16), bits, scheme, what=f"special rows bf16 {cols}")
 
 
 def test_deterministic(fqlib):
