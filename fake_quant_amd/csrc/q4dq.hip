@@ -8,12 +8,16 @@
 // i/2, even i in the high nibble, two's complement).  The first-level quantizer
 // (imported by the page): blocks of 64, scale = absmax / 7, ties to even.
 //
-// One workgroup (256 threads) owns a super-block of 256 blocks = 16384 elements =
-// 64 KiB of input.  Thread t loads float4 number j*256 + t for j = 0..15, so each
-// 64-element block is one 16-lane DPP row of a wave; the block absmax is a 4-step
-// row reduction.  The whole super-block stays in registers: codes are written at
-// once, the super-scale comes from a wave + LDS maximum, and the reconstruction
-// is written from the codes kept in registers -- the input is read once.
+// A 1024-thread workgroup owns super-blocks of 256 blocks = 16384 elements =
+// 64 KiB of input, two consecutive ones in turn (four for the dequantize).
+// Thread t loads float4 number j*1024 + t for j = 0..3, so each 64-element block
+// is one 16-lane DPP row of a wave; the block absmax is a 4-step row reduction.
+// The super-block stays in registers: codes are written at once, the
+// super-scale comes from a wave + LDS maximum, and the reconstruction is written
+// from the codes kept in registers -- the input is read once.  The next
+// super-block's loads are issued before the current reconstruction is stored,
+// and an LDS reservation keeps one workgroup per compute unit (both measured
+// fastest on MI355X).
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -40,6 +44,14 @@ constexpr int kQ4Threads = FQ_Q4_THREADS;            // threads per super-block 
 #ifndef FQ_OCC_Q4DQ
 #define FQ_OCC_Q4DQ 1
 #endif
+#ifndef FQ_Q4_NSB
+#define FQ_Q4_NSB 2
+#endif
+constexpr int kQuantNsb = FQ_Q4_NSB;  // super-blocks per workgroup of the quantize kernel
+#ifndef FQ_Q4DQ_NSB
+#define FQ_Q4DQ_NSB 4
+#endif
+constexpr int kDequantNsb = FQ_Q4DQ_NSB;  // super-blocks per workgroup of the dequantize kernel
 constexpr int kOccQuant = FQ_OCC_Q4;
 constexpr int kOccDequant = FQ_OCC_Q4DQ;
 constexpr int kQuantLds = 2048;
@@ -91,7 +103,7 @@ __device__ __forceinline__ int q4_general(float x, float s, float y, bool fast) 
     return (int)q4_code(d, x);
 }
 
-template <int TPB>
+template <int TPB, int NSB>
 __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, uint8_t* __restrict__ packed,
                                                    uint8_t* __restrict__ qscale, float* __restrict__ super_scale,
                                                    float* __restrict__ block_scale, float* __restrict__ recon,
@@ -99,17 +111,26 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
     constexpr int J = kSuperElems / (4 * TPB);  // float4 per thread
     constexpr int RW = TPB / 16;                // 16-lane rows per workgroup
     constexpr int NW = TPB / kWave;             // waves per workgroup
-    const int64_t sb = blockIdx.x;
     const int t = threadIdx.x;
     const int lrow = t & 15;  // position inside the 16-lane row
-    const float4* xv = reinterpret_cast<const float4*>(x + sb * kSuperElems);
     float4 v[J];
+    {
+        const float4* xv = reinterpret_cast<const float4*>(x + (int64_t)blockIdx.x * NSB * kSuperElems);
 #pragma unroll
-    for (int j = 0; j < J; ++j) v[j] = xv[j * TPB + t];
+        for (int j = 0; j < J; ++j) v[j] = xv[j * TPB + t];
+    }
 
     __shared__ float s_scale[kGroup];
     __shared__ uint32_t s_u8[kGroup / 4];
     __shared__ float s_max[NW];
+
+    // NSB consecutive super-blocks per workgroup: the loads of the next one are
+    // issued before the reconstruction of the current one is stored.  (The LDS
+    // arrays are rewritten only after the next iteration's first barrier, which
+    // every reader of the current values has passed.)
+#pragma unroll
+    for (int isb = 0; isb < NSB; ++isb) {
+    const int64_t sb = (int64_t)blockIdx.x * NSB + isb;
 
     // Block absmax bits (raw: Inf / NaN included); lane lrow (< J) of each row
     // keeps the maximum of block j = lrow of that row.  The wave's non-finite
@@ -142,10 +163,10 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
             constexpr int j = decltype(jc)::value;
             const float s = row_bcast_f<j>(my_s);
             const float y = row_bcast_f<j>(my_y);
-            const float f0 = fminf(fmaxf(quick_div(v[j].x, s, y), -7.0f), 7.0f) + kMagic;
-            const float f1 = fminf(fmaxf(quick_div(v[j].y, s, y), -7.0f), 7.0f) + kMagic;
-            const float f2 = fminf(fmaxf(quick_div(v[j].z, s, y), -7.0f), 7.0f) + kMagic;
-            const float f3 = fminf(fmaxf(quick_div(v[j].w, s, y), -7.0f), 7.0f) + kMagic;
+            const float f0 = __builtin_amdgcn_fmed3f(quick_div(v[j].x, s, y), -7.0f, 7.0f) + kMagic;
+            const float f1 = __builtin_amdgcn_fmed3f(quick_div(v[j].y, s, y), -7.0f, 7.0f) + kMagic;
+            const float f2 = __builtin_amdgcn_fmed3f(quick_div(v[j].z, s, y), -7.0f, 7.0f) + kMagic;
+            const float f3 = __builtin_amdgcn_fmed3f(quick_div(v[j].w, s, y), -7.0f, 7.0f) + kMagic;
             const uint32_t w = nib_pair(f0, f1) | (nib_pair(f2, f3) << 8);
             pk[j * TPB + t] = (uint16_t)w;
             pc[j] = w;
@@ -184,18 +205,25 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
     const float my_sh = recon_scale(u8_scale(my_s, S), S);
     __syncthreads();
     if (t < kGroup / 4) reinterpret_cast<uint32_t*>(qscale + sb * kGroup)[t] = s_u8[t];
-    if (!recon) return;
-    float4* rv = reinterpret_cast<float4*>(recon + sb * kSuperElems);
-    StaticFor<0, J>::run([&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        const float sh = row_bcast_f<j>(my_sh);
-        const uint32_t w = pc[j];
-        const float c0 = (float)(int)__builtin_amdgcn_sbfe((int)w, 4, 4);
-        const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w, 0, 4);
-        const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w, 12, 4);
-        const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w, 8, 4);
-        store_nt(rv + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
-    });
+    if (isb + 1 < NSB) {
+        const float4* xn = reinterpret_cast<const float4*>(x + (sb + 1) * kSuperElems);
+#pragma unroll
+        for (int j = 0; j < J; ++j) v[j] = xn[j * TPB + t];
+    }
+    if (recon) {
+        float4* rv = reinterpret_cast<float4*>(recon + sb * kSuperElems);
+        StaticFor<0, J>::run([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const float sh = row_bcast_f<j>(my_sh);
+            const uint32_t w = pc[j];
+            const float c0 = (float)(int)__builtin_amdgcn_sbfe((int)w, 4, 4);
+            const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w, 0, 4);
+            const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w, 12, 4);
+            const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w, 8, 4);
+            store_nt(rv + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
+        });
+    }
+    }  // super-blocks of this workgroup
 }
 
 // Any super-block (partial, unaligned): element-wise, one thread per element
@@ -263,31 +291,47 @@ __global__ __launch_bounds__(kB) void k_q4dq_any(const float* __restrict__ x, in
 // [DQ] dequantize_4bit_double, full super-block: thread t reconstructs block t's
 // scale into LDS, every packed word is loaded up front, then each float4 is
 // decoded with its block's scale.
-template <int TPB>
+template <int TPB, int NSB>
 __global__ __launch_bounds__(TPB) void k_q4dq_dequant_full(const uint8_t* __restrict__ packed,
                                                            const uint8_t* __restrict__ qscale,
                                                            const float* __restrict__ super_scale,
                                                            float* __restrict__ out) {
     constexpr int J = kSuperElems / (4 * TPB);
     constexpr int RW = TPB / 16;
-    const int64_t sb = blockIdx.x;
     const int t = threadIdx.x;
     __shared__ float s_sh[kGroup];
-    const uint16_t* pk = reinterpret_cast<const uint16_t*>(packed + sb * (kSuperElems / 2));
     uint32_t w[J];
+    {
+        const uint16_t* pk = reinterpret_cast<const uint16_t*>(packed + (int64_t)blockIdx.x * NSB * (kSuperElems / 2));
 #pragma unroll
-    for (int j = 0; j < J; ++j) w[j] = pk[j * TPB + t];
-    if (t < kGroup) s_sh[t] = recon_scale(qscale[sb * kGroup + t], super_scale[sb]);
-    __syncthreads();
-    float4* o = reinterpret_cast<float4*>(out + sb * kSuperElems);
+        for (int j = 0; j < J; ++j) w[j] = pk[j * TPB + t];
+    }
+    // NSB consecutive super-blocks per workgroup; the codes of the next one are
+    // loaded before the current one is stored.
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-        const float sh = s_sh[j * RW + (t >> 4)];
-        const float c0 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 4, 4);
-        const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 0, 4);
-        const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 12, 4);
-        const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w[j], 8, 4);
-        store_nt(o + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
+    for (int isb = 0; isb < NSB; ++isb) {
+        const int64_t sb = (int64_t)blockIdx.x * NSB + isb;
+        if (isb > 0) __syncthreads();  // every thread is done reading s_sh of the previous super-block
+        if (t < kGroup) s_sh[t] = recon_scale(qscale[sb * kGroup + t], super_scale[sb]);
+        __syncthreads();
+        uint32_t wc[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) wc[j] = w[j];
+        if (isb + 1 < NSB) {
+            const uint16_t* pn = reinterpret_cast<const uint16_t*>(packed + (sb + 1) * (kSuperElems / 2));
+#pragma unroll
+            for (int j = 0; j < J; ++j) w[j] = pn[j * TPB + t];
+        }
+        float4* o = reinterpret_cast<float4*>(out + sb * kSuperElems);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const float sh = s_sh[j * RW + (t >> 4)];
+            const float c0 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 4, 4);
+            const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 0, 4);
+            const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 12, 4);
+            const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 8, 4);
+            store_nt(o + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
+        }
     }
 }
 
@@ -334,8 +378,17 @@ int fq_q4dq_quantize(const float* x, int64_t n, uint8_t* packed, uint8_t* qscale
                     fqh::aligned(recon, 16);
     int64_t done = 0;
     if (al && nfull > 0) {
-        k_q4dq_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, fqh::lds_cap(kOccQuant, kQuantLds), stream>>>(
-            x, packed, qscale, super_scale, block_scale, recon, flags);
+        const size_t lds = fqh::lds_cap(kOccQuant, kQuantLds);
+        const int64_t pairs = kQuantNsb > 1 ? nfull / kQuantNsb : 0;
+        if (pairs > 0)
+            k_q4dq_full<kQ4Threads, kQuantNsb><<<(unsigned)pairs, kQ4Threads, lds, stream>>>(
+                x, packed, qscale, super_scale, block_scale, recon, flags);
+        done = pairs * kQuantNsb;
+        if (done < nfull)
+            k_q4dq_full<kQ4Threads, 1><<<(unsigned)(nfull - done), kQ4Threads, lds, stream>>>(
+                x + done * kSuperElems, packed + done * (kSuperElems / 2), qscale + done * kGroup,
+                super_scale + done, block_scale ? block_scale + done * kGroup : nullptr,
+                recon ? recon + done * kSuperElems : nullptr, flags);
         done = nfull;
     }
     if (done < nsb)
@@ -354,8 +407,16 @@ int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float
     const bool al = fqh::aligned(packed, 2) && fqh::aligned(out, 16);
     int64_t done = 0;
     if (al && nfull > 0) {
-        k_q4dq_dequant_full<kQ4Threads><<<(unsigned)nfull, kQ4Threads, fqh::lds_cap(kOccDequant, kDequantLds), stream>>>(
-            packed, qscale, super_scale, out);
+        const size_t lds = fqh::lds_cap(kOccDequant, kDequantLds);
+        const int64_t groups = kDequantNsb > 1 ? nfull / kDequantNsb : 0;
+        if (groups > 0)
+            k_q4dq_dequant_full<kQ4Threads, kDequantNsb><<<(unsigned)groups, kQ4Threads, lds, stream>>>(
+                packed, qscale, super_scale, out);
+        done = groups * kDequantNsb;
+        if (done < nfull)
+            k_q4dq_dequant_full<kQ4Threads, 1><<<(unsigned)(nfull - done), kQ4Threads, lds, stream>>>(
+                packed + done * (kSuperElems / 2), qscale + done * kGroup, super_scale + done,
+                out + done * kSuperElems);
         done = nfull;
     }
     if (done < nsb)

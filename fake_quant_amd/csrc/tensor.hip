@@ -139,7 +139,10 @@ __global__ __launch_bounds__(kRT) void k_reduce_partial(const float* __restrict_
                 r.y = as_f(max(as_u(r.y), as_u(o.y)));
             }
         }
-        part[blockIdx.x] = r;
+        // amax partials are packed as 4-byte words (pass 2 then reads a quarter of
+        // the bytes); min / max partials stay 16-byte records
+        if (MODE == kAmax) reinterpret_cast<uint32_t*>(part)[blockIdx.x] = as_u(r.y);
+        else part[blockIdx.x] = r;
     }
 }
 
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kFT) void k_params_int_final(const float4* __restri
 }
 
 // Pass 2 for fp8: amax over the finite elements -> scale = amax / max-normal.
-__global__ __launch_bounds__(kFT) void k_fp8_scale_final(const float4* __restrict__ part, int nparts,
+__global__ __launch_bounds__(kFT) void k_fp8_scale_final(const uint32_t* __restrict__ part, int nparts,
                                                         float* __restrict__ s_e4m3,
                                                         float* __restrict__ s_e5m2,
                                                         uint32_t* __restrict__ flags) {
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(kFT) void k_fp8_scale_final(const float4* __restric
 #pragma unroll
     for (int u = 0; u < kFinalLoads; ++u) {
         const int i = threadIdx.x + u * kFT;
-        p[u] = i < nparts ? as_u(part[i].y) : 0u;
+        p[u] = i < nparts ? part[i] : 0u;
     }
     uint32_t a = 0;
 #pragma unroll
@@ -487,7 +490,7 @@ int fq_fp8_tensor_scale(const float* x, int64_t n, void* workspace, size_t works
         !fqh::aligned(flags, 4))
         return FQ_E_INVALID;
     unsigned G = launch_partial<kAmax>(x, n, workspace, stream);
-    k_fp8_scale_final<<<1, kFT, 0, stream>>>((const float4*)workspace, (int)G, scale_e4m3, scale_e5m2,
+    k_fp8_scale_final<<<1, kFT, 0, stream>>>((const uint32_t*)workspace, (int)G, scale_e4m3, scale_e5m2,
                                             flags);
     return fqh::launched();
 }

@@ -85,7 +85,9 @@ def test_page_examples_and_specials(fqlib, orc):
     i = torch.arange(4096, device="cuda", dtype=torch.float32)
     check_q4(fqlib, orc, torch.sin(i * 0.1) * 2.0, what="page sinusoid")
     rng = np.random.default_rng(2)
-    x = (rng.standard_t(4, 2 * SB) * 0.02).astype(np.float32)
+    x = (rng.standard_t(4, 5 * SB) * 0.02).astype(np.float32)
+    x[3 * SB + 11] = np.nan        # specials in later super-blocks of a workgroup too
+    x[4 * SB + 999] = np.inf
     x[100] = np.nan
     x[5000] = np.inf
     x[SB + 7] = -np.inf
