@@ -317,14 +317,8 @@ static float fp8_round_magnitude(float a, int mbits, int bias, float maxv) {
  * biases; an fp8 subnormal has exponent field 0.  Every NaN input encodes to 0x7F
  * in both formats (E4M3's only NaN pattern is S.1111.111; 0x7F is also a NaN of
  * E5M2). */
-uint8_t orc_fp8_encode(float y, int fmt) {
-    int mbits, ebits, bias;
-    float maxv;
-    fp8_format(fmt, &mbits, &ebits, &bias, &maxv);
-    if (isnan(y)) return 0x7F;
-    uint8_t sign = signbit(y) ? 0x80 : 0x00;
-    float a = fabsf(y);
-    float m = isinf(a) ? maxv : fp8_round_magnitude(a, mbits, bias, maxv);
+/* Byte of a magnitude m already on the fp8 grid (0 <= m <= max-normal). */
+static uint8_t fp8_bits(float m, uint8_t sign, int mbits, int bias) {
     if (m == 0.0f) return sign;
     float min_normal = ldexpf(1.0f, 1 - bias);
     uint32_t E, M;
@@ -336,8 +330,18 @@ uint8_t orc_fp8_encode(float y, int fmt) {
         E = (uint32_t)(e + bias);
         M = (uint32_t)((m / ldexpf(1.0f, e) - 1.0f) * (float)(1 << mbits));
     }
-    (void)ebits;
     return (uint8_t)(sign | (E << mbits) | M);
+}
+
+uint8_t orc_fp8_encode(float y, int fmt) {
+    int mbits, ebits, bias;
+    float maxv;
+    fp8_format(fmt, &mbits, &ebits, &bias, &maxv);
+    if (isnan(y)) return 0x7F;
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    float a = fabsf(y);
+    float m = isinf(a) ? maxv : fp8_round_magnitude(a, mbits, bias, maxv);
+    return fp8_bits(m, sign, mbits, bias);
 }
 
 /* Value of an fp8 byte ([QAT] table): E4M3 has no infinities and S.1111.111 is
@@ -568,4 +572,142 @@ void orc_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Stochastic rounding: [QAT] module docs "Rounding modes",                    */
+/* RoundingMode::Stochastic (round_to_int), quantize, fp8_quantize_magnitude   */
+/* ------------------------------------------------------------------------- */
+
+/* Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel
+ * random numbers: as easy as 1, 2, 3", SC'11).  One round maps the counter
+ * (c0, c1, c2, c3) with key (k0, k1) to
+ *   (hi(M1 c2) ^ c1 ^ k0,  lo(M1 c2),  hi(M0 c0) ^ c3 ^ k1,  lo(M0 c0))
+ * where hi / lo are the halves of the 64-bit product; the key grows by the Weyl
+ * constants (W0, W1) between rounds; ten rounds. */
+#define PHILOX_M0 0xD2511F53u
+#define PHILOX_M1 0xCD9E8D57u
+#define PHILOX_W0 0x9E3779B9u
+#define PHILOX_W1 0xBB67AE85u
+
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += PHILOX_W0;
+            k1 += PHILOX_W1;
+        }
+        uint64_t p0 = (uint64_t)PHILOX_M0 * c0;
+        uint64_t p1 = (uint64_t)PHILOX_M1 * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* The uniform [0, 1) variate of element index i (the page draws one per rounded
+ * element from a sequential Rng).
+ * READING: the variate is a function of (seed, i), so any split of a tensor draws
+ * the same numbers: word i mod 4 of Philox4x32-10 at counter
+ * (floor(i/4) mod 2^32, floor(i/4) div 2^32, 0, 0) under key
+ * (seed mod 2^32, seed div 2^32), scaled as (word >> 8) * 2^-24 -- a binary32
+ * with 24 random bits, exactly representable. */
+float orc_sr_uniform(uint64_t seed, uint64_t i) {
+    uint64_t b = i >> 2;
+    uint32_t ctr[4] = {(uint32_t)b, (uint32_t)(b >> 32), 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    orc_philox4x32_10(ctr, key, w);
+    return (float)(w[i & 3] >> 8) * 0x1p-24f;
+}
+
+/* [QAT] RoundingMode::Stochastic: floor(t) + 1 when the draw is below the
+ * fractional part, floor(t) otherwise.
+ * READING: binary32 throughout, frac = fl(t - floor(t)) compared with the 24-bit
+ * draw u (so the probability of rounding up is ceil(frac 2^24) / 2^24). */
+static float round_stochastic(float t, float u) {
+    float lower = floorf(t);
+    float frac = t - lower;
+    return u < frac ? lower + 1.0f : lower;
+}
+
+/* [QAT] quantize with RoundingMode::Stochastic.  Same readings as orc_quantize
+ * (the quotient is rounded, then the integer zero-point is added; scale 0 and a
+ * NaN quotient give code 0; +-Inf clamp to the range ends). */
+int32_t orc_quantize_sr(float x, float scale, int32_t zp, int32_t qmin, int32_t qmax, float u) {
+    if (scale == 0.0f) return 0;
+    float t = x / scale;
+    if (isnan(t)) return 0;
+    double r = isinf(t) ? (double)t : (double)round_stochastic(t, u);
+    double v = r + (double)zp;
+    if (v < (double)qmin) v = (double)qmin;
+    if (v > (double)qmax) v = (double)qmax;
+    return (int32_t)v;
+}
+
+/* [QAT] fake_quant_int with RoundingMode::Stochastic; element i of x uses the
+ * variate of index offset + i.  Either output may be NULL. */
+void orc_fake_quant_int_sr(const float* x, int64_t n, int bits, int scheme, float scale, int32_t zp,
+                           uint64_t seed, uint64_t offset, int8_t* codes, float* fq) {
+    int32_t qmin, qmax;
+    if (orc_q_range(bits, scheme, &qmin, &qmax) != 0) return;
+    for (int64_t i = 0; i < n; ++i) {
+        float u = orc_sr_uniform(seed, offset + (uint64_t)i);
+        int32_t q = orc_quantize_sr(x[i], scale, zp, qmin, qmax, u);
+        if (codes) codes[i] = (int8_t)q;
+        if (fq) fq[i] = orc_dequantize(q, scale, zp);
+    }
+}
+
+/* [QAT] fp8_quantize_magnitude with RoundingMode::Stochastic: the ratio a / step
+ * (exact) is rounded stochastically, then saturated as for Nearest. */
+static float fp8_round_magnitude_sr(float a, int mbits, int bias, float maxv, float u) {
+    if (a == 0.0f) return 0.0f;
+    int emin = 1 - bias;
+    int e = floor_log2(a);
+    int step_exp = (e > emin ? e : emin) - mbits;
+    float step = ldexpf(1.0f, step_exp);
+    float m = round_stochastic(a / step, u) * step;
+    return m > maxv ? maxv : m;
+}
+
+/* [QAT] fake_quant_fp8 with RoundingMode::Stochastic, then the byte encoding of
+ * orc_fp8_encode (NaN -> 0x7F, +-Inf -> +-max, sign kept). */
+uint8_t orc_fp8_encode_sr(float y, int fmt, float u) {
+    int mbits, ebits, bias;
+    float maxv;
+    fp8_format(fmt, &mbits, &ebits, &bias, &maxv);
+    if (isnan(y)) return 0x7F;
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    float a = fabsf(y);
+    float m = isinf(a) ? maxv : fp8_round_magnitude_sr(a, mbits, bias, maxv, u);
+    return fp8_bits(m, sign, mbits, bias);
+}
+
+/* Per-tensor fp8 quantize / fake-quant with stochastic rounding: byte =
+ * encode_sr(x / scale), fq = decode(byte) * scale; a zero scale gives byte 0;
+ * element i uses the variate of index offset + i.  Either output may be NULL. */
+void orc_fp8_quantize_sr(const float* x, int64_t n, int fmt, float scale, uint64_t seed,
+                         uint64_t offset, uint8_t* q, float* fq) {
+    for (int64_t i = 0; i < n; ++i) {
+        float u = orc_sr_uniform(seed, offset + (uint64_t)i);
+        uint8_t b = scale == 0.0f ? 0 : orc_fp8_encode_sr(x[i] / scale, fmt, u);
+        if (q) q[i] = b;
+        if (fq) fq[i] = orc_fp8_decode(b, fmt) * scale;
+    }
+}
+
+/* Variates of indices offset .. offset + n - 1 (for tests of the stream). */
+void orc_sr_uniform_n(uint64_t seed, uint64_t offset, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_sr_uniform(seed, offset + (uint64_t)i);
 }

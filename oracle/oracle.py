@@ -70,6 +70,14 @@ _SIGS = {
     "orc_q4dq_dequantize": (None, [_P, _P, _P, _I64, _P]),
     "orc_mxfp8_rows": (None, [_P, _INT, _I64, _I64, _P, _P, _P]),
     "orc_bf16_to_f32": (_F, [ctypes.c_uint16]),
+    "orc_philox4x32_10": (None, [_P, _P, _P]),
+    "orc_sr_uniform": (_F, [ctypes.c_uint64, ctypes.c_uint64]),
+    "orc_sr_uniform_n": (None, [ctypes.c_uint64, ctypes.c_uint64, _I64, _P]),
+    "orc_quantize_sr": (_I32, [_F, _F, _I32, _I32, _I32, _F]),
+    "orc_fake_quant_int_sr": (None, [_P, _I64, _INT, _INT, _F, _I32, ctypes.c_uint64, ctypes.c_uint64,
+                                     _P, _P]),
+    "orc_fp8_encode_sr": (_U8, [_F, _INT, _F]),
+    "orc_fp8_quantize_sr": (None, [_P, _I64, _INT, _F, ctypes.c_uint64, ctypes.c_uint64, _P, _P]),
 }
 
 
@@ -277,3 +285,51 @@ def mxfp8_rows(x, dtype: int = BF16, want_fq: bool = True):
     fq = np.empty((rows, cols), np.float32) if want_fq else None
     lib().orc_mxfp8_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(e8), _ptr(fq))
     return dict(q=q, e8m0=e8, fq=fq)
+
+
+# ---------------------------------------------------------------------------
+# Stochastic rounding ([QAT] RoundingMode::Stochastic) and its Philox4x32-10 stream
+# ---------------------------------------------------------------------------
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_uniform(seed: int, index: int) -> np.float32:
+    return np.float32(lib().orc_sr_uniform(seed, index))
+
+
+def sr_uniform_n(seed: int, offset: int, n: int):
+    out = np.empty(n, np.float32)
+    lib().orc_sr_uniform_n(seed, offset, n, _ptr(out))
+    return out
+
+
+def quantize_sr(x: float, scale: float, zp: int, qmin: int, qmax: int, u: float) -> int:
+    return lib().orc_quantize_sr(x, scale, zp, qmin, qmax, u)
+
+
+def fake_quant_int_sr(x, bits: int, scheme: int, scale: float, zp: int, seed: int, offset: int = 0):
+    x = _f32(x).ravel()
+    codes = np.empty(x.size, np.int8)
+    fq = np.empty(x.size, np.float32)
+    lib().orc_fake_quant_int_sr(_ptr(x), x.size, bits, scheme, scale, zp, seed, offset, _ptr(codes),
+                                _ptr(fq))
+    return codes, fq
+
+
+def fp8_encode_sr(y: float, fmt: int, u: float) -> int:
+    return lib().orc_fp8_encode_sr(y, fmt, u)
+
+
+def fp8_quantize_sr(x, fmt: int, scale: float, seed: int, offset: int = 0, want_q: bool = True,
+                    want_fq: bool = True):
+    x = _f32(x).ravel()
+    q = np.empty(x.size, np.uint8) if want_q else None
+    fq = np.empty(x.size, np.float32) if want_fq else None
+    lib().orc_fp8_quantize_sr(_ptr(x), x.size, fmt, scale, seed, offset, _ptr(q), _ptr(fq))
+    return q, fq
