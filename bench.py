@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the fake-quant hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu] [--no-cold] [--copy-ref]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...] [--no-cpu] [--no-cold] [--no-next] [--copy-ref]
 
 One step runs every operation of the path once, each on the full-size synthetic
 input of its workload (all inputs resident in HBM before timing starts):
@@ -22,8 +22,10 @@ output written once) / measured step time, in GB/s; `roofline` is the dominant
 kernel's achieved bandwidth against the 8 TB/s HBM peak; `kernels` gives every
 op's share of the timed steps; `per_op_cold_warm` times each op on its own with
 its inputs evicted from the caches (cold) and back to back (warm);
-`copy_f32_ceiling` is a plain device copy timed the same ways; `cpu_baseline`
-is the CPU oracle on a bounded sample of the same work.  Prints one JSON line.
+`copy_f32_ceiling` is a plain device copy timed the same ways; `next_rows`
+times the rows beyond the step (stochastic rounding) the same ways, outside
+`value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -56,6 +58,8 @@ def parse():
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the rows beyond the step (stochastic rounding), timed cold / warm on their own")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only run COPY_REF_LAUNCHES plain device copies of COPY_REF_BYTES each (the known-size "
                          "reference that scales HBM counter readings) and exit")
@@ -190,6 +194,46 @@ WORKLOADS = {"tensor": ops_tensor, "rows_f32": ops_rows_f32, "fp8": ops_fp8, "q4
              "rows_bf16": ops_rows_bf16}
 
 
+def ops_next_sr(fq, syn, torch, dev):
+    """Stochastic rounding ([QAT] RoundingMode::Stochastic), measured beside the
+    step but not part of it: per-tensor int8 fake-quant of the 2^20 tensor and
+    fp8 E4M3 / E5M2 quantize of the 2^26 fp8 workload; the parameters and scales
+    are calibrated once at set-up."""
+    n1 = syn.FULL["tensor"]["n"]
+    x1, _ = syn.tensor_inputs(n1, device=dev)
+    wsb1 = fq.fq_workspace_bytes(n1)
+    ws1 = torch.empty(wsb1 // 4, dtype=torch.float32, device=dev)
+    params = torch.empty(4, dtype=torch.int32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    fq.fq_tensor_params_int(x1, n1, 8, fq.SYM, ws1, wsb1, params, flags)
+    codes = torch.empty(n1, dtype=torch.int8, device=dev)
+    fq1 = torch.empty(n1, dtype=torch.float32, device=dev)
+    n = syn.FULL["fp8"]["n"]
+    x = syn.fp8_inputs(n, device=dev)
+    wsb = fq.fq_workspace_bytes(n)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    scales = torch.empty(2, dtype=torch.float32, device=dev)
+    fq.fq_fp8_tensor_scale(x, n, ws, wsb, scales[0:1], scales[1:2], flags)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    fqo = torch.empty(n, dtype=torch.float32, device=dev)
+    seed = 0x5EED
+    ops = [Op("sr.fake_quant_int8", "k_fq_int_tensor_sr",
+              lambda: fq.fq_fake_quant_int_tensor_sr(x1, n1, 8, fq.SYM, params, seed, 0, codes, fq1), 9 * n1)]
+    for fmt, fname in ((fq.E4M3, "e4m3"), (fq.E5M2, "e5m2")):
+        s = scales[fmt:fmt + 1]
+        ops.append(Op(f"sr.fp8_quantize_{fname}", "k_fp8_quant_sr",
+                      lambda s=s, fmt=fmt: fq.fq_fp8_quantize_sr(x, n, fmt, s, seed, 0, q, fqo), 9 * n))
+    return ops
+
+
+NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr}
+
+
+def build_next_ops(fq, syn, torch, dev="cuda"):
+    """The rows beyond the step (measured on their own, not counted in `value`)."""
+    return {name: make(fq, syn, torch, dev) for name, make in NEXT_WORKLOADS.items()}
+
+
 def build_ops(fq, syn, torch, only, dev="cuda"):
     """Draw inputs and allocate outputs on the GPU, one workload per function (each
     op's closure owns that workload's buffers); return the timed ops."""
@@ -228,7 +272,7 @@ def _timed_reps(fn, reps, torch, stream, before=None):
     return [a.elapsed_time(b) for a, b in ev]
 
 
-def cold_warm(ops, fq, torch, stream):
+def cold_warm(ops, fq, torch, stream, ceiling=True):
     """Every op on its own, cold (a 1 GiB read of scratch before each repetition
     evicts its inputs from L2 and the Infinity Cache) and warm (back to back);
     median and minimum over the repetitions.  Also the plain-copy ceiling."""
@@ -248,6 +292,11 @@ def cold_warm(ops, fq, torch, stream):
                             warm_us=round(wm * 1e3, 2), warm_us_min=round(wmin * 1e3, 2),
                             warm_gbs=round(op.nbytes / (wm * 1e-3) / 1e9, 1),
                             warm_frac=round(op.nbytes / (wm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+        res[op.name]["kernel"] = op.kernel
+        res[op.name]["bytes"] = op.nbytes
+    if not ceiling:
+        del scratch
+        return res, None
     n = COPY_REF_BYTES // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -440,6 +489,12 @@ def main():
     if not args.no_cold:
         log("per-op cold / warm timings and the copy ceiling")
         per_op, copy_ceiling = cold_warm(ops, fq, torch, stream)
+    next_rows = None
+    if not args.no_next and args.only is None:
+        log("rows beyond the step, cold / warm")
+        next_rows = {name: cold_warm(nops, fq, torch, stream, ceiling=False)[0]
+                     for name, nops in build_next_ops(fq, syn, torch).items()}
+        torch.cuda.synchronize()
 
     cpu = None
     n_ops = len(ops)
@@ -475,6 +530,7 @@ def main():
         "kernels": kernels,
         "per_op_cold_warm": per_op,
         "copy_f32_ceiling": copy_ceiling,
+        "next_rows": next_rows,
     }
     print(json.dumps(out), flush=True)
 

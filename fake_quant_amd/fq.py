@@ -41,6 +41,7 @@ _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _INT = ctypes.c_int
 _SZ = ctypes.c_size_t
+_U64 = ctypes.c_uint64
 
 _SIGS = {
     "fq_version": (_INT, []),
@@ -59,6 +60,8 @@ _SIGS = {
     "fq_q4dq_quantize": (_INT, [_P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "fq_q4dq_dequantize": (_INT, [_P, _P, _P, _I64, _P, _P]),
     "fq_mxfp8_rows": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _P]),
+    "fq_fake_quant_int_tensor_sr": (_INT, [_P, _I64, _INT, _INT, _P, _U64, _U64, _P, _P, _P]),
+    "fq_fp8_quantize_sr": (_INT, [_P, _I64, _INT, _P, _U64, _U64, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -165,6 +168,16 @@ def fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes=None, fq=None, st
                                          _stream(stream)))
 
 
+def fq_fake_quant_int_tensor_sr(x, n, bits, scheme, params, seed, offset=0, codes=None, fq=None, stream=None):
+    nm = "fq_fake_quant_int_tensor_sr"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "params", params, 16)
+    _need(nm, "codes", codes, _codes_bytes(n, bits))
+    _need(nm, "fq", fq, 4 * n)
+    _check(nm, _lib.fq_fake_quant_int_tensor_sr(_ptr(x), n, bits, scheme, _ptr(params), seed, offset, _ptr(codes),
+                                                _ptr(fq), _stream(stream)))
+
+
 def fq_dequantize_int_tensor(codes, n, bits, params, out, stream=None):
     nm = "fq_dequantize_int_tensor"
     _need(nm, "codes", codes, _codes_bytes(n, bits))
@@ -230,6 +243,16 @@ def fq_fp8_quantize(x, n, fmt, scale, q=None, fq=None, stream=None):
     _need(nm, "fq", fq, 4 * n)
     _check("fq_fp8_quantize",
            _lib.fq_fp8_quantize(_ptr(x), n, fmt, _ptr(scale), _ptr(q), _ptr(fq), _stream(stream)))
+
+
+def fq_fp8_quantize_sr(x, n, fmt, scale, seed, offset=0, q=None, fq=None, stream=None):
+    nm = "fq_fp8_quantize_sr"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "scale", scale, 4)
+    _need(nm, "q", q, n)
+    _need(nm, "fq", fq, 4 * n)
+    _check(nm, _lib.fq_fp8_quantize_sr(_ptr(x), n, fmt, _ptr(scale), seed, offset, _ptr(q), _ptr(fq),
+                                       _stream(stream)))
 
 
 def fq_fp8_dequantize(q, n, fmt, scale, out, stream=None):
@@ -316,6 +339,14 @@ def fake_quant_int_tensor(x, params, bits=8, scheme=SYM, want_codes=True, want_f
     return codes, fq
 
 
+def fake_quant_int_tensor_sr(x, params, seed, offset=0, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+    n = x.numel()
+    codes = _empty(n if bits == 8 else (n + 1) // 2, torch.int8 if bits == 8 else torch.uint8, x) if want_codes else None
+    fq = _empty(n, torch.float32, x) if want_fq else None
+    fq_fake_quant_int_tensor_sr(x, n, bits, scheme, params, seed, offset, codes, fq)
+    return codes, fq
+
+
 def dequantize_int_tensor(codes, n, params, bits=8):
     out = _empty(n, torch.float32, codes)
     fq_dequantize_int_tensor(codes, n, bits, params, out)
@@ -364,6 +395,14 @@ def fp8_quantize(x, fmt, scale, want_q=True, want_fq=True):
     q = _empty(n, torch.uint8, x) if want_q else None
     fq = _empty(n, torch.float32, x) if want_fq else None
     fq_fp8_quantize(x, n, fmt, scale, q, fq)
+    return q, fq
+
+
+def fp8_quantize_sr(x, fmt, scale, seed, offset=0, want_q=True, want_fq=True):
+    n = x.numel()
+    q = _empty(n, torch.uint8, x) if want_q else None
+    fq = _empty(n, torch.float32, x) if want_fq else None
+    fq_fp8_quantize_sr(x, n, fmt, scale, seed, offset, q, fq)
     return q, fq
 
 

@@ -203,6 +203,32 @@ int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float
 int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8m0,
                   float* fq, hipStream_t stream);
 
+/* ---- stochastic rounding ------------------------------------------------
+ * [QAT] module docs "Rounding modes", RoundingMode::Stochastic: a quotient t is
+ * rounded to floor(t) + 1 with probability equal to its fractional part and to
+ * floor(t) otherwise (unbiased).  Here: up iff u < fl(t - floor(t)), where the
+ * variate of element index i is u = (w >> 8) * 2^-24 and w is word (i mod 4) of
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) at counter
+ * (floor(i/4) mod 2^32, floor(i/4) div 2^32, 0, 0) under key
+ * (seed mod 2^32, seed div 2^32).  x[k] has index offset + k, so a tensor split
+ * over calls (or devices) with matching offsets draws the same numbers. */
+
+/* fq_fake_quant_int_tensor with stochastic rounding of t = x / scale:
+ * code = clamp(round_sr(t), qmin - zp, qmax - zp) + zp (NaN -> 0, +-Inf clamp,
+ * scale 0 -> 0); fq = (code - zp) * scale.  Arguments and layouts as
+ * fq_fake_quant_int_tensor, plus seed and offset. */
+int fq_fake_quant_int_tensor_sr(const float* x, int64_t n, int bits, int scheme, const fq_int_params* params,
+                                uint64_t seed, uint64_t offset, void* codes, float* fq, hipStream_t stream);
+
+/* fq_fp8_quantize with stochastic rounding on the fp8 grid ([QAT]
+ * fp8_quantize_magnitude with the stochastic mode): for y = x / scale with
+ * binade step 2^(max(e, emin) - mbits), |y| / step is rounded stochastically,
+ * times step, saturated at max-normal; NaN -> 0x7F, +-Inf -> +-max, sign kept,
+ * scale 0 -> byte 0.  Arguments and layouts as fq_fp8_quantize, plus seed and
+ * offset. */
+int fq_fp8_quantize_sr(const float* x, int64_t n, int fmt, const float* scale, uint64_t seed, uint64_t offset,
+                       uint8_t* q, float* fq, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 16
+    assert len(decl) == 18
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -130,6 +130,16 @@ def test_argument_checks(fq):
     assert L.fq_q4dq_dequantize(P, P, None, 8, P, None) == fq.E_INVALID
     assert L.fq_mxfp8_rows(P, 1, 1, 32, None, P, None, None) == fq.E_INVALID
     assert L.fq_mxfp8_rows(P, 1, 0, 32, P, P, None, None) == fq.E_INVALID
+    # stochastic rounding entry points share the checks of their nearest-rounding twins
+    assert L.fq_fake_quant_int_tensor_sr(P, 8, 3, 0, P, 1, 0, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_fake_quant_int_tensor_sr(P, 8, 8, 2, P, 1, 0, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_fake_quant_int_tensor_sr(P, 0, 8, 0, P, 1, 0, P, P, None) == fq.E_INVALID
+    assert L.fq_fake_quant_int_tensor_sr(P, 8, 8, 0, None, 1, 0, P, P, None) == fq.E_INVALID
+    assert L.fq_fake_quant_int_tensor_sr(P, 8, 8, 0, P, 1, 0, None, None, None) == fq.E_INVALID
+    assert L.fq_fp8_quantize_sr(P, 8, 2, P, 1, 0, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_fp8_quantize_sr(P, 8, 0, None, 1, 0, P, P, None) == fq.E_INVALID
+    assert L.fq_fp8_quantize_sr(P, 8, 0, P, 1, 0, None, None, None) == fq.E_INVALID
+    assert L.fq_fp8_quantize_sr(P + 2, 8, 0, P, 1, 0, P, P, None) == fq.E_INVALID
     # STE: length mismatch, empty
     assert L.fq_ste_backward(P, 3, P, 2, P, P, None) == fq.E_DIM
     assert L.fq_ste_backward(P, 0, P, 0, P, P, None) == fq.E_INVALID

@@ -55,6 +55,21 @@ def test_every_bench_op_passes_buffers_that_fit(monkeypatch):
     assert sum(op.nbytes for op in ops) > 0
 
 
+def test_next_rows_pass_buffers_that_fit(monkeypatch):
+    monkeypatch.setattr(synthetic, "FULL", TINY)
+    recorder = RecordingLib(fq.lib())
+    monkeypatch.setattr(fq, "_lib", recorder)
+    monkeypatch.setattr(fq, "_need", cpu_need)
+    monkeypatch.setattr(fq, "_stream", lambda stream=None: None)
+    groups = bench.build_next_ops(fq, synthetic, torch, dev="cpu")
+    ops = [op for g in groups.values() for op in g]
+    assert [op.name for op in ops] == ["sr.fake_quant_int8", "sr.fp8_quantize_e4m3", "sr.fp8_quantize_e5m2"]
+    before = len(recorder.calls)
+    for op in ops:
+        op.fn()
+    assert recorder.calls[before:] == ["fq_fake_quant_int_tensor_sr", "fq_fp8_quantize_sr", "fq_fp8_quantize_sr"]
+
+
 def test_binding_guards_reject_bad_buffers():
     x = torch.zeros(16)
     with pytest.raises(fq.FqError, match="not a GPU tensor"):
