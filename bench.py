@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None,
-                    help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16")
+                    help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16 (step), "
+                         "stochastic_rounding (beside the step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
     ap.add_argument("--no-next", action="store_true",
@@ -490,10 +491,11 @@ def main():
         log("per-op cold / warm timings and the copy ceiling")
         per_op, copy_ceiling = cold_warm(ops, fq, torch, stream)
     next_rows = None
-    if not args.no_next and args.only is None:
+    if not args.no_next and (args.only is None or any(w in NEXT_WORKLOADS for w in args.only)):
         log("rows beyond the step, cold / warm")
         next_rows = {name: cold_warm(nops, fq, torch, stream, ceiling=False)[0]
-                     for name, nops in build_next_ops(fq, syn, torch).items()}
+                     for name, nops in build_next_ops(fq, syn, torch).items()
+                     if args.only is None or name in args.only}
         torch.cuda.synchronize()
 
     cpu = None
