@@ -711,3 +711,74 @@ void orc_fp8_quantize_sr(const float* x, int64_t n, int fmt, float scale, uint64
 void orc_sr_uniform_n(uint64_t seed, uint64_t offset, int64_t n, float* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = orc_sr_uniform(seed, offset + (uint64_t)i);
 }
+
+/* ------------------------------------------------------------------------- */
+/* QAT step: [QAT] QatOptimizer::step (AdamW master update) and requantize     */
+/* ------------------------------------------------------------------------- */
+
+/* Bias corrections 1 - beta1^t and 1 - beta2^t for step t >= 1.
+ * READING: the page forms them in f64 (beta.powi(t)); here they are formed in
+ * double from the binary32 betas and rounded to binary32 once. */
+void orc_adamw_bias_corrections(float beta1, float beta2, int64_t t, float* bc1, float* bc2) {
+    *bc1 = (float)(1.0 - pow((double)beta1, (double)t));
+    *bc2 = (float)(1.0 - pow((double)beta2, (double)t));
+}
+
+/* [QAT] QatOptimizer::step, the master update, element by element in the page's
+ * order (READING: binary32, one rounding per operation, left to right):
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g g;
+ *   m_hat = m / bc1;  v_hat = v / bc2;
+ *   if wd != 0: w = w - lr wd w   (decoupled weight decay, before the step);
+ *   w = w - lr m_hat / (sqrt(v_hat) + eps). */
+void orc_adamw_update(float* w, const float* g, float* m, float* v, int64_t n, float lr, float beta1,
+                      float beta2, float eps, float wd, float bc1, float bc2) {
+    const float c1 = 1.0f - beta1, c2 = 1.0f - beta2, lrwd = lr * wd;
+    for (int64_t i = 0; i < n; ++i) {
+        float mi = beta1 * m[i] + c1 * g[i];
+        float vi = beta2 * v[i] + c2 * g[i] * g[i];
+        m[i] = mi;
+        v[i] = vi;
+        float m_hat = mi / bc1;
+        float v_hat = vi / bc2;
+        float wi = w[i];
+        if (wd != 0.0f) wi = wi - lrwd * wi;
+        wi = wi - lr * m_hat / (sqrtf(v_hat) + eps);
+        w[i] = wi;
+    }
+}
+
+/* [QAT] QatOptimizer::step with an integer target: the update, then requantize:
+ * QuantParams::per_tensor_minmax of the updated master (finite min / max, flags
+ * as orc_tensor_params_int) and fake_quant_int with the rounding mode
+ * (0 nearest, 1 stochastic with the stream of orc_sr_uniform at offset + i).
+ * Outputs: params (scale, zp, real_min, real_max), codes (int8 per element, may
+ * be NULL), view = the fake-quant view. */
+uint32_t orc_qat_step_int(float* w, const float* g, float* m, float* v, int64_t n, float lr, float beta1,
+                          float beta2, float eps, float wd, int64_t t, int bits, int scheme, int rounding,
+                          uint64_t seed, uint64_t offset, float* scale, int32_t* zp, float* lo, float* hi,
+                          int8_t* codes, float* view) {
+    float bc1, bc2;
+    orc_adamw_bias_corrections(beta1, beta2, t, &bc1, &bc2);
+    orc_adamw_update(w, g, m, v, n, lr, beta1, beta2, eps, wd, bc1, bc2);
+    uint32_t flags = orc_tensor_params_int(w, n, bits, scheme, scale, zp, lo, hi);
+    if (rounding == 0) orc_fake_quant_int(w, n, bits, scheme, *scale, *zp, codes, view);
+    else orc_fake_quant_int_sr(w, n, bits, scheme, *scale, *zp, seed, offset, codes, view);
+    return flags;
+}
+
+/* [QAT] QatOptimizer::step with an fp8 target: the update, then fake_quant_fp8 of
+ * the master itself (the page's fp8 view has no scale): byte = encode(w) or
+ * encode_sr(w, u), view = decode(byte).  q (may be NULL): the bytes. */
+void orc_qat_step_fp8(float* w, const float* g, float* m, float* v, int64_t n, float lr, float beta1,
+                      float beta2, float eps, float wd, int64_t t, int fmt, int rounding, uint64_t seed,
+                      uint64_t offset, uint8_t* q, float* view) {
+    float bc1, bc2;
+    orc_adamw_bias_corrections(beta1, beta2, t, &bc1, &bc2);
+    orc_adamw_update(w, g, m, v, n, lr, beta1, beta2, eps, wd, bc1, bc2);
+    for (int64_t i = 0; i < n; ++i) {
+        uint8_t b = rounding == 0 ? orc_fp8_encode(w[i], fmt)
+                                  : orc_fp8_encode_sr(w[i], fmt, orc_sr_uniform(seed, offset + (uint64_t)i));
+        if (q) q[i] = b;
+        if (view) view[i] = orc_fp8_decode(b, fmt);
+    }
+}

@@ -78,6 +78,12 @@ _SIGS = {
                                      _P, _P]),
     "orc_fp8_encode_sr": (_U8, [_F, _INT, _F]),
     "orc_fp8_quantize_sr": (None, [_P, _I64, _INT, _F, ctypes.c_uint64, ctypes.c_uint64, _P, _P]),
+    "orc_adamw_bias_corrections": (None, [_F, _F, _I64, _P, _P]),
+    "orc_adamw_update": (None, [_P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _F, _F]),
+    "orc_qat_step_int": (_U32, [_P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _I64, _INT, _INT, _INT,
+                                ctypes.c_uint64, ctypes.c_uint64, _P, _P, _P, _P, _P, _P]),
+    "orc_qat_step_fp8": (None, [_P, _P, _P, _P, _I64, _F, _F, _F, _F, _F, _I64, _INT, _INT, ctypes.c_uint64,
+                                ctypes.c_uint64, _P, _P]),
 }
 
 
@@ -333,3 +339,56 @@ def fp8_quantize_sr(x, fmt: int, scale: float, seed: int, offset: int = 0, want_
     fq = np.empty(x.size, np.float32) if want_fq else None
     lib().orc_fp8_quantize_sr(_ptr(x), x.size, fmt, scale, seed, offset, _ptr(q), _ptr(fq))
     return q, fq
+
+
+# ---------------------------------------------------------------------------
+# QAT step ([QAT] QatOptimizer::step): AdamW master update, then requantize
+# ---------------------------------------------------------------------------
+ADAM_DEFAULTS = dict(beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def adamw_bias_corrections(beta1: float, beta2: float, t: int):
+    b1, b2 = _F(), _F()
+    lib().orc_adamw_bias_corrections(beta1, beta2, t, ctypes.byref(b1), ctypes.byref(b2))
+    return np.float32(b1.value), np.float32(b2.value)
+
+
+def _state(w, g, m, v):
+    w = _f32(w).ravel().copy()
+    g = _f32(g).ravel()
+    m = _f32(m).ravel().copy()
+    v = _f32(v).ravel().copy()
+    assert w.size == g.size == m.size == v.size
+    return w, g, m, v
+
+
+def adamw_update(w, g, m, v, lr, t, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+    """One master update; returns the new (w, m, v) (inputs are not modified)."""
+    w, g, m, v = _state(w, g, m, v)
+    bc1, bc2 = adamw_bias_corrections(beta1, beta2, t)
+    lib().orc_adamw_update(_ptr(w), _ptr(g), _ptr(m), _ptr(v), w.size, lr, beta1, beta2, eps, weight_decay,
+                           float(bc1), float(bc2))
+    return w, m, v
+
+
+def qat_step_int(w, g, m, v, lr, t, bits=8, scheme=0, rounding=0, seed=0, offset=0, beta1=0.9,
+                 beta2=0.999, eps=1e-8, weight_decay=0.0):
+    w, g, m, v = _state(w, g, m, v)
+    codes = np.empty(w.size, np.int8)
+    view = np.empty(w.size, np.float32)
+    s, z, lo, hi = _F(), _I32(), _F(), _F()
+    flags = lib().orc_qat_step_int(_ptr(w), _ptr(g), _ptr(m), _ptr(v), w.size, lr, beta1, beta2, eps,
+                                   weight_decay, t, bits, scheme, rounding, seed, offset, ctypes.byref(s),
+                                   ctypes.byref(z), ctypes.byref(lo), ctypes.byref(hi), _ptr(codes), _ptr(view))
+    return dict(w=w, m=m, v=v, scale=np.float32(s.value), zp=z.value, lo=np.float32(lo.value),
+                hi=np.float32(hi.value), codes=codes, view=view, flags=flags)
+
+
+def qat_step_fp8(w, g, m, v, lr, t, fmt=0, rounding=0, seed=0, offset=0, beta1=0.9, beta2=0.999,
+                 eps=1e-8, weight_decay=0.0):
+    w, g, m, v = _state(w, g, m, v)
+    q = np.empty(w.size, np.uint8)
+    view = np.empty(w.size, np.float32)
+    lib().orc_qat_step_fp8(_ptr(w), _ptr(g), _ptr(m), _ptr(v), w.size, lr, beta1, beta2, eps, weight_decay, t,
+                           fmt, rounding, seed, offset, _ptr(q), _ptr(view))
+    return dict(w=w, m=m, v=v, q=q, view=view)
