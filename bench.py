@@ -23,8 +23,8 @@ kernel's achieved bandwidth against the 8 TB/s HBM peak; `kernels` gives every
 op's share of the timed steps; `per_op_cold_warm` times each op on its own with
 its inputs evicted from the caches (cold) and back to back (warm);
 `copy_f32_ceiling` is a plain device copy timed the same ways; `next_rows`
-times the rows beyond the step (stochastic rounding) the same ways, outside
-`value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
+times the rows beyond the step (stochastic rounding, the QAT optimizer step) the
+same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None,
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16 (step), "
-                         "stochastic_rounding (beside the step)")
+                         "stochastic_rounding qat_step (beside the step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
     ap.add_argument("--no-next", action="store_true",
@@ -227,7 +227,37 @@ def ops_next_sr(fq, syn, torch, dev):
     return ops
 
 
-NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr}
+def ops_next_qat(fq, syn, torch, dev):
+    """One QAT optimizer step ([QAT] QatOptimizer::step) on the [4096, 4096] fp32
+    weight workload as master: AdamW update, then the int8 symmetric view
+    (recalibrated per tensor) or the fp8 E4M3 view.  Contract bytes per element:
+    read master, grad, m, v (16); write master, m, v, view (16) and the codes or
+    bytes (1)."""
+    r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
+    n = r * c
+    w = syn.rows_f32_inputs(r, c, device=dev).reshape(-1)
+    g = syn.rows_f32_inputs(r, c, device=dev, seed=7).reshape(-1)
+    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev)
+    cfg = fq.adamw_config(1e-4, weight_decay=0.01)
+    wsb = fq.fq_workspace_bytes(n)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    params = torch.empty(4, dtype=torch.int32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    codes = torch.empty(n, dtype=torch.int8, device=dev)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    view = torch.empty(n, dtype=torch.float32, device=dev)
+    t = 10
+    return [
+        Op("qat.step_int8_sym", "k_adamw_minmax+k_params_int_final+k_fq_int_tensor",
+           lambda: fq.fq_qat_step_int(w, g, m, v, n, cfg, t, 8, fq.SYM, fq.ROUND_NEAREST, 0, 0, ws, wsb, params,
+                                      codes, view, flags), 33 * n),
+        Op("qat.step_fp8_e4m3", "k_adamw_fp8",
+           lambda: fq.fq_qat_step_fp8(w, g, m, v, n, cfg, t, fq.E4M3, fq.ROUND_NEAREST, 0, 0, q, view), 33 * n),
+    ]
+
+
+NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat}
 
 
 def build_next_ops(fq, syn, torch, dev="cuda"):

@@ -435,6 +435,92 @@ __device__ __forceinline__ float fp8_decode(uint32_t b) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// Stochastic rounding ([QAT] module docs "Rounding modes", RoundingMode::
+// Stochastic): the uniform variate of element index i is word i mod 4 of
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11) at counter (floor(i/4) low 32 bits, high 32 bits, 0, 0)
+// under key (seed low, seed high), as a binary32 with 24 random bits:
+// (word >> 8) 2^-24.  Rounding: up iff the draw is below fl(t - floor(t)).
+// ---------------------------------------------------------------------------
+// multipliers and Weyl key increments of the published generator
+constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+
+__device__ __forceinline__ uint4 philox4x32_10(uint64_t block, uint32_t k0, uint32_t k1) {
+    uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32), c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += kW0;
+            k1 += kW1;
+        }
+        const uint64_t p0 = (uint64_t)kM0 * c0;
+        const uint64_t p1 = (uint64_t)kM1 * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& w, int i) {
+    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
+}
+
+// The four 24-bit draws of chunk c (elements offset + 4c .. offset + 4c + 3), as
+// integers j (the variate is j 2^-24).
+struct Draws {
+    uint32_t k0, k1;
+    uint64_t base;  // offset >> 2
+    int shift;      // offset & 3
+    static Draws make(uint64_t seed, uint64_t offset) {
+        return Draws{(uint32_t)seed, (uint32_t)(seed >> 32), offset >> 2, (int)(offset & 3)};
+    }
+    __device__ __forceinline__ void get(int64_t c, uint32_t (&j)[4]) const {
+        const uint64_t b = base + (uint64_t)c;
+        const uint4 w0 = philox4x32_10(b, k0, k1);
+        if (shift == 0) {
+            j[0] = w0.x >> 8;
+            j[1] = w0.y >> 8;
+            j[2] = w0.z >> 8;
+            j[3] = w0.w >> 8;
+        } else {
+            const uint4 w1 = philox4x32_10(b + 1, k0, k1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = e + shift;
+                j[e] = (s < 4 ? word(w0, s) : word(w1, s - 4)) >> 8;
+            }
+        }
+    }
+};
+
+// round t stochastically with the draw j 2^-24: floor(t) + (j 2^-24 < frac);
+// +-Inf stay themselves (their frac is NaN, which compares false), NaN stays NaN
+__device__ __forceinline__ float round_sr(float t, uint32_t j) {
+    const float lower = floorf(t);
+    const float frac = t - lower;
+    return ((float)j * 0x1p-24f < frac) ? lower + 1.0f : lower;
+}
+
+// fp8 cast with stochastic rounding: the unified-ULP step of |y|, ratio = |y| /
+// step exact, rounded stochastically, code = k + binade, saturated; NaN -> 0x7F
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_encode_sr(float y, uint32_t j) {
+    using F = Fp8Fmt<FMT>;
+    constexpr uint32_t emin_biased = 127u + 1u - F::bias;  // binary32 field of 2^emin
+    const float a = fminf(fabsf(y), F::big);                // anything >= big saturates
+    const uint32_t E = max(as_u(a) >> 23, emin_biased);
+    const float k = round_sr(__builtin_amdgcn_ldexpf(a, (int)(127u + F::mbits) - (int)E), j);
+    const uint32_t code = min((uint32_t)k + ((E - emin_biased) << F::mbits), F::max_code);
+    return (y != y) ? 0x7Fu : (code | ((as_u(y) >> 24) & 0x80u));
+}
+
+
 // pack the low bytes of four words into one word (little-endian order)
 __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
     uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);

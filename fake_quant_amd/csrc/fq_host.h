@@ -88,4 +88,11 @@ inline unsigned reduce_blocks(int64_t n) {
     return (unsigned)want;
 }
 
+// Pass 2 of the tensor-scope min / max over `nparts` partial records (float4:
+// finite min, finite max, max |x| bits, -) that a fused kernel left in the
+// workspace: derives the integer parameters on the device ([QAT] from_minmax,
+// real_min / real_max) and ORs NONFINITE / DEGENERATE into flags.
+int params_from_partials(const void* workspace, unsigned nparts, int bits, int scheme, fq_int_params* params,
+                         uint32_t* flags, hipStream_t stream);
+
 }  // namespace fqh

@@ -25,67 +25,6 @@ namespace {
 
 constexpr int kB = fqh::kBlock;
 
-// Philox4x32-10: multipliers and Weyl key increments of the published generator
-constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
-constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
-
-__device__ __forceinline__ uint4 philox4x32_10(uint64_t block, uint32_t k0, uint32_t k1) {
-    uint32_t c0 = (uint32_t)block, c1 = (uint32_t)(block >> 32), c2 = 0u, c3 = 0u;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += kW0;
-            k1 += kW1;
-        }
-        const uint64_t p0 = (uint64_t)kM0 * c0;
-        const uint64_t p1 = (uint64_t)kM1 * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
-        c1 = (uint32_t)p1;
-        c3 = (uint32_t)p0;
-        c0 = n0;
-        c2 = n2;
-    }
-    return make_uint4(c0, c1, c2, c3);
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& w, int i) {
-    return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w;
-}
-
-// The four 24-bit draws of chunk c (elements offset + 4c .. offset + 4c + 3), as
-// integers j (the variate is j 2^-24).
-struct Draws {
-    uint32_t k0, k1;
-    uint64_t base;  // offset >> 2
-    int shift;      // offset & 3
-    __device__ __forceinline__ void get(int64_t c, uint32_t (&j)[4]) const {
-        const uint64_t b = base + (uint64_t)c;
-        const uint4 w0 = philox4x32_10(b, k0, k1);
-        if (shift == 0) {
-            j[0] = w0.x >> 8;
-            j[1] = w0.y >> 8;
-            j[2] = w0.z >> 8;
-            j[3] = w0.w >> 8;
-        } else {
-            const uint4 w1 = philox4x32_10(b + 1, k0, k1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = e + shift;
-                j[e] = (s < 4 ? word(w0, s) : word(w1, s - 4)) >> 8;
-            }
-        }
-    }
-};
-
-// round t stochastically with the draw j 2^-24: floor(t) + (j 2^-24 < frac);
-// +-Inf stay themselves (their frac is NaN, which compares false), NaN stays NaN
-__device__ __forceinline__ float round_sr(float t, uint32_t j) {
-    const float lower = floorf(t);
-    const float frac = t - lower;
-    return ((float)j * 0x1p-24f < frac) ? lower + 1.0f : lower;
-}
-
 // ---------------------------------------------------------------------------
 // integer grid: code = clamp(round_sr(x / s), qmin - zp, qmax - zp) + zp
 // ---------------------------------------------------------------------------
@@ -165,21 +104,6 @@ __global__ __launch_bounds__(kB) void k_fq_int_tensor_sr(const float* __restrict
     else int_sr_loop<BITS, kTrue, AL>(x, n, q, P.scale, P.zero_point, d, codes, fq);
 }
 
-// ---------------------------------------------------------------------------
-// fp8 grid: the unified-ULP step of |y| (y = x / scale), ratio = |y| / step
-// exact, rounded stochastically, code = k + binade, saturated; NaN -> 0x7F
-// ---------------------------------------------------------------------------
-template <int FMT>
-__device__ __forceinline__ uint32_t fp8_encode_sr(float y, uint32_t j) {
-    using F = Fp8Fmt<FMT>;
-    constexpr uint32_t emin_biased = 127u + 1u - F::bias;  // binary32 field of 2^emin
-    const float a = fminf(fabsf(y), F::big);                // anything >= big saturates
-    const uint32_t E = max(as_u(a) >> 23, emin_biased);
-    const float k = round_sr(__builtin_amdgcn_ldexpf(a, (int)(127u + F::mbits) - (int)E), j);
-    const uint32_t code = min((uint32_t)k + ((E - emin_biased) << F::mbits), F::max_code);
-    return (y != y) ? 0x7Fu : (code | ((as_u(y) >> 24) & 0x80u));
-}
-
 template <int FMT>
 __device__ __forceinline__ float fp8_value_sr(uint32_t b, float scale) {
     const float v = fp8_decode_finite<FMT>(b) * scale;
@@ -242,10 +166,6 @@ __global__ __launch_bounds__(kB) void k_fp8_quant_sr(const float* __restrict__ x
     else fp8_sr_loop<FMT, kTrue, AL>(x, n, dv, s, d, q, fq);
 }
 
-Draws make_draws(uint64_t seed, uint64_t offset) {
-    return Draws{(uint32_t)seed, (uint32_t)(seed >> 32), offset >> 2, (int)(offset & 3)};
-}
-
 }  // namespace
 
 extern "C" {
@@ -257,7 +177,7 @@ int fq_fake_quant_int_tensor_sr(const float* x, int64_t n, int bits, int scheme,
     if (!fqh::aligned(x, 4) || !fqh::aligned(params, 4) || !fqh::aligned(fq, 4)) return FQ_E_INVALID;
     const bool al = fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, bits == 8 ? 4 : 2);
     const unsigned G = fqh::grid_all(n / 4 + 1, kB);
-    const Draws d = make_draws(seed, offset);
+    const Draws d = Draws::make(seed, offset);
     uint8_t* cd = (uint8_t*)codes;
     const int aff = scheme == FQ_AFFINE;
     if (bits == 8) {
@@ -277,7 +197,7 @@ int fq_fp8_quantize_sr(const float* x, int64_t n, int fmt, const float* scale, u
     if (!fqh::aligned(x, 4) || !fqh::aligned(scale, 4) || !fqh::aligned(fq, 4)) return FQ_E_INVALID;
     const bool al = fqh::aligned(x, 16) && fqh::aligned(q, 4) && fqh::aligned(fq, 16);
     const unsigned G = fqh::grid_all(n / 4 + 1, kB);
-    const Draws d = make_draws(seed, offset);
+    const Draws d = Draws::make(seed, offset);
     if (fmt == FQ_E4M3) {
         if (al) k_fp8_quant_sr<0, true><<<G, kB, 0, stream>>>(x, n, scale, d, q, fq);
         else k_fp8_quant_sr<0, false><<<G, kB, 0, stream>>>(x, n, scale, d, q, fq);

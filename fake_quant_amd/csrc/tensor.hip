@@ -412,6 +412,17 @@ unsigned launch_partial(const float* x, int64_t n, void* ws, hipStream_t st) {
 
 }  // namespace
 
+namespace fqh {
+
+int params_from_partials(const void* workspace, unsigned nparts, int bits, int scheme, fq_int_params* params,
+                         uint32_t* flags, hipStream_t stream) {
+    k_params_int_final<<<1, kFT, 0, stream>>>((const float4*)workspace, (int)nparts, bits,
+                                              scheme == FQ_AFFINE ? 1 : 0, params, flags);
+    return launched();
+}
+
+}  // namespace fqh
+
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------

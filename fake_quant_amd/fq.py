@@ -23,6 +23,13 @@ FLAG_NONFINITE, FLAG_DEGENERATE = 1, 2
 SYM, AFFINE = 0, 1
 E4M3, E5M2 = 0, 1
 F32, BF16 = 0, 1
+ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
+
+
+class AdamWConfig(ctypes.Structure):
+    """fq_adamw_config (include/fq.h): QatConfig's Adam / AdamW hyper-parameters."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
 
 
 class FqError(RuntimeError):
@@ -62,6 +69,9 @@ _SIGS = {
     "fq_mxfp8_rows": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _P]),
     "fq_fake_quant_int_tensor_sr": (_INT, [_P, _I64, _INT, _INT, _P, _U64, _U64, _P, _P, _P]),
     "fq_fp8_quantize_sr": (_INT, [_P, _I64, _INT, _P, _U64, _U64, _P, _P, _P]),
+    "fq_qat_step_int": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _U64, _U64, _P, _SZ, _P, _P, _P,
+                               _P, _P]),
+    "fq_qat_step_fp8": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _U64, _U64, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -253,6 +263,29 @@ def fq_fp8_quantize_sr(x, n, fmt, scale, seed, offset=0, q=None, fq=None, stream
     _need(nm, "fq", fq, 4 * n)
     _check(nm, _lib.fq_fp8_quantize_sr(_ptr(x), n, fmt, _ptr(scale), seed, offset, _ptr(q), _ptr(fq),
                                        _stream(stream)))
+
+
+def fq_qat_step_int(master, grad, m, v, n, cfg, t, bits, scheme, rounding, seed, offset, workspace,
+                    workspace_bytes, params, codes=None, view=None, flags=None, stream=None):
+    nm = "fq_qat_step_int"
+    for what, tt in (("master", master), ("grad", grad), ("m", m), ("v", v), ("view", view)):
+        _need(nm, what, tt, 4 * n)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "params", params, 16)
+    _need(nm, "codes", codes, _codes_bytes(n, bits))
+    _need(nm, "flags", flags, 4)
+    _check(nm, _lib.fq_qat_step_int(_ptr(master), _ptr(grad), _ptr(m), _ptr(v), n, ctypes.byref(cfg), t, bits,
+                                    scheme, rounding, seed, offset, _ptr(workspace), workspace_bytes, _ptr(params),
+                                    _ptr(codes), _ptr(view), _ptr(flags), _stream(stream)))
+
+
+def fq_qat_step_fp8(master, grad, m, v, n, cfg, t, fmt, rounding, seed, offset, q=None, view=None, stream=None):
+    nm = "fq_qat_step_fp8"
+    for what, tt in (("master", master), ("grad", grad), ("m", m), ("v", v), ("view", view)):
+        _need(nm, what, tt, 4 * n)
+    _need(nm, "q", q, n)
+    _check(nm, _lib.fq_qat_step_fp8(_ptr(master), _ptr(grad), _ptr(m), _ptr(v), n, ctypes.byref(cfg), t, fmt,
+                                    rounding, seed, offset, _ptr(q), _ptr(view), _stream(stream)))
 
 
 def fq_fp8_dequantize(q, n, fmt, scale, out, stream=None):
@@ -455,3 +488,34 @@ def fqb_copy_f32(x, y, n, stream=None):
     _need("fqb_copy_f32", "x", x, 4 * n)
     _need("fqb_copy_f32", "y", y, 4 * n)
     _check("fqb_copy_f32", _lib.fqb_copy_f32(_ptr(x), _ptr(y), n, _stream(stream)))
+
+
+def adamw_config(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+    return AdamWConfig(lr, beta1, beta2, eps, weight_decay)
+
+
+def qat_step_int(master, grad, m, v, t, cfg, bits=8, scheme=SYM, rounding=ROUND_NEAREST, seed=0, offset=0,
+                 want_codes=True):
+    """One QAT step with an integer target; master / m / v are updated in place.
+    Returns dict(params, codes, view, flags)."""
+    n = master.numel()
+    wsb = fq_workspace_bytes(n)
+    ws = _empty(max(wsb // 4, 1), torch.float32, master)
+    params = _empty(4, torch.int32, master)
+    flags = _zeros_flags(master)
+    codes = (_empty(n if bits == 8 else (n + 1) // 2, torch.int8 if bits == 8 else torch.uint8, master)
+             if want_codes else None)
+    view = _empty(n, torch.float32, master)
+    fq_qat_step_int(master, grad, m, v, n, cfg, t, bits, scheme, rounding, seed, offset, ws, wsb, params, codes,
+                    view, flags)
+    return dict(params=params, codes=codes, view=view, flags=flags)
+
+
+def qat_step_fp8(master, grad, m, v, t, cfg, fmt=E4M3, rounding=ROUND_NEAREST, seed=0, offset=0):
+    """One QAT step with an fp8 target; master / m / v are updated in place.
+    Returns dict(q, view)."""
+    n = master.numel()
+    q = _empty(n, torch.uint8, master)
+    view = _empty(n, torch.float32, master)
+    fq_qat_step_fp8(master, grad, m, v, n, cfg, t, fmt, rounding, seed, offset, q, view)
+    return dict(q=q, view=view)

@@ -229,6 +229,46 @@ int fq_fake_quant_int_tensor_sr(const float* x, int64_t n, int bits, int scheme,
 int fq_fp8_quantize_sr(const float* x, int64_t n, int fmt, const float* scale, uint64_t seed, uint64_t offset,
                        uint8_t* q, float* fq, hipStream_t stream);
 
+/* ---- QAT optimizer step -------------------------------------------------
+ * [QAT] QatOptimizer::step: an Adam / AdamW update of the fp32 master weights
+ * (QatConfig lr, beta1, beta2, eps, weight_decay), then the quantized view
+ * re-derived from the updated master (requantize).  Per element, binary32, one
+ * rounding per operation, in the page's order:
+ *   m = beta1 m + (1 - beta1) g;   v = beta2 v + ((1 - beta2) g) g;
+ *   m_hat = m / bc1;   v_hat = v / bc2;   (bc = 1 - beta^t, formed in double
+ *   from the binary32 beta and rounded once)
+ *   if weight_decay != 0: w = w - (lr weight_decay) w;
+ *   w = w - (lr m_hat) / (sqrt(v_hat) + eps).
+ * master, m, v are updated in place (caller-owned optimizer state, zero before
+ * step t = 1); grad is read.  All are float32 [n], device memory.  cfg is a HOST
+ * pointer; t >= 1 is the step number (FQ_E_INVALID otherwise, or when a beta is
+ * outside [0, 1)). */
+typedef struct {
+    float lr, beta1, beta2, eps, weight_decay;
+} fq_adamw_config;
+
+/* rounding of the view ([QAT] RoundingMode) */
+#define FQ_ROUND_NEAREST 0
+#define FQ_ROUND_STOCHASTIC 1
+
+/* Integer target: the update, then per_tensor_minmax of the updated master
+ * (params, flags as fq_tensor_params_int, same workspace size
+ * fq_workspace_bytes(n)) and fake_quant_int with `rounding` (stochastic: the
+ * stream of fq_fake_quant_int_tensor_sr at seed / offset).  codes (as
+ * fq_fake_quant_int_tensor) and view (float32 [n], the fake-quant view) may each
+ * be NULL, not both.  Four launches, no host synchronisation. */
+int fq_qat_step_int(float* master, const float* grad, float* m, float* v, int64_t n, const fq_adamw_config* cfg,
+                    int64_t t, int bits, int scheme, int rounding, uint64_t seed, uint64_t offset, void* workspace,
+                    size_t workspace_bytes, fq_int_params* params, void* codes, float* view, uint32_t* flags,
+                    hipStream_t stream);
+
+/* fp8 target: the update, then fake_quant_fp8 of the updated master itself (no
+ * scale, as the page's optimizer): q (bytes as fq_fp8_quantize, may be NULL) and
+ * view = decode(q) (float32 [n], may be NULL; not both NULL).  One launch. */
+int fq_qat_step_fp8(float* master, const float* grad, float* m, float* v, int64_t n, const fq_adamw_config* cfg,
+                    int64_t t, int fmt, int rounding, uint64_t seed, uint64_t offset, uint8_t* q, float* view,
+                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

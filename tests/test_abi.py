@@ -42,7 +42,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 18
+    assert len(decl) == 20
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -140,6 +140,20 @@ def test_argument_checks(fq):
     assert L.fq_fp8_quantize_sr(P, 8, 0, None, 1, 0, P, P, None) == fq.E_INVALID
     assert L.fq_fp8_quantize_sr(P, 8, 0, P, 1, 0, None, None, None) == fq.E_INVALID
     assert L.fq_fp8_quantize_sr(P + 2, 8, 0, P, 1, 0, P, P, None) == fq.E_INVALID
+    # QAT step: configuration and step number checked on the host
+    import ctypes
+    cfg = fq.AdamWConfig(0.1, 0.9, 0.999, 1e-8, 0.0)
+    bad = fq.AdamWConfig(0.1, 1.0, 0.999, 1e-8, 0.0)
+    ws = 1 << 20
+    assert L.fq_qat_step_int(P, P, P, P, 8, ctypes.byref(cfg), 1, 8, 0, 2, 0, 0, P, ws, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_qat_step_int(P, P, P, P, 8, ctypes.byref(cfg), 0, 8, 0, 0, 0, 0, P, ws, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_int(P, P, P, P, 8, ctypes.byref(bad), 1, 8, 0, 0, 0, 0, P, ws, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_int(P, P, P, P, 8, None, 1, 8, 0, 0, 0, 0, P, ws, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_int(P, P, P, P, 8, ctypes.byref(cfg), 1, 8, 0, 0, 0, 0, P, ws, P, None, None, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_int(P, P, P, P, 8, ctypes.byref(cfg), 1, 8, 0, 0, 0, 0, P, 0, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_fp8(P, P, P, P, 8, ctypes.byref(cfg), 1, 3, 0, 0, 0, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_qat_step_fp8(P, P, P, P, 8, ctypes.byref(cfg), 1, 0, 0, 0, 0, None, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_fp8(P, None, P, P, 8, ctypes.byref(cfg), 1, 0, 0, 0, 0, P, P, None) == fq.E_INVALID
     # STE: length mismatch, empty
     assert L.fq_ste_backward(P, 3, P, 2, P, P, None) == fq.E_DIM
     assert L.fq_ste_backward(P, 0, P, 0, P, P, None) == fq.E_INVALID
