@@ -267,6 +267,40 @@ uint32_t orc_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, in
     return flags;
 }
 
+/* [QAT] per_channel_params + fake_quant_int_per_channel along axis 1: every
+ * column is a channel with its own parameters, calibrated on that column only.
+ * Layouts as orc_quant_rows (codes: int8 [rows, cols] or, for 4 bits, packed
+ * nibbles ceil(cols/2) bytes per row); scale / zp: one per column. */
+uint32_t orc_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits,
+                        int scheme, uint8_t* codes, float* fq, float* scale, int32_t* zp) {
+    int32_t qmin, qmax;
+    if (orc_q_range(bits, scheme, &qmin, &qmax) != 0) return 0;
+    uint32_t flags = 0;
+    int64_t packed_row = (cols + 1) / 2;
+    for (int64_t c = 0; c < cols; ++c) {
+        const void* col = dtype == ORC_BF16 ? (const void*)((const uint16_t*)x + c)
+                                            : (const void*)((const float*)x + c);
+        float mn, mx;
+        flags |= orc_finite_min_max(col, dtype, rows, cols, &mn, &mx);
+        flags |= orc_params_from_minmax(mn, mx, bits, scheme, &scale[c], &zp[c]);
+    }
+    if (codes && bits == 4) memset(codes, 0, (size_t)(rows * packed_row));
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t c = 0; c < cols; ++c) {
+            int32_t q = orc_quantize(widen(x, dtype, r * cols + c), scale[c], zp[c], qmin, qmax);
+            if (fq) fq[r * cols + c] = orc_dequantize(q, scale[c], zp[c]);
+            if (!codes) continue;
+            if (bits == 8) {
+                ((int8_t*)codes)[r * cols + c] = (int8_t)q;
+            } else {
+                uint8_t nib = (uint8_t)(q & 0xF);
+                codes[r * packed_row + c / 2] |= (c % 2 == 0) ? (uint8_t)(nib << 4) : nib;
+            }
+        }
+    }
+    return flags;
+}
+
 /* ------------------------------------------------------------------------- */
 /* fp8: [QAT] module docs "fp8 quantization", Fp8Format, fp8_quantize_magnitude */
 /* ------------------------------------------------------------------------- */
