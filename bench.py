@@ -23,8 +23,8 @@ kernel's achieved bandwidth against the 8 TB/s HBM peak; `kernels` gives every
 op's share of the timed steps; `per_op_cold_warm` times each op on its own with
 its inputs evicted from the caches (cold) and back to back (warm);
 `copy_f32_ceiling` is a plain device copy timed the same ways; `next_rows`
-times the rows beyond the step (stochastic rounding, the QAT optimizer step) the
-same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
+times the rows beyond the step (stochastic rounding, the QAT optimizer step,
+per-column calibration) the same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None,
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16 (step), "
-                         "stochastic_rounding qat_step (beside the step)")
+                         "stochastic_rounding qat_step per_column (beside the step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
     ap.add_argument("--no-next", action="store_true",
@@ -257,7 +257,29 @@ def ops_next_qat(fq, syn, torch, dev):
     ]
 
 
-NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat}
+def ops_next_cols(fq, syn, torch, dev):
+    """Per-column (axis 1) calibration + int8 / int4 quantize of the [4096, 4096]
+    fp32 weight workload (codes, fake-quant, scale and zero-point per column)."""
+    r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
+    w = syn.rows_f32_inputs(r, c, device=dev)
+    wsb = fq.fq_cols_workspace_bytes(r, c)
+    ws = torch.empty(max(wsb // 4, 1), dtype=torch.float32, device=dev)
+    fqo = torch.empty(r * c, dtype=torch.float32, device=dev)
+    scale = torch.empty(c, dtype=torch.float32, device=dev)
+    zp = torch.empty(c, dtype=torch.int32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ops = []
+    for bits, scheme, name in ((8, fq.SYM, "int8_sym"), (4, fq.AFFINE, "int4_affine")):
+        nb = r * c if bits == 8 else r * ((c + 1) // 2)
+        codes = torch.empty(nb, dtype=torch.uint8, device=dev)
+        ops.append(Op(f"cols.{name}", "k_cols_partial+k_cols_params+k_cols_quant",
+                      lambda bits=bits, scheme=scheme, codes=codes: fq.fq_quant_cols(
+                          w, fq.F32, r, c, bits, scheme, ws, wsb, codes, fqo, scale, zp, flags),
+                      4 * r * c + nb + 4 * r * c + 8 * c))
+    return ops
+
+
+NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols}
 
 
 def build_next_ops(fq, syn, torch, dev="cuda"):

@@ -51,6 +51,10 @@ struct ExactDiv {
         y = 1.0f / s_;
         fast = (s_ >= 0x1p-60f) && (s_ <= 0x1p60f);
     }
+    // from a divisor and its reciprocal RN(1 / s) computed earlier
+    __device__ __forceinline__ ExactDiv(float s_, float y_) : s(s_), y(y_) {
+        fast = (s_ >= 0x1p-60f) && (s_ <= 0x1p60f);
+    }
     // Markstein path only; valid when `fast`.
     __device__ __forceinline__ float quick(float x) const {
         float q = x * y;

@@ -69,6 +69,8 @@ _SIGS = {
     "fq_mxfp8_rows": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _P]),
     "fq_fake_quant_int_tensor_sr": (_INT, [_P, _I64, _INT, _INT, _P, _U64, _U64, _P, _P, _P]),
     "fq_fp8_quantize_sr": (_INT, [_P, _I64, _INT, _P, _U64, _U64, _P, _P, _P]),
+    "fq_cols_workspace_bytes": (_SZ, [_I64, _I64]),
+    "fq_quant_cols": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "fq_qat_step_int": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _U64, _U64, _P, _SZ, _P, _P, _P,
                                _P, _P]),
     "fq_qat_step_fp8": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _U64, _U64, _P, _P, _P]),
@@ -176,6 +178,26 @@ def fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes=None, fq=None, st
     _check("fq_fake_quant_int_tensor",
            _lib.fq_fake_quant_int_tensor(_ptr(x), n, bits, scheme, _ptr(params), _ptr(codes), _ptr(fq),
                                          _stream(stream)))
+
+
+def fq_cols_workspace_bytes(rows, cols) -> int:
+    return int(_lib.fq_cols_workspace_bytes(rows, cols))
+
+
+def fq_quant_cols(x, dtype, rows, cols, bits, scheme, workspace, workspace_bytes, codes, fq, scale, zero_point,
+                  flags=None, stream=None):
+    nm = "fq_quant_cols"
+    esz = 4 if dtype == F32 else 2
+    _need(nm, "x", x, esz * rows * cols)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "codes", codes, rows * (cols if bits == 8 else (cols + 1) // 2))
+    _need(nm, "fq", fq, 4 * rows * cols)
+    _need(nm, "scale", scale, 4 * cols)
+    _need(nm, "zero_point", zero_point, 4 * cols)
+    _need(nm, "flags", flags, 4)
+    _check(nm, _lib.fq_quant_cols(_ptr(x), dtype, rows, cols, bits, scheme, _ptr(workspace), workspace_bytes,
+                                  _ptr(codes), _ptr(fq), _ptr(scale), _ptr(zero_point), _ptr(flags),
+                                  _stream(stream)))
 
 
 def fq_fake_quant_int_tensor_sr(x, n, bits, scheme, params, seed, offset=0, codes=None, fq=None, stream=None):
@@ -519,3 +541,21 @@ def qat_step_fp8(master, grad, m, v, t, cfg, fmt=E4M3, rounding=ROUND_NEAREST, s
     view = _empty(n, torch.float32, master)
     fq_qat_step_fp8(master, grad, m, v, n, cfg, t, fmt, rounding, seed, offset, q, view)
     return dict(q=q, view=view)
+
+
+def quant_cols(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+    """Per-column calibration + quantize of a 2-D fp32 / bf16 tensor."""
+    rows, cols = x.shape
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    wsb = fq_cols_workspace_bytes(rows, cols)
+    ws = _empty(wsb // 4, torch.float32, x)
+    codes = None
+    if want_codes:
+        codes = (_empty((rows, cols), torch.int8, x) if bits == 8
+                 else _empty((rows, (cols + 1) // 2), torch.uint8, x))
+    fq = _empty((rows, cols), torch.float32, x) if want_fq else None
+    scale = _empty(cols, torch.float32, x)
+    zp = _empty(cols, torch.int32, x)
+    flags = _zeros_flags(x)
+    fq_quant_cols(x, dtype, rows, cols, bits, scheme, ws, wsb, codes, fq, scale, zp, flags)
+    return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)

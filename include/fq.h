@@ -203,6 +203,26 @@ int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float
 int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8m0,
                   float* fq, hipStream_t stream);
 
+/* ---- per-column calibration --------------------------------------------- */
+
+/* Workspace bytes fq_quant_cols needs for a [rows, cols] tensor (0 for empty
+ * shapes): min(rows, 64) + 1 records of 16 bytes per column. */
+size_t fq_cols_workspace_bytes(int64_t rows, int64_t cols);
+
+/* [QAT] per_channel_params + fake_quant_int_per_channel with axis = 1: every
+ * column of the row-major x [rows, cols] (FQ_F32 or FQ_BF16) is a channel,
+ * calibrated on that column only (finite min / max, [QAT] from_minmax) and
+ * quantized with its own scale / zero-point, as fq_quant_rows does per row.
+ * codes (may be NULL): int8 [rows, cols] or, for 4 bits, packed nibbles
+ * ceil(cols/2) bytes per row (even column in the high nibble); fq (may be NULL):
+ * float32 [rows, cols]; scale, zero_point: [cols].  workspace: device memory of
+ * fq_cols_workspace_bytes(rows, cols), 16-byte aligned, contents not kept.
+ * Three launches (column partials over row chunks, per-column parameters,
+ * element-wise quantize); x is read twice. */
+int fq_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits, int scheme, void* workspace,
+                  size_t workspace_bytes, void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags,
+                  hipStream_t stream);
+
 /* ---- stochastic rounding ------------------------------------------------
  * [QAT] module docs "Rounding modes", RoundingMode::Stochastic: a quotient t is
  * rounded to floor(t) + 1 with probability equal to its fractional part and to

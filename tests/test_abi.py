@@ -42,7 +42,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 20
+    assert len(decl) == 22
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -140,6 +140,15 @@ def test_argument_checks(fq):
     assert L.fq_fp8_quantize_sr(P, 8, 0, None, 1, 0, P, P, None) == fq.E_INVALID
     assert L.fq_fp8_quantize_sr(P, 8, 0, P, 1, 0, None, None, None) == fq.E_INVALID
     assert L.fq_fp8_quantize_sr(P + 2, 8, 0, P, 1, 0, P, P, None) == fq.E_INVALID
+    # per-column calibration
+    assert fq.fq_cols_workspace_bytes(0, 5) == 0
+    assert fq.fq_cols_workspace_bytes(3, 5) == 4 * 5 * 16
+    assert fq.fq_cols_workspace_bytes(4096, 4096) == 65 * 4096 * 16
+    assert L.fq_quant_cols(P, 2, 4, 4, 8, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_cols(P, 0, 4, 4, 5, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_cols(P, 0, 0, 4, 8, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 16, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 1 << 20, P, P, None, P, None, None) == fq.E_INVALID
     # QAT step: configuration and step number checked on the host
     import ctypes
     cfg = fq.AdamWConfig(0.1, 0.9, 0.999, 1e-8, 0.0)

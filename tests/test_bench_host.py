@@ -64,12 +64,12 @@ def test_next_rows_pass_buffers_that_fit(monkeypatch):
     groups = bench.build_next_ops(fq, synthetic, torch, dev="cpu")
     ops = [op for g in groups.values() for op in g]
     assert [op.name for op in ops] == ["sr.fake_quant_int8", "sr.fp8_quantize_e4m3", "sr.fp8_quantize_e5m2",
-                                       "qat.step_int8_sym", "qat.step_fp8_e4m3"]
+                                       "qat.step_int8_sym", "qat.step_fp8_e4m3", "cols.int8_sym", "cols.int4_affine"]
     before = len(recorder.calls)
     for op in ops:
         op.fn()
     assert recorder.calls[before:] == ["fq_fake_quant_int_tensor_sr", "fq_fp8_quantize_sr", "fq_fp8_quantize_sr",
-                                       "fq_qat_step_int", "fq_qat_step_fp8"]
+                                       "fq_qat_step_int", "fq_qat_step_fp8", "fq_quant_cols", "fq_quant_cols"]
 
 
 def test_binding_guards_reject_bad_buffers():

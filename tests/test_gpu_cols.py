@@ -1,0 +1,80 @@
+"""GPU parity of per-column (axis 1) calibration + quantize against the oracle:
+codes, fake-quant, scales, zero-points and flags for the [4096, 4096] fp32
+weight workload (all four widths / schemes), a bf16 activation-shaped tensor,
+ragged shapes (aligned and unaligned paths, one to many row chunks), special
+columns and unaligned views."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import log
+from fake_quant_amd import synthetic
+from parity import assert_bits, assert_f32, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def check_cols(fq, orc, x_t, bits, scheme, what=""):
+    log(f"cols case {what} shape={tuple(x_t.shape)} dtype={x_t.dtype} bits={bits} scheme={scheme}")
+    bf = x_t.dtype == torch.bfloat16
+    r = fq.quant_cols(x_t, bits, scheme)
+    torch.cuda.synchronize()
+    xs = to_np(x_t)
+    ref = orc.quant_cols(xs.view(np.uint16) if bf else xs, bits, scheme, dtype=1 if bf else 0)
+    assert_bits(to_np(r["codes"]), ref["codes"], what + " codes")
+    assert_bits(to_np(r["scale"]), ref["scale"], what + " scale")
+    assert_bits(to_np(r["zp"]), ref["zp"], what + " zp")
+    assert_f32(to_np(r["fq"]), ref["fq"], what + " fq")
+    assert int(r["flags"].item()) == ref["flags"], what + " flags"
+
+
+@pytest.mark.parametrize("bits,scheme", [(8, 0), (8, 1), (4, 0), (4, 1)])
+def test_weight_full_size(fqlib, orc, bits, scheme):
+    w = synthetic.rows_f32_inputs(device="cuda")
+    check_cols(fqlib, orc, w, bits, scheme, "weights [4096, 4096]")
+
+
+def test_bf16_activation_shape(fqlib, orc):
+    a = synthetic.rows_bf16_inputs(4096, 8192, device="cuda")
+    check_cols(fqlib, orc, a, 8, 1, "bf16 [4096, 8192]")
+
+
+SHAPES = [(1, 1), (3, 5), (7, 127), (2, 4095), (5, 4097), (64, 3), (65, 9), (130, 1000), (1000, 7), (300, 256)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("bf16", [False, True])
+def test_ragged_shapes(fqlib, orc, shape, bf16):
+    rows, cols = shape
+    w = synthetic.rows_f32_inputs(rows, cols, device="cuda", seed=rows * 13 + cols)
+    if bf16:
+        w = w.to(torch.bfloat16)
+    for bits, scheme in ((8, 1), (4, 0)):
+        check_cols(fqlib, orc, w, bits, scheme, f"ragged {shape}")
+
+
+def test_special_columns(fqlib, orc):
+    rng = np.random.default_rng(1)
+    rows, cols = 200, 24
+    x = (rng.standard_normal((rows, cols)) * np.exp(rng.normal(-3, 0.5, (1, cols)))).astype(np.float32)
+    x[:, 0] = 0.0
+    x[5, 1] = np.nan
+    x[7, 2] = np.inf
+    x[:, 3] = np.nan
+    x[:, 4] *= np.float32(1e-33)
+    x[:, 5] = np.abs(x[:, 5]) + 1.0
+    x[:, 6] = -np.abs(x[:, 6]) - 1.0
+    x[:, 7] = -0.0
+    x[:, 8] *= np.float32(1e30)
+    x[::2, 9] = -np.inf
+    xt = torch.from_numpy(x).cuda()
+    for bits in (8, 4):
+        for scheme in (0, 1):
+            check_cols(fqlib, orc, xt, bits, scheme, "special columns")
+            check_cols(fqlib, orc, xt.to(torch.bfloat16), bits, scheme, "special columns bf16")
+
+
+def test_unaligned_view(fqlib, orc):
+    buf = synthetic.rows_f32_inputs(1, 100 * 64 + 3, device="cuda").reshape(-1)
+    x = buf[3:].reshape(100, 64)
+    check_cols(fqlib, orc, x, 8, 1, "unaligned")
