@@ -301,6 +301,54 @@ uint32_t orc_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, in
     return flags;
 }
 
+/* Ascending total order of binary32 values (-0 before +0), as the page's
+ * f64::total_cmp on finite values. */
+static int cmp_total(const void* a, const void* b) {
+    uint32_t ua, ub;
+    memcpy(&ua, a, 4);
+    memcpy(&ub, b, 4);
+    uint32_t ka = (ua & 0x80000000u) ? ~ua : (ua | 0x80000000u);
+    uint32_t kb = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
+    return ka < kb ? -1 : (ka > kb ? 1 : 0);
+}
+
+/* [QAT] QuantParams::per_tensor_percentile: sort the values, take the
+ * nearest-rank quantiles lo = floor(cf * last), hi = ceil((1 - cf) * last)
+ * (f64 arithmetic, last = count - 1, indices capped at last) and calibrate with
+ * from_minmax(sorted[lo], sorted[hi]).
+ * READING: non-finite values set NONFINITE and are left out (the page rejects
+ * them); with no finite value the result is DEGENERATE (scale 0, zp 0).  The
+ * caller checks 0 <= cf < 0.5.  Also returns the two selected values. */
+uint32_t orc_percentile_params(const float* x, int64_t n, int bits, int scheme, double clip_fraction,
+                               float* scale, int32_t* zp, float* lo, float* hi, float* sel_min, float* sel_max) {
+    int32_t qmin, qmax;
+    if (orc_q_range(bits, scheme, &qmin, &qmax) != 0) return 0;
+    uint32_t flags = 0;
+    float* f = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (isfinite(x[i])) f[m++] = x[i];
+        else flags |= ORC_FLAG_NONFINITE;
+    }
+    float mn = INFINITY, mx = -INFINITY;
+    if (m > 0) {
+        qsort(f, (size_t)m, sizeof(float), cmp_total);
+        int64_t last = m - 1;
+        int64_t lo_idx = (int64_t)floor(clip_fraction * (double)last);
+        int64_t hi_idx = (int64_t)ceil((1.0 - clip_fraction) * (double)last);
+        if (lo_idx > last) lo_idx = last;
+        if (hi_idx > last) hi_idx = last;
+        mn = f[lo_idx];
+        mx = f[hi_idx];
+    }
+    free(f);
+    *sel_min = mn;
+    *sel_max = mx;
+    flags |= orc_params_from_minmax(mn, mx, bits, scheme, scale, zp);
+    orc_real_bounds(*scale, *zp, qmin, qmax, lo, hi);
+    return flags;
+}
+
 /* ------------------------------------------------------------------------- */
 /* fp8: [QAT] module docs "fp8 quantization", Fp8Format, fp8_quantize_magnitude */
 /* ------------------------------------------------------------------------- */

@@ -58,6 +58,7 @@ _SIGS = {
     "orc_dequantize_int": (None, [_P, _I64, _F, _I32, _P]),
     "orc_ste_backward": (None, [_P, _P, _I64, _F, _F, _P]),
     "orc_quant_rows": (_U32, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "orc_percentile_params": (_U32, [_P, _I64, _INT, _INT, ctypes.c_double, _P, _P, _P, _P, _P, _P]),
     "orc_quant_cols": (_U32, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
     "orc_fp8_encode": (_U8, [_F, _INT]),
     "orc_fp8_decode": (_F, [_U8, _INT]),
@@ -210,6 +211,15 @@ def quant_rows(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True
     flags = lib().orc_quant_rows(_ptr(x), dtype, rows, cols, bits, scheme, _ptr(codes), _ptr(fq),
                                  _ptr(scale), _ptr(zp))
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
+
+
+def percentile_params(x, bits: int, scheme: int, clip_fraction: float):
+    x = _f32(x).ravel()
+    s, z, lo, hi, a, b = _F(), _I32(), _F(), _F(), _F(), _F()
+    flags = lib().orc_percentile_params(_ptr(x), x.size, bits, scheme, clip_fraction, ctypes.byref(s), ctypes.byref(z),
+                                        ctypes.byref(lo), ctypes.byref(hi), ctypes.byref(a), ctypes.byref(b))
+    return dict(scale=np.float32(s.value), zp=z.value, lo=np.float32(lo.value), hi=np.float32(hi.value),
+                sel_min=np.float32(a.value), sel_max=np.float32(b.value), flags=flags)
 
 
 def quant_cols(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True):
