@@ -279,7 +279,30 @@ def ops_next_cols(fq, syn, torch, dev):
     return ops
 
 
-NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols}
+def ops_next_percentile(fq, syn, torch, dev):
+    """Percentile calibration ([QAT] QuantParams::per_tensor_percentile, clip
+    fraction 0.001, int8 affine) of the 2^20 tensor and of the [4096, 4096] fp32
+    weights flattened; the algorithmic bytes are one read of the tensor, though
+    the radix selection reads it four times."""
+    params = torch.empty(4, dtype=torch.int32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    n1 = syn.FULL["tensor"]["n"]
+    x1, _ = syn.tensor_inputs(n1, device=dev)
+    r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
+    w = syn.rows_f32_inputs(r, c, device=dev)
+    ops = []
+    for name, x, n in (("tensor_2^20", x1, n1), ("weights_2^24", w, r * c)):
+        wsb = fq.fq_percentile_workspace_bytes(n)
+        ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+        ops.append(Op(f"percentile.{name}", "k_pct_first+k_pct_second+k_pct_third",
+                      lambda x=x, n=n, ws=ws, wsb=wsb: fq.fq_tensor_params_percentile(
+                          x, n, 8, fq.AFFINE, 0.001, ws, wsb, params, flags),
+                      4 * n + 16))
+    return ops
+
+
+NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols,
+                  "percentile": ops_next_percentile}
 
 
 def build_next_ops(fq, syn, torch, dev="cuda"):

@@ -5,19 +5,20 @@
 // Training (QAT) primitives": per_channel_params and fake_quant_int_per_channel
 // with axis = 1 (each column is a channel, calibrated on that column only).
 //
-// A column's elements are cols apart, so the work is three launches:
-//   1. k_cols_partial: thread (column vector, row chunk) folds the finite min /
-//      max / max |x| bits of N consecutive columns (N = 4 fp32 or 8 bf16: one
-//      16-byte load per row) over its chunk of rows -- every load instruction of
-//      a wave reads one contiguous run of a row;
-//   2. k_cols_params: one thread per column folds the chunk partials, derives the
-//      column's parameters ([QAT] from_minmax) and the reciprocal for the exact
-//      quotient;
-//   3. k_cols_quant: element-wise quantize with the parameters of each element's
-//      column, one vector of N columns of one row per thread (so one thread owns
-//      every packed nibble byte it writes).
-// Workspace: nrc chunk partials per column (16 bytes each), then one 16-byte
-// record per column (scale, reciprocal, zero-point, quotient mode).
+// A column's elements are cols apart, so a block works on a tile of 64 column
+// vectors (N = 4 fp32 or 8 bf16 columns each: one 16-byte load per row, so each
+// wave reads one contiguous run of a row) over a band of rows, its four waves
+// taking every fourth row with several row loads in flight per thread.  Three
+// launches, none with a global atomic on the data path:
+//   1. k_cols_minmax: finite min / max / non-finite of each column over each
+//      band of rows (at most 64 bands), waves merged through LDS, one partial
+//      record per (band, column);
+//   2. k_cols_fold: four threads per column fold its band partials, merged
+//      through LDS into one record per column;
+//   3. k_cols_quant: each block derives the parameters of its tile's columns
+//      ([QAT] from_minmax) into LDS once, then quantizes its rows; the blocks of
+//      the first band also write the scales, zero-points and flags.
+// x is read twice; the workspace holds the partials and the column records.
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -26,9 +27,13 @@ using namespace fqk;
 namespace {
 
 constexpr int kB = fqh::kBlock;
-constexpr int64_t kMaxChunks = 64;  // row chunks (partials per column)
+constexpr int kWaves = kB / kWave;   // waves per block
+constexpr int64_t kMaxBands = 64;    // bands of the min / max pass (partials per column)
+constexpr int kQuantRows = 32;       // rows per band of the quantize pass
+constexpr int kU = 8;                // row loads in flight per thread
+constexpr int64_t kMaxQuantBands = 65535;  // grid y limit; blocks loop over further bands
 
-int64_t row_chunks(int64_t rows) { return rows < kMaxChunks ? rows : kMaxChunks; }
+int64_t minmax_bands(int64_t rows) { return rows < kMaxBands ? rows : kMaxBands; }
 
 template <int DT>
 struct ColVec {
@@ -75,49 +80,74 @@ __device__ __forceinline__ void load_cols(const void* __restrict__ x, int64_t r,
 }
 
 template <int DT, bool AL>
-__global__ __launch_bounds__(kB) void k_cols_partial(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                     int64_t rows_per_chunk, float4* __restrict__ part) {
+__global__ __launch_bounds__(kB) void k_cols_minmax(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                    int64_t rows_per_band, float4* __restrict__ part) {
     constexpr int N = ColVec<DT>::N;
-    const int64_t cv = (int64_t)blockIdx.x * kB + threadIdx.x;
-    const int64_t c0 = cv * N;
-    if (c0 >= cols) return;
-    const int64_t chunk = blockIdx.y;
-    const int64_t r0 = chunk * rows_per_chunk;
-    const int64_t r1 = r0 + rows_per_chunk < rows ? r0 + rows_per_chunk : rows;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t c0 = ((int64_t)blockIdx.x * kWave + lane) * N;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_band;
+    const int64_t r1 = r0 + rows_per_band < rows ? r0 + rows_per_band : rows;
     MinMax m[N];
-    for (int64_t r = r0; r < r1; ++r) {
-        float v[N];
-        load_cols<DT, AL>(x, r, cols, c0, v);
+    if (c0 < cols) {
+        for (int64_t r = r0 + w; r < r1; r += kWaves * kU) {
+            float v[kU][N];
+            // rows past the band repeat the band's last row: min / max unchanged
 #pragma unroll
-        for (int e = 0; e < N; ++e) m[e].add(v[e]);
+            for (int u = 0; u < kU; ++u) {
+                const int64_t rr = r + u * kWaves;
+                load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+#pragma unroll
+                for (int e = 0; e < N; ++e) m[e].add(v[u][e]);
+        }
     }
+    __shared__ float s_mn[kWaves - 1][N][kWave], s_mx[kWaves - 1][N][kWave];
+    __shared__ uint32_t s_nf[kWaves - 1][N][kWave];
+    if (w > 0) {
 #pragma unroll
-    for (int e = 0; e < N; ++e)
-        if (c0 + e < cols) part[chunk * cols + c0 + e] = make_float4(m[e].mn, m[e].mx, as_f(m[e].nf), 0.0f);
+        for (int e = 0; e < N; ++e) {
+            s_mn[w - 1][e][lane] = m[e].mn;
+            s_mx[w - 1][e][lane] = m[e].mx;
+            s_nf[w - 1][e][lane] = m[e].nf;
+        }
+    }
+    __syncthreads();
+    if (w != 0 || c0 >= cols) return;
+    float4* prow = part + blockIdx.y * cols;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        for (int k = 0; k < kWaves - 1; ++k) m[e].merge(s_mn[k][e][lane], s_mx[k][e][lane], s_nf[k][e][lane]);
+        if (c0 + e < cols) prow[c0 + e] = make_float4(m[e].mn, m[e].mx, as_f(m[e].nf), 0.0f);
+    }
 }
 
-template <int BITS>
-__global__ __launch_bounds__(kB) void k_cols_params(const float4* __restrict__ part, int64_t nchunks, int64_t cols,
-                                                    int affine, float4* __restrict__ cpar, float* __restrict__ scale,
-                                                    int32_t* __restrict__ zp, uint32_t* __restrict__ flags) {
-    const int64_t c = (int64_t)blockIdx.x * kB + threadIdx.x;
-    if (c >= cols) return;
+// record of column c: the fold of its band partials (finite min, finite max,
+// max |x| bits)
+__global__ __launch_bounds__(kB) void k_cols_fold(const float4* __restrict__ part, int64_t nbands, int64_t cols,
+                                                  float4* __restrict__ rec) {
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t c = (int64_t)blockIdx.x * kWave + lane;
     MinMax m;
-    for (int64_t k = 0; k < nchunks; ++k) {
-        const float4 p = part[k * cols + c];
-        m.merge(p.x, p.y, as_u(p.z));
+    if (c < cols) {
+        for (int64_t b = w; b < nbands; b += kWaves * 4) {
+            float4 p[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t bb = b + u * kWaves;
+                p[u] = part[(bb < nbands ? bb : b) * cols + c];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m.merge(p[u].x, p[u].y, as_u(p[u].z));
+        }
     }
-    const IntRange rg = int_range(BITS, affine != 0);
-    const IntCal cal = calibrate(m.mn, m.mx, rg, affine != 0);
-    scale[c] = cal.scale;
-    zp[c] = cal.zp;
-    const float s = cal.scale == 0.0f ? 1.0f : cal.scale;
-    const ExactDiv d(s);
-    // (scale, reciprocal, zero-point bits, quotient mode: 0 zero scale, 1 exact fast, 2 true division)
-    const uint32_t mode = cal.scale == 0.0f ? 0u : (d.fast ? 1u : 2u);
-    cpar[c] = make_float4(cal.scale, d.y, as_f((uint32_t)cal.zp), as_f(mode));
-    const uint32_t f = (m.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
-    if (flags && f) atomicOr(flags, f);
+    __shared__ float4 s[kWaves - 1][kWave];
+    if (w > 0) s[w - 1][lane] = make_float4(m.mn, m.mx, as_f(m.nf), 0.0f);
+    __syncthreads();
+    if (w != 0 || c >= cols) return;
+    for (int k = 0; k < kWaves - 1; ++k) m.merge(s[k][lane].x, s[k][lane].y, as_u(s[k][lane].z));
+    rec[c] = make_float4(m.mn, m.mx, as_f(m.nf), 0.0f);
 }
 
 // code offset q - zp of x for one column's record (the per-element rule of
@@ -131,67 +161,121 @@ __device__ __forceinline__ float col_offset(float x, const float4& cp, float lo,
     return (t != t) ? zpf : r;
 }
 
+// codes and fake-quant values of the N columns from c0 of row r
+template <int N, int BITS, bool AL>
+__device__ __forceinline__ void store_row(const int (&code)[N], const float (&o)[N], int64_t r, int64_t cols,
+                                          int64_t c0, int64_t pstride, uint8_t* __restrict__ codes,
+                                          float* __restrict__ fq) {
+    if (AL) {
+        if (codes) {
+            uint8_t* crow = codes + r * pstride;
+            if (BITS == 8) {
+                const uint32_t w0 = pack4(code[0], code[1], code[2], code[3]);
+                if (N == 4) reinterpret_cast<uint32_t*>(crow)[c0 / 4] = w0;
+                else reinterpret_cast<uint2*>(crow)[c0 / 8] = make_uint2(w0, pack4(code[4 % N], code[5 % N], code[6 % N], code[7 % N]));
+            } else {
+                const uint32_t b01 = nib2(code[0], code[1]), b23 = nib2(code[2], code[3]);
+                if (N == 4) {
+                    reinterpret_cast<uint16_t*>(crow)[c0 / 4] = (uint16_t)(b01 | (b23 << 8));
+                } else {
+                    const uint32_t b45 = nib2(code[4 % N], code[5 % N]), b67 = nib2(code[6 % N], code[7 % N]);
+                    reinterpret_cast<uint32_t*>(crow)[c0 / 8] = b01 | (b23 << 8) | (b45 << 16) | (b67 << 24);
+                }
+            }
+        }
+        if (fq) {
+            float4* fr = reinterpret_cast<float4*>(fq + r * cols + c0);
+            store_nt(fr, make_float4(o[0], o[1], o[2], o[3]));
+            if (N == 8) store_nt(fr + 1, make_float4(o[4 % N], o[5 % N], o[6 % N], o[7 % N]));
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        const int64_t c = c0 + e;
+        if (c >= cols) break;
+        if (fq) fq[r * cols + c] = o[e];
+        if (codes && BITS == 8) codes[r * pstride + c] = (uint8_t)code[e];
+    }
+    if (codes && BITS == 4) {
+#pragma unroll
+        for (int e = 0; e < N; e += 2) {
+            const int64_t c = c0 + e;
+            if (c >= cols) break;
+            codes[r * pstride + c / 2] = (uint8_t)nib2(code[e], c + 1 < cols ? code[e + 1] : 0);
+        }
+    }
+}
+
 template <int DT, int BITS, bool AL>
 __global__ __launch_bounds__(kB) void k_cols_quant(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                   int affine, const float4* __restrict__ cpar,
-                                                   uint8_t* __restrict__ codes, float* __restrict__ fq) {
+                                                   int affine, const float4* __restrict__ rec,
+                                                   uint8_t* __restrict__ codes, float* __restrict__ fq,
+                                                   float* __restrict__ scale, int32_t* __restrict__ zp,
+                                                   uint32_t* __restrict__ flags) {
     constexpr int N = ColVec<DT>::N;
-    const int64_t ncv = (cols + N - 1) / N;
-    const int64_t total = rows * ncv;
+    constexpr int TC = kWave * N;  // columns of the tile
+    __shared__ float4 s_par[TC];
+    const int64_t ct0 = (int64_t)blockIdx.x * TC;
     const IntRange rg = int_range(BITS, affine != 0);
-    const int64_t pstride = BITS == 8 ? cols : (cols + 1) / 2;
-    for (int64_t i = (int64_t)blockIdx.x * kB + threadIdx.x; i < total; i += (int64_t)gridDim.x * kB) {
-        const int64_t r = i / ncv, c0 = (i % ncv) * N;
-        float v[N];
-        load_cols<DT, AL>(x, r, cols, c0, v);
-        int code[N];
-        float o[N];
-#pragma unroll
-        for (int e = 0; e < N; ++e) {
-            const int64_t c = c0 + e < cols ? c0 + e : cols - 1;
-            const float4 cp = cpar[c];
-            const int zpv = (int)as_u(cp.z);
-            o[e] = col_offset(v[e], cp, (float)(rg.qmin - zpv), (float)(rg.qmax - zpv));
-            code[e] = (int)o[e] + zpv;
-            o[e] *= cp.x;
+    // (scale, reciprocal, zero-point bits, quotient mode: 0 zero scale, 1 exact fast, 2 true division)
+    for (int j = threadIdx.x; j < TC; j += kB) {
+        const int64_t c = ct0 + j;
+        if (c >= cols) {
+            s_par[j] = make_float4(0.0f, 1.0f, 0.0f, 0.0f);
+            continue;
         }
-        if (AL) {
-            if (codes) {
-                uint8_t* crow = codes + r * pstride;
-                if (BITS == 8) {
-                    const uint32_t w0 = pack4(code[0], code[1], code[2], code[3]);
-                    if (N == 4) reinterpret_cast<uint32_t*>(crow)[c0 / 4] = w0;
-                    else reinterpret_cast<uint2*>(crow)[c0 / 8] = make_uint2(w0, pack4(code[4 % N], code[5 % N], code[6 % N], code[7 % N]));
-                } else {
-                    const uint32_t b01 = nib2(code[0], code[1]), b23 = nib2(code[2], code[3]);
-                    if (N == 4) {
-                        reinterpret_cast<uint16_t*>(crow)[c0 / 4] = (uint16_t)(b01 | (b23 << 8));
-                    } else {
-                        const uint32_t b45 = nib2(code[4 % N], code[5 % N]), b67 = nib2(code[6 % N], code[7 % N]);
-                        reinterpret_cast<uint32_t*>(crow)[c0 / 8] = b01 | (b23 << 8) | (b45 << 16) | (b67 << 24);
-                    }
-                }
-            }
-            if (fq) {
-                float4* fr = reinterpret_cast<float4*>(fq + r * cols + c0);
-                store_nt(fr, make_float4(o[0], o[1], o[2], o[3]));
-                if (N == 8) store_nt(fr + 1, make_float4(o[4 % N], o[5 % N], o[6 % N], o[7 % N]));
-            }
-        } else {
+        const float4 k = rec[c];
+        const IntCal cal = calibrate(k.x, k.y, rg, affine != 0);
+        const ExactDiv d(cal.scale == 0.0f ? 1.0f : cal.scale);
+        const uint32_t mode = cal.scale == 0.0f ? 0u : (d.fast ? 1u : 2u);
+        s_par[j] = make_float4(cal.scale, d.y, as_f((uint32_t)cal.zp), as_f(mode));
+        if (blockIdx.y == 0) {
+            scale[c] = cal.scale;
+            zp[c] = cal.zp;
+            const uint32_t f = (as_u(k.z) >= 0x7F800000u ? FQ_FLAG_NONFINITE : 0u) |
+                               (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+            if (flags && f) atomicOr(flags, f);
+        }
+    }
+    __syncthreads();
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t c0 = ct0 + (int64_t)lane * N;
+    if (c0 >= cols) return;
+    float4 cp[N];
+    float lo[N], hi[N];
+    int zpv[N];
 #pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const int64_t c = c0 + e;
-                if (c >= cols) break;
-                if (fq) fq[r * cols + c] = o[e];
-                if (codes && BITS == 8) codes[r * pstride + c] = (uint8_t)code[e];
-            }
-            if (codes && BITS == 4) {
+    for (int e = 0; e < N; ++e) {
+        cp[e] = s_par[lane * N + e];
+        zpv[e] = (int)as_u(cp[e].z);
+        lo[e] = (float)(rg.qmin - zpv[e]);
+        hi[e] = (float)(rg.qmax - zpv[e]);
+    }
+    const int64_t pstride = BITS == 8 ? cols : (cols + 1) / 2;
+    for (int64_t band = blockIdx.y; band * kQuantRows < rows; band += gridDim.y) {
+        const int64_t r0 = band * kQuantRows;
+        const int64_t r1 = r0 + kQuantRows < rows ? r0 + kQuantRows : rows;
+        for (int64_t rb = r0 + w; rb < r1; rb += kWaves * kU) {
+            float v[kU][N];
 #pragma unroll
-                for (int e = 0; e < N; e += 2) {
-                    const int64_t c = c0 + e;
-                    if (c >= cols) break;
-                    codes[r * pstride + c / 2] = (uint8_t)nib2(code[e], c + 1 < cols ? code[e + 1] : 0);
+            for (int u = 0; u < kU; ++u) {
+                const int64_t rr = rb + u * kWaves;
+                load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t r = rb + u * kWaves;
+                if (r >= r1) break;
+                int code[N];
+                float o[N];
+#pragma unroll
+                for (int e = 0; e < N; ++e) {
+                    o[e] = col_offset(v[u][e], cp[e], lo[e], hi[e]);
+                    code[e] = (int)o[e] + zpv[e];
+                    o[e] *= cp[e].x;
                 }
+                store_row<N, BITS, AL>(code, o, r, cols, c0, pstride, codes, fq);
             }
         }
     }
@@ -201,21 +285,23 @@ template <int DT, int BITS>
 int launch_cols(const void* x, int64_t rows, int64_t cols, int affine, void* ws, uint8_t* codes, float* fq,
                 float* scale, int32_t* zp, uint32_t* flags, hipStream_t st) {
     constexpr int N = ColVec<DT>::N;
-    const int64_t nrc = row_chunks(rows);
-    const int64_t rpc = (rows + nrc - 1) / nrc;
+    const int64_t nb = minmax_bands(rows);
+    const int64_t rpb = (rows + nb - 1) / nb;
     float4* part = reinterpret_cast<float4*>(ws);
-    float4* cpar = part + nrc * cols;
+    float4* rec = part + nb * cols;
     const size_t code_align = BITS == 8 ? (N == 4 ? 4 : 8) : (N == 4 ? 2 : 4);
     const bool al = (cols % N == 0) && fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, code_align);
-    const int64_t ncv = (cols + N - 1) / N;
-    const dim3 g1((unsigned)((ncv + kB - 1) / kB), (unsigned)nrc);
-    if (al) k_cols_partial<DT, true><<<g1, kB, 0, st>>>(x, rows, cols, rpc, part);
-    else k_cols_partial<DT, false><<<g1, kB, 0, st>>>(x, rows, cols, rpc, part);
-    k_cols_params<BITS><<<(unsigned)((cols + kB - 1) / kB), kB, 0, st>>>(part, nrc, cols, affine, cpar, scale, zp,
-                                                                        flags);
-    const unsigned g3 = fqh::grid_all(rows * ncv, kB);
-    if (al) k_cols_quant<DT, BITS, true><<<g3, kB, 0, st>>>(x, rows, cols, affine, cpar, codes, fq);
-    else k_cols_quant<DT, BITS, false><<<g3, kB, 0, st>>>(x, rows, cols, affine, cpar, codes, fq);
+    const int64_t tiles = (cols + kWave * N - 1) / (kWave * N);
+    if (tiles > 0x7FFFFFFF) return FQ_E_INVALID;
+    const dim3 g1((unsigned)tiles, (unsigned)nb);
+    if (al) k_cols_minmax<DT, true><<<g1, kB, 0, st>>>(x, rows, cols, rpb, part);
+    else k_cols_minmax<DT, false><<<g1, kB, 0, st>>>(x, rows, cols, rpb, part);
+    k_cols_fold<<<(unsigned)((cols + kWave - 1) / kWave), kB, 0, st>>>(part, nb, cols, rec);
+    int64_t qb = (rows + kQuantRows - 1) / kQuantRows;
+    qb = qb < kMaxQuantBands ? qb : kMaxQuantBands;
+    const dim3 g2((unsigned)tiles, (unsigned)qb);
+    if (al) k_cols_quant<DT, BITS, true><<<g2, kB, 0, st>>>(x, rows, cols, affine, rec, codes, fq, scale, zp, flags);
+    else k_cols_quant<DT, BITS, false><<<g2, kB, 0, st>>>(x, rows, cols, affine, rec, codes, fq, scale, zp, flags);
     return fqh::launched();
 }
 
@@ -225,7 +311,7 @@ extern "C" {
 
 size_t fq_cols_workspace_bytes(int64_t rows, int64_t cols) {
     if (rows < 1 || cols < 1) return 0;
-    return (size_t)((row_chunks(rows) + 1) * cols * 16);
+    return (size_t)((minmax_bands(rows) + 1) * cols * 16);
 }
 
 int fq_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits, int scheme, void* workspace,

@@ -71,6 +71,8 @@ _SIGS = {
     "fq_fp8_quantize_sr": (_INT, [_P, _I64, _INT, _P, _U64, _U64, _P, _P, _P]),
     "fq_cols_workspace_bytes": (_SZ, [_I64, _I64]),
     "fq_quant_cols": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _SZ, _P, _P, _P, _P, _P, _P]),
+    "fq_percentile_workspace_bytes": (_SZ, [_I64]),
+    "fq_tensor_params_percentile": (_INT, [_P, _I64, _INT, _INT, ctypes.c_double, _P, _SZ, _P, _P, _P]),
     "fq_qat_step_int": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _U64, _U64, _P, _SZ, _P, _P, _P,
                                _P, _P]),
     "fq_qat_step_fp8": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _U64, _U64, _P, _P, _P]),
@@ -364,6 +366,21 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def fq_percentile_workspace_bytes(n) -> int:
+    return int(_lib.fq_percentile_workspace_bytes(n))
+
+
+def fq_tensor_params_percentile(x, n, bits, scheme, clip_fraction, workspace, workspace_bytes, params, flags=None,
+                                stream=None):
+    nm = "fq_tensor_params_percentile"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "params", params, 16)
+    _need(nm, "flags", flags, 4)
+    _check(nm, _lib.fq_tensor_params_percentile(_ptr(x), n, bits, scheme, float(clip_fraction), _ptr(workspace),
+                                                workspace_bytes, _ptr(params), _ptr(flags), _stream(stream)))
+
+
 def _zeros_flags(like):
     return torch.zeros(1, dtype=torch.int32, device=like.device)
 
@@ -376,6 +393,17 @@ def params_int(x, bits=8, scheme=SYM):
     params = _empty(4, torch.int32, x)
     flags = _zeros_flags(x)
     fq_tensor_params_int(x, n, bits, scheme, ws, wsb, params, flags)
+    return params, flags
+
+
+def params_percentile(x, clip_fraction, bits=8, scheme=SYM):
+    """Per-tensor calibration on the clipped tails -> (params int32[4], flags)."""
+    n = x.numel()
+    wsb = fq_percentile_workspace_bytes(n)
+    ws = _empty(wsb // 4, torch.float32, x)
+    params = _empty(4, torch.int32, x)
+    flags = _zeros_flags(x)
+    fq_tensor_params_percentile(x, n, bits, scheme, clip_fraction, ws, wsb, params, flags)
     return params, flags
 
 

@@ -217,11 +217,36 @@ size_t fq_cols_workspace_bytes(int64_t rows, int64_t cols);
  * ceil(cols/2) bytes per row (even column in the high nibble); fq (may be NULL):
  * float32 [rows, cols]; scale, zero_point: [cols].  workspace: device memory of
  * fq_cols_workspace_bytes(rows, cols), 16-byte aligned, contents not kept.
- * Three launches (column partials over row chunks, per-column parameters,
- * element-wise quantize); x is read twice. */
+ * Three launches (column min / max over at most 64 bands of rows, the fold of
+ * the bands, quantize with per-column parameters); x is read twice. */
 int fq_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits, int scheme, void* workspace,
                   size_t workspace_bytes, void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags,
                   hipStream_t stream);
+
+/* ---- percentile calibration ---------------------------------------------- */
+
+/* Workspace bytes fq_tensor_params_percentile needs for n elements (0 for
+ * n < 1): the selection state plus candidate slots for about one element in 16. */
+size_t fq_percentile_workspace_bytes(int64_t n);
+
+/* [QAT] QuantParams::per_tensor_percentile: calibration on the clipped tails of
+ * x[n] (float32, device).  With the m finite elements in ascending order
+ * (-0 before +0) and last = m - 1, lo = floor(cf * last) and
+ * hi = ceil((1 - cf) * last), both in double and at most last; the order
+ * statistics f[lo] and f[hi] take the place of min and max in the calibration of
+ * fq_tensor_params_int.  Non-finite elements are left out and set
+ * FQ_FLAG_NONFINITE (the page refuses them); no finite element gives scale 0 and
+ * FQ_FLAG_DEGENERATE as well.  clip_fraction cf in [0, 0.5) (FQ_E_INVALID
+ * otherwise; 0 gives the min / max calibration).  workspace: device memory of
+ * fq_percentile_workspace_bytes(n), 16-byte aligned, cleared by the call itself,
+ * contents not kept.  params, flags: device, as fq_tensor_params_int.  Four
+ * launches (three passes that narrow both order statistics by 11, 11 and 10 bits
+ * of an order-preserving key; x is read twice, the last pass reading only the
+ * candidates the second one kept, or x once more if they did not fit); no host
+ * synchronisation. */
+int fq_tensor_params_percentile(const float* x, int64_t n, int bits, int scheme, double clip_fraction,
+                                void* workspace, size_t workspace_bytes, fq_int_params* params, uint32_t* flags,
+                                hipStream_t stream);
 
 /* ---- stochastic rounding ------------------------------------------------
  * [QAT] module docs "Rounding modes", RoundingMode::Stochastic: a quotient t is

@@ -42,7 +42,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 22
+    assert len(decl) == 24
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -149,6 +149,20 @@ def test_argument_checks(fq):
     assert L.fq_quant_cols(P, 0, 0, 4, 8, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_INVALID
     assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 16, P, P, P, P, None, None) == fq.E_INVALID
     assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 1 << 20, P, P, None, P, None, None) == fq.E_INVALID
+    # percentile calibration: clip fraction in [0, 0.5), fixed workspace
+    assert fq.fq_percentile_workspace_bytes(0) == 0
+    wsp = fq.fq_percentile_workspace_bytes(8)
+    assert wsp >= 3 * 2 * 2048 * 8 and wsp % 4 == 0
+    assert fq.fq_percentile_workspace_bytes(1 << 24) >= wsp + 4 * (1 << 24) // 16
+    assert L.fq_tensor_params_percentile(P, 8, 5, 0, 0.01, P, wsp, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_tensor_params_percentile(P, 8, 8, 2, 0.01, P, wsp, P, None, None) == fq.E_UNSUPPORTED
+    for cf in (-0.01, 0.5, 0.7, float("nan"), float("inf")):
+        assert L.fq_tensor_params_percentile(P, 8, 8, 0, cf, P, wsp, P, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_percentile(P, 0, 8, 0, 0.01, P, wsp, P, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_percentile(P, 8, 8, 0, 0.01, P, wsp - 1, P, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_percentile(P, 8, 8, 0, 0.01, None, wsp, P, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_percentile(P, 8, 8, 0, 0.01, P, wsp, None, None, None) == fq.E_INVALID
+    assert L.fq_tensor_params_percentile(P + 2, 8, 8, 0, 0.01, P, wsp, P, None, None) == fq.E_INVALID
     # QAT step: configuration and step number checked on the host
     import ctypes
     cfg = fq.AdamWConfig(0.1, 0.9, 0.999, 1e-8, 0.0)

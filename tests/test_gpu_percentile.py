@@ -1,0 +1,137 @@
+"""GPU parity of percentile calibration ([QAT] QuantParams::per_tensor_percentile)
+against the oracle: scale, zero-point, real bounds and flags bit for bit, for
+every width / scheme, clip fractions from 0 to just under 1/2, sizes from one
+element through several histogram workgroups and a ragged tail to the 2^24
+weight and 2^26 fp8 workloads, and the cases that stress the selection: ties
+across the selected rank, signed zeros, subnormals, values at the binary32
+limits, one-sided data, non-finite elements (none finite at all included), an
+unaligned view, and a workspace reused dirty between calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import log
+from fake_quant_amd import synthetic
+from parity import assert_bits, to_np
+
+pytestmark = pytest.mark.gpu
+
+CFS = [0.0, 1e-4, 0.001, 0.01, 0.1, 0.25, 0.49999]
+
+
+def check(fq, orc, x_t, bits, scheme, cf, what="", ws=None):
+    n = x_t.numel()
+    log(f"percentile case {what} n={n} bits={bits} scheme={scheme} cf={cf}")
+    if ws is None:
+        params, flags = fq.params_percentile(x_t, cf, bits, scheme)
+    else:
+        wsb = ws.numel() * ws.element_size()
+        params = torch.empty(4, dtype=torch.int32, device=x_t.device)
+        flags = torch.zeros(1, dtype=torch.int32, device=x_t.device)
+        fq.fq_tensor_params_percentile(x_t, n, bits, scheme, cf, ws, wsb, params, flags)
+    torch.cuda.synchronize()
+    ref = orc.percentile_params(to_np(x_t), bits, scheme, cf)
+    s, zp, lo, hi = fq.params_fields(params)
+    assert_bits(np.float32([s, lo, hi]), np.float32([ref["scale"], ref["lo"], ref["hi"]]), what + " params")
+    assert zp == ref["zp"], what
+    assert int(flags.item()) == ref["flags"], what
+    return ref
+
+
+def test_page_outlier(fqlib, orc):
+    v = np.concatenate([np.arange(100) / 100.0, [1000.0]]).astype(np.float32)
+    x = torch.from_numpy(v).cuda()
+    ref = check(fqlib, orc, x, 8, 0, 0.02, "page outlier")
+    assert ref["sel_max"] == np.float32(0.98)
+
+
+@pytest.mark.parametrize("bits,scheme", [(8, 0), (8, 1), (4, 0), (4, 1)])
+@pytest.mark.parametrize("cf", CFS)
+def test_tensor_workload(fqlib, orc, bits, scheme, cf):
+    x, _ = synthetic.tensor_inputs(device="cuda")
+    check(fqlib, orc, x, bits, scheme, cf, "tensor 2^20")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 63, 255, 1023, 1024, 1025, 4097, 65539, (1 << 20) + 3])
+def test_sizes(fqlib, orc, n):
+    rng = np.random.default_rng(n)
+    v = (rng.standard_t(3, n) * 0.3 + 0.05).astype(np.float32)
+    x = torch.from_numpy(v).cuda()
+    for cf, scheme in ((0.0, 0), (0.01, 1), (0.2, 1), (0.49999, 0)):
+        check(fqlib, orc, x, 8, scheme, cf, f"n={n}")
+
+
+def test_weight_full_size(fqlib, orc):
+    w = synthetic.rows_f32_inputs(device="cuda").reshape(-1)
+    for cf, scheme in ((0.001, 1), (0.01, 0)):
+        check(fqlib, orc, w, 8, scheme, cf, "weights 2^24")
+
+
+def test_fp8_workload_with_specials(fqlib, orc):
+    # the 2^26 fp8 workload carries NaN / +-Inf / huge / subnormal elements
+    x = synthetic.fp8_inputs(device="cuda")
+    check(fqlib, orc, x, 8, 1, 0.001, "fp8 2^26")
+
+
+def test_ties_and_special_values(fqlib, orc):
+    rng = np.random.default_rng(11)
+    cases = {
+        "all equal": np.full(5000, 0.75, np.float32),
+        "few levels": rng.integers(-3, 4, 100000).astype(np.float32) * 0.5,
+        "signed zeros": np.where(rng.random(3001) < 0.5, -0.0, 0.0).astype(np.float32),
+        "zeros and one": np.concatenate([np.zeros(999, np.float32), np.float32([-0.0, 1.0])]),
+        "subnormals": (rng.standard_normal(7000) * 1e-40).astype(np.float32),
+        "binary32 limits": np.float32([3.4028235e38, -3.4028235e38, 1e-45, -1e-45] * 300
+                                      + list(rng.standard_normal(800))),
+        "negative only": -np.abs(rng.standard_normal(9001)).astype(np.float32) - 1.0,
+        "positive only": np.abs(rng.standard_normal(9001)).astype(np.float32) + 2.0,
+        "near ties": (1.0 + np.arange(4096, dtype=np.float32) * np.float32(2 ** -23)).astype(np.float32),
+    }
+    for name, v in cases.items():
+        x = torch.from_numpy(np.ascontiguousarray(v)).cuda()
+        for cf in (0.0, 0.001, 0.1, 0.3):
+            for bits, scheme in ((8, 0), (4, 1)):
+                check(fqlib, orc, x, bits, scheme, cf, name)
+
+
+def test_nonfinite(fqlib, orc):
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal(20011).astype(np.float32)
+    v[::97] = np.nan
+    v[5::101] = np.inf
+    v[7::103] = -np.inf
+    x = torch.from_numpy(v).cuda()
+    for cf in (0.0, 0.05):
+        check(fqlib, orc, x, 8, 1, cf, "mixed non-finite")
+    for name, w in (("all NaN", np.full(777, np.nan, np.float32)),
+                    ("only infinities", np.float32([np.inf, -np.inf] * 50)),
+                    ("one finite", np.float32([np.nan] * 40 + [-2.5] + [np.inf] * 40))):
+        check(fqlib, orc, torch.from_numpy(w).cuda(), 8, 0, 0.1, name)
+        check(fqlib, orc, torch.from_numpy(w).cuda(), 4, 1, 0.0, name)
+
+
+def test_unaligned_view_and_dirty_workspace(fqlib, orc):
+    rng = np.random.default_rng(13)
+    base = torch.from_numpy(rng.standard_normal(50003).astype(np.float32)).cuda()
+    wsb = fqlib.fq_percentile_workspace_bytes(50003)
+    ws = torch.full((wsb,), 0xA5, dtype=torch.uint8, device="cuda")
+    for off, n in ((1, 50001), (3, 49999), (0, 50003), (2, 7)):
+        check(fqlib, orc, base[off:off + n], 8, 1, 0.01, f"view +{off}", ws=ws)
+    # a second, smaller call on the workspace the larger one left behind
+    check(fqlib, orc, base[:100], 4, 0, 0.1, "reuse smaller", ws=ws)
+
+
+def test_candidate_slice_overflow(fqlib, orc):
+    # 2^20 elements: 2^18 16-byte chunks over 256 histogram workgroups of 256
+    # threads, chunk c taken by thread c mod 65536, so workgroup 0 owns the chunks
+    # with c mod 65536 < 256.  Filling exactly those with the tensor's top value
+    # sends 4096 keys into workgroup 0's candidate slice (room for about 1 in 16)
+    # while the other slices stay small: the last pass must fall back to x.
+    n = 1 << 20
+    v = (np.random.default_rng(14).standard_normal(n) * 0.1).astype(np.float32)
+    chunks = v.reshape(-1, 4)
+    chunks[(np.arange(chunks.shape[0]) % 65536) < 256] = 1.0
+    x = torch.from_numpy(v).cuda()
+    for cf, scheme in ((0.001, 1), (0.0001, 0), (0.01, 1)):
+        check(fqlib, orc, x, 8, scheme, cf, "one slice overflows")
