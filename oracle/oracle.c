@@ -301,6 +301,53 @@ uint32_t orc_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, in
     return flags;
 }
 
+/* [CS] demo 3 "granularity": group-wise quantization -- groups of `group`
+ * consecutive elements along the last dimension of each row, one scale per
+ * group.
+ * READING (the body of quantize_int is not on the pages): a group is calibrated
+ * as a channel is ([QAT] per_channel_params: finite min / max, from_minmax) and
+ * quantized with the channel rule; when group does not divide cols, the last
+ * group of a row holds the cols mod group elements left; scales are binary32
+ * (the demo's FP16 scale enters only its bits-per-element count).
+ * Layouts: codes as orc_quant_rows; scale / zp: [rows, ceil(cols / group)]. */
+uint32_t orc_quant_groups(const void* x, int dtype, int64_t rows, int64_t cols, int64_t group, int bits,
+                          int scheme, uint8_t* codes, float* fq, float* scale, int32_t* zp) {
+    int32_t qmin, qmax;
+    if (orc_q_range(bits, scheme, &qmin, &qmax) != 0 || group < 1) return 0;
+    uint32_t flags = 0;
+    int64_t packed_row = (cols + 1) / 2;
+    int64_t ngroups = (cols + group - 1) / group;
+    if (codes && bits == 4) memset(codes, 0, (size_t)(rows * packed_row));
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t g = 0; g < ngroups; ++g) {
+            int64_t start = g * group;
+            int64_t len = cols - start < group ? cols - start : group;
+            int64_t base = r * cols + start;
+            const void* grp = dtype == ORC_BF16 ? (const void*)((const uint16_t*)x + base)
+                                                : (const void*)((const float*)x + base);
+            float mn, mx, s;
+            int32_t z;
+            flags |= orc_finite_min_max(grp, dtype, len, 1, &mn, &mx);
+            flags |= orc_params_from_minmax(mn, mx, bits, scheme, &s, &z);
+            scale[r * ngroups + g] = s;
+            zp[r * ngroups + g] = z;
+            for (int64_t i = 0; i < len; ++i) {
+                int64_t c = start + i;
+                int32_t q = orc_quantize(widen(grp, dtype, i), s, z, qmin, qmax);
+                if (fq) fq[r * cols + c] = orc_dequantize(q, s, z);
+                if (!codes) continue;
+                if (bits == 8) {
+                    ((int8_t*)codes)[r * cols + c] = (int8_t)q;
+                } else {
+                    uint8_t nib = (uint8_t)(q & 0xF);
+                    codes[r * packed_row + c / 2] |= (c % 2 == 0) ? (uint8_t)(nib << 4) : nib;
+                }
+            }
+        }
+    }
+    return flags;
+}
+
 /* Ascending total order of binary32 values (-0 before +0), as the page's
  * f64::total_cmp on finite values. */
 static int cmp_total(const void* a, const void* b) {

@@ -60,6 +60,7 @@ _SIGS = {
     "orc_quant_rows": (_U32, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
     "orc_percentile_params": (_U32, [_P, _I64, _INT, _INT, ctypes.c_double, _P, _P, _P, _P, _P, _P]),
     "orc_quant_cols": (_U32, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "orc_quant_groups": (_U32, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
     "orc_fp8_encode": (_U8, [_F, _INT]),
     "orc_fp8_decode": (_F, [_U8, _INT]),
     "orc_fp8_encode_n": (None, [_P, _I64, _INT, _P]),
@@ -238,6 +239,27 @@ def quant_cols(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True
     zp = np.empty(cols, np.int32)
     flags = lib().orc_quant_cols(_ptr(x), dtype, rows, cols, bits, scheme, _ptr(codes), _ptr(fq), _ptr(scale),
                                  _ptr(zp))
+    return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
+
+
+def quant_groups(x, group: int, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True):
+    """Group-wise calibration + fake-quant along the last dimension; x as for
+    quant_rows; scale / zp: [rows, ceil(cols / group)]."""
+    if dtype == BF16:
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+    else:
+        x = _f32(x)
+    rows, cols = x.shape
+    ng = (cols + group - 1) // group
+    if bits == 8:
+        codes = np.empty((rows, cols), np.int8)
+    else:
+        codes = np.empty((rows, (cols + 1) // 2), np.uint8)
+    fq = np.empty((rows, cols), np.float32) if want_fq else None
+    scale = np.empty((rows, ng), np.float32)
+    zp = np.empty((rows, ng), np.int32)
+    flags = lib().orc_quant_groups(_ptr(x), dtype, rows, cols, group, bits, scheme, _ptr(codes), _ptr(fq),
+                                   _ptr(scale), _ptr(zp))
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
 
 
