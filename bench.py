@@ -301,8 +301,37 @@ def ops_next_percentile(fq, syn, torch, dev):
     return ops
 
 
+def ops_next_groups(fq, syn, torch, dev):
+    """Group-wise quantization along rows ([CS] demo 3 granularity): the
+    [4096, 4096] fp32 weights in INT4 groups of 128 and INT8 groups of 32, and
+    the bf16 activations in INT8 groups of 128 (codes, fake-quant, and a scale
+    and zero-point per group)."""
+    ops = []
+    r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
+    w = syn.rows_f32_inputs(r, c, device=dev)
+    rb, cb = syn.FULL["rows_bf16"]["rows"], syn.FULL["rows_bf16"]["cols"]
+    a = syn.rows_bf16_inputs(rb, cb, device=dev)
+    for name, x, dt, rows, cols, group, bits in (("f32_int4_g128", w, fq.F32, r, c, 128, 4),
+                                                 ("f32_int8_g32", w, fq.F32, r, c, 32, 8),
+                                                 ("bf16_int8_g128", a, fq.BF16, rb, cb, 128, 8)):
+        ng = (cols + group - 1) // group
+        nb = rows * cols if bits == 8 else rows * ((cols + 1) // 2)
+        codes = torch.empty(nb, dtype=torch.uint8, device=dev)
+        fqo = torch.empty(rows * cols, dtype=torch.float32, device=dev)
+        scale = torch.empty(rows * ng, dtype=torch.float32, device=dev)
+        zp = torch.empty(rows * ng, dtype=torch.int32, device=dev)
+        flags = torch.zeros(1, dtype=torch.int32, device=dev)
+        esz = 4 if dt == fq.F32 else 2
+        ops.append(Op(f"groups.{name}", "k_groups",
+                      lambda x=x, dt=dt, rows=rows, cols=cols, group=group, bits=bits, codes=codes, fqo=fqo,
+                      scale=scale, zp=zp, flags=flags: fq.fq_quant_groups(
+                          x, dt, rows, cols, group, bits, fq.SYM, codes, fqo, scale, zp, flags),
+                      esz * rows * cols + nb + 4 * rows * cols + 8 * rows * ng))
+    return ops
+
+
 NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols,
-                  "percentile": ops_next_percentile}
+                  "percentile": ops_next_percentile, "group_wise": ops_next_groups}
 
 
 def build_next_ops(fq, syn, torch, dev="cuda"):

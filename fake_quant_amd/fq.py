@@ -71,6 +71,7 @@ _SIGS = {
     "fq_fp8_quantize_sr": (_INT, [_P, _I64, _INT, _P, _U64, _U64, _P, _P, _P]),
     "fq_cols_workspace_bytes": (_SZ, [_I64, _I64]),
     "fq_quant_cols": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _SZ, _P, _P, _P, _P, _P, _P]),
+    "fq_quant_groups": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P]),
     "fq_percentile_workspace_bytes": (_SZ, [_I64]),
     "fq_tensor_params_percentile": (_INT, [_P, _I64, _INT, _INT, ctypes.c_double, _P, _SZ, _P, _P, _P]),
     "fq_qat_step_int": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _U64, _U64, _P, _SZ, _P, _P, _P,
@@ -366,6 +367,21 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def fq_quant_groups(x, dtype, rows, cols, group, bits, scheme, codes, fq, scale, zero_point, flags=None,
+                    stream=None):
+    nm = "fq_quant_groups"
+    esz = 4 if dtype == F32 else 2
+    ng = (cols + group - 1) // group if group > 0 else 0
+    _need(nm, "x", x, esz * rows * cols)
+    _need(nm, "codes", codes, rows * (cols if bits == 8 else (cols + 1) // 2))
+    _need(nm, "fq", fq, 4 * rows * cols)
+    _need(nm, "scale", scale, 4 * rows * ng)
+    _need(nm, "zero_point", zero_point, 4 * rows * ng)
+    _need(nm, "flags", flags, 4)
+    _check(nm, _lib.fq_quant_groups(_ptr(x), dtype, rows, cols, group, bits, scheme, _ptr(codes), _ptr(fq),
+                                    _ptr(scale), _ptr(zero_point), _ptr(flags), _stream(stream)))
+
+
 def fq_percentile_workspace_bytes(n) -> int:
     return int(_lib.fq_percentile_workspace_bytes(n))
 
@@ -569,6 +585,23 @@ def qat_step_fp8(master, grad, m, v, t, cfg, fmt=E4M3, rounding=ROUND_NEAREST, s
     view = _empty(n, torch.float32, master)
     fq_qat_step_fp8(master, grad, m, v, n, cfg, t, fmt, rounding, seed, offset, q, view)
     return dict(q=q, view=view)
+
+
+def quant_groups(x, group, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+    """Group-wise calibration + quantize of a 2-D fp32 / bf16 tensor along its rows."""
+    rows, cols = x.shape
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    ng = (cols + group - 1) // group
+    codes = None
+    if want_codes:
+        codes = (_empty((rows, cols), torch.int8, x) if bits == 8
+                 else _empty((rows, (cols + 1) // 2), torch.uint8, x))
+    fq = _empty((rows, cols), torch.float32, x) if want_fq else None
+    scale = _empty((rows, ng), torch.float32, x)
+    zp = _empty((rows, ng), torch.int32, x)
+    flags = _zeros_flags(x)
+    fq_quant_groups(x, dtype, rows, cols, group, bits, scheme, codes, fq, scale, zp, flags)
+    return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
 
 
 def quant_cols(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):

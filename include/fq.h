@@ -223,6 +223,24 @@ int fq_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits
                   size_t workspace_bytes, void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags,
                   hipStream_t stream);
 
+/* ---- group-wise calibration ---------------------------------------------- */
+
+/* [CS] demo 3 "granularity": groups of `group` consecutive elements along each
+ * row of the row-major x [rows, cols] (FQ_F32 or FQ_BF16), each calibrated and
+ * quantized as a [QAT] channel is (finite min / max, from_minmax, RNE; as
+ * fq_quant_rows does per row).  When group does not divide cols, the last group
+ * of each row holds the cols mod group elements left.  group >= 1 (group >= cols
+ * is per-row quantization).
+ * codes (may be NULL): int8 [rows, cols] or, for 4 bits, packed nibbles
+ * ceil(cols/2) bytes per row (even column in the high nibble); fq (may be NULL):
+ * float32 [rows, cols]; scale, zero_point: [rows, ceil(cols / group)], group g of
+ * row r at r * ceil(cols / group) + g.  One launch when group divides cols (four
+ * elements per lane, a group of 4..256 elements = 1..64 lanes reduced in
+ * registers; other dividing sizes run as the rows of the [rows * cols / group,
+ * group] reshape); otherwise one thread per group. */
+int fq_quant_groups(const void* x, int dtype, int64_t rows, int64_t cols, int64_t group, int bits, int scheme,
+                    void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags, hipStream_t stream);
+
 /* ---- percentile calibration ---------------------------------------------- */
 
 /* Workspace bytes fq_tensor_params_percentile needs for n elements (0 for

@@ -42,7 +42,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 24
+    assert len(decl) == 25
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -149,6 +149,14 @@ def test_argument_checks(fq):
     assert L.fq_quant_cols(P, 0, 0, 4, 8, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_INVALID
     assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 16, P, P, P, P, None, None) == fq.E_INVALID
     assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 1 << 20, P, P, None, P, None, None) == fq.E_INVALID
+    # group-wise calibration
+    assert L.fq_quant_groups(P, 2, 4, 64, 32, 8, 0, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_groups(P, 0, 4, 64, 32, 5, 0, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_groups(P, 0, 4, 64, 32, 8, 3, P, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_quant_groups(P, 0, 4, 64, 0, 8, 0, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_groups(P, 0, 0, 64, 32, 8, 0, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_groups(P, 0, 4, 64, 32, 8, 0, P, P, None, P, None, None) == fq.E_INVALID
+    assert L.fq_quant_groups(P + 2, 0, 4, 64, 32, 8, 0, P, P, P, P, None, None) == fq.E_INVALID
     # percentile calibration: clip fraction in [0, 0.5), fixed workspace
     assert fq.fq_percentile_workspace_bytes(0) == 0
     wsp = fq.fq_percentile_workspace_bytes(8)
