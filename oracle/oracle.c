@@ -35,7 +35,7 @@
 #define ORC_FLAG_DEGENERATE 2u /* a calibration group had no usable range (zero) */
 
 enum { ORC_SYM = 0, ORC_AFFINE = 1 };
-enum { ORC_E4M3 = 0, ORC_E5M2 = 1 };
+enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_E2M1 = 2, ORC_E2M3 = 3, ORC_E3M2 = 4 };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 
 /* ------------------------------------------------------------------------- */
@@ -699,6 +699,131 @@ void orc_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_
                 q[r * cols + c] = byte;
                 if (fq) fq[r * cols + c] = orc_fp8_decode(byte, ORC_E4M3) * X;
             }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Narrow element formats in block-scaled tensors: [CS] demo 4 block_scaled,   */
+/* "e8m0" (MXFP4 / MXFP6) and "e4m3" with a tensor scale (NVFP4)               */
+/* ------------------------------------------------------------------------- */
+
+/* READING (the element tables sit in a module the pages do not show): the FP4
+ * and FP6 elements follow the same minifloat rule as the page's fp8 formats --
+ * sign, E exponent bits with bias 2^(E-1) - 1, M mantissa bits, exponent field
+ * 0 subnormal -- and every code is a finite number (no Inf or NaN codes), so the
+ * largest magnitude is (2 - 2^-M) 2^(2^E - 1 - bias).  This gives E2M1 max 6
+ * and emax 2, which the page states (scaled block maxima in [4, 8), values
+ * beyond 6 clipped); E2M3 max 7.5, emax 2; E3M2 max 28, emax 4. */
+static void narrow_format(int elem, int* ebits, int* mbits, int* bias, int* emax, float* maxv) {
+    switch (elem) {
+        case ORC_E2M1: *ebits = 2; *mbits = 1; break;
+        case ORC_E2M3: *ebits = 2; *mbits = 3; break;
+        default: *ebits = 3; *mbits = 2; break; /* ORC_E3M2 */
+    }
+    *bias = (1 << (*ebits - 1)) - 1;
+    *emax = (1 << *ebits) - 1 - *bias;
+    *maxv = ldexpf(2.0f - ldexpf(1.0f, -*mbits), *emax);
+}
+
+/* Element cast with saturation (elem.round(y, saturate=True)): the page's
+ * magnitude rule (step 2^(max(e, emin) - M), ties to even, saturate at max),
+ * sign kept (-0 included), +-Inf -> +-max.
+ * READING: these formats cannot hold NaN; a NaN element encodes to +0, as NaN
+ * does in the integer formats. */
+uint8_t orc_narrow_encode(float y, int elem) {
+    int ebits, mbits, bias, emax;
+    float maxv;
+    narrow_format(elem, &ebits, &mbits, &bias, &emax, &maxv);
+    if (isnan(y)) return 0;
+    uint8_t sign = signbit(y) ? (uint8_t)(1u << (ebits + mbits)) : 0;
+    float a = fabsf(y);
+    float m = isinf(a) ? maxv : fp8_round_magnitude(a, mbits, bias, maxv);
+    return fp8_bits(m, sign, mbits, bias);
+}
+
+float orc_narrow_decode(uint8_t code, int elem) {
+    int ebits, mbits, bias, emax;
+    float maxv;
+    narrow_format(elem, &ebits, &mbits, &bias, &emax, &maxv);
+    uint32_t E = (code >> mbits) & ((1u << ebits) - 1u);
+    uint32_t M = code & ((1u << mbits) - 1u);
+    float v = E == 0 ? ldexpf((float)M, 1 - bias - mbits) : ldexpf(1.0f + (float)M / (float)(1 << mbits), (int)E - bias);
+    return (code >> (ebits + mbits)) & 1u ? -v : v;
+}
+
+/* [CS] block_scaled(x, elem, 32, "e8m0") along rows, as orc_mxfp8_rows with the
+ * element's emax: X = 2^(k - 1 - emax), k from frexp of the block's finite amax
+ * (amax 0 taken as 1), exponent clamped below at -127, E8M0 byte = exponent +
+ * 127; q = elem(x / X), fq = decode(q) * X.
+ * Layouts: q for E2M1 is packed two codes per byte, ceil(cols/2) bytes per row,
+ * the even column in the high nibble (the nibble order of the 4-bit integer
+ * codes); for E2M3 / E3M2 one code per byte [rows, cols] (low six bits); e8m0:
+ * [rows, ceil(cols/32)]; fq (NULL allowed): float32 [rows, cols]. */
+void orc_mx_rows(const void* x, int dtype, int64_t rows, int64_t cols, int elem, uint8_t* q, uint8_t* e8m0,
+                 float* fq) {
+    int ebits, mbits, bias, emax;
+    float maxv;
+    narrow_format(elem, &ebits, &mbits, &bias, &emax, &maxv);
+    int64_t nbr = (cols + MX_BLOCK - 1) / MX_BLOCK;
+    int64_t pstride = (cols + 1) / 2;
+    if (elem == ORC_E2M1) memset(q, 0, (size_t)(rows * pstride));
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nbr; ++b) {
+            int64_t c0 = b * MX_BLOCK;
+            int64_t c1 = c0 + MX_BLOCK < cols ? c0 + MX_BLOCK : cols;
+            float amax = 0.0f;
+            for (int64_t c = c0; c < c1; ++c) {
+                float a = fabsf(widen(x, dtype, r * cols + c));
+                if (isfinite(a) && a > amax) amax = a;
+            }
+            int k;
+            frexpf(amax > 0.0f ? amax : 1.0f, &k);
+            int xe = k - 1 - emax;
+            if (xe < -127) xe = -127;
+            float X = ldexpf(1.0f, xe);
+            e8m0[r * nbr + b] = (uint8_t)(xe + 127);
+            for (int64_t c = c0; c < c1; ++c) {
+                uint8_t code = orc_narrow_encode(widen(x, dtype, r * cols + c) / X, elem);
+                if (elem == ORC_E2M1) q[r * pstride + c / 2] |= (c % 2 == 0) ? (uint8_t)(code << 4) : code;
+                else q[r * cols + c] = code;
+                if (fq) fq[r * cols + c] = orc_narrow_decode(code, elem) * X;
+            }
+        }
+    }
+}
+
+/* [CS] block_scaled(x, FP4_E2M1, 16, "e4m3") over the flattened tensor (the
+ * page's nvfp4_quantize): tensor scale g = amax(x) / (6 * 448); block scale
+ * s = E4M3(amax_block / 6 / g) with saturation, X = s * g, and X = 1 where that
+ * is not > 0; elements y = x / X cast to E2M1, fq = decode * X.
+ * READINGS: binary32 throughout, one rounding per operation, in the page's
+ * order; amax over finite elements; a partial last block when n % 16 != 0.
+ * q: packed E2M1 codes, ceil(n/2) bytes (even element in the high nibble);
+ * sbytes: the E4M3 byte of s per block, ceil(n/16); *g: the tensor scale. */
+#define NV_BLOCK 16
+void orc_nvfp4(const float* x, int64_t n, uint8_t* q, uint8_t* sbytes, float* g_out, float* fq) {
+    float g = orc_amax_finite(x, n) / (6.0f * 448.0f);
+    *g_out = g;
+    memset(q, 0, (size_t)((n + 1) / 2));
+    int64_t nb = (n + NV_BLOCK - 1) / NV_BLOCK;
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t i0 = b * NV_BLOCK, i1 = i0 + NV_BLOCK < n ? i0 + NV_BLOCK : n;
+        float amax = 0.0f;
+        for (int64_t i = i0; i < i1; ++i) {
+            float a = fabsf(x[i]);
+            if (isfinite(a) && a > amax) amax = a;
+        }
+        float ratio = amax / 6.0f / g;
+        uint8_t sb = orc_fp8_encode(ratio, ORC_E4M3);
+        float s = orc_fp8_decode(sb, ORC_E4M3);
+        float X = s * g;
+        if (!(X > 0.0f)) X = 1.0f;
+        sbytes[b] = sb;
+        for (int64_t i = i0; i < i1; ++i) {
+            uint8_t code = orc_narrow_encode(x[i] / X, ORC_E2M1);
+            q[i / 2] |= (i % 2 == 0) ? (uint8_t)(code << 4) : code;
+            if (fq) fq[i] = orc_narrow_decode(code, ORC_E2M1) * X;
         }
     }
 }

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 FLAG_NONFINITE = 1
 FLAG_DEGENERATE = 2
 SYM, AFFINE = 0, 1
-E4M3, E5M2 = 0, 1
+E4M3, E5M2, E2M1, E2M3, E3M2 = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 
 # Strict binary32: no FMA contraction, no fast-math, no re-association.
@@ -61,6 +61,10 @@ _SIGS = {
     "orc_percentile_params": (_U32, [_P, _I64, _INT, _INT, ctypes.c_double, _P, _P, _P, _P, _P, _P]),
     "orc_quant_cols": (_U32, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
     "orc_quant_groups": (_U32, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "orc_narrow_encode": (ctypes.c_uint8, [ctypes.c_float, _INT]),
+    "orc_narrow_decode": (ctypes.c_float, [ctypes.c_uint8, _INT]),
+    "orc_mx_rows": (None, [_P, _INT, _I64, _I64, _INT, _P, _P, _P]),
+    "orc_nvfp4": (None, [_P, _I64, _P, _P, _P, _P]),
     "orc_fp8_encode": (_U8, [_F, _INT]),
     "orc_fp8_decode": (_F, [_U8, _INT]),
     "orc_fp8_encode_n": (None, [_P, _I64, _INT, _P]),
@@ -261,6 +265,40 @@ def quant_groups(x, group: int, bits: int, scheme: int, dtype: int = F32, want_f
     flags = lib().orc_quant_groups(_ptr(x), dtype, rows, cols, group, bits, scheme, _ptr(codes), _ptr(fq),
                                    _ptr(scale), _ptr(zp))
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
+
+
+def narrow_encode(y, elem: int) -> int:
+    return int(lib().orc_narrow_encode(float(np.float32(y)), elem))
+
+
+def narrow_decode(code: int, elem: int) -> np.float32:
+    return np.float32(lib().orc_narrow_decode(code, elem))
+
+
+def mx_rows(x, elem: int, dtype: int = F32, want_fq: bool = True):
+    """Block-scaled E2M1 / E2M3 / E3M2 (E8M0 scale per 32 elements along rows)."""
+    if dtype == BF16:
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+    else:
+        x = _f32(x)
+    rows, cols = x.shape
+    q = np.empty((rows, (cols + 1) // 2) if elem == E2M1 else (rows, cols), np.uint8)
+    e8m0 = np.empty((rows, (cols + 31) // 32), np.uint8)
+    fq = np.empty((rows, cols), np.float32) if want_fq else None
+    lib().orc_mx_rows(_ptr(x), dtype, rows, cols, elem, _ptr(q), _ptr(e8m0), _ptr(fq))
+    return dict(q=q, e8m0=e8m0, fq=fq)
+
+
+def nvfp4(x, want_fq: bool = True):
+    """E2M1 elements, E4M3 scale per 16 elements, fp32 tensor scale (flattened x)."""
+    x = _f32(x).ravel()
+    n = x.size
+    q = np.empty((n + 1) // 2, np.uint8)
+    sb = np.empty((n + 15) // 16, np.uint8)
+    g = _F()
+    fq = np.empty(n, np.float32) if want_fq else None
+    lib().orc_nvfp4(_ptr(x), n, _ptr(q), _ptr(sb), ctypes.byref(g), _ptr(fq))
+    return dict(q=q, sbytes=sb, g=np.float32(g.value), fq=fq)
 
 
 def fp8_encode_n(y, fmt: int):
