@@ -330,8 +330,38 @@ def ops_next_groups(fq, syn, torch, dev):
     return ops
 
 
+def ops_next_block_formats(fq, syn, torch, dev):
+    """FP4 / FP6 block formats ([CS] demo 4): MXFP4 (E2M1) and MXFP6 (E2M3) with
+    E8M0 scales per 32 on the [16384, 8192] bf16 activations, and NVFP4 (E2M1,
+    E4M3 scales per 16, fp32 tensor scale) on the 2^26 fp8-workload tensor (its
+    tensor amax pass counted as one more read)."""
+    ops = []
+    rb, cb = syn.FULL["rows_bf16"]["rows"], syn.FULL["rows_bf16"]["cols"]
+    a = syn.rows_bf16_inputs(rb, cb, device=dev)
+    fqo = torch.empty(rb * cb, dtype=torch.float32, device=dev)
+    e8 = torch.empty(rb * ((cb + 31) // 32), dtype=torch.uint8, device=dev)
+    for name, elem, qb in (("mxfp4_e2m1", fq.E2M1, rb * ((cb + 1) // 2)), ("mxfp6_e2m3", fq.E2M3, rb * cb)):
+        q = torch.empty(qb, dtype=torch.uint8, device=dev)
+        ops.append(Op(f"block.{name}", "k_mxn_vec",
+                      lambda elem=elem, q=q: fq.fq_mx_rows(a, fq.BF16, rb, cb, elem, q, e8, fqo),
+                      2 * rb * cb + qb + rb * ((cb + 31) // 32) + 4 * rb * cb))
+    n = syn.FULL["fp8"]["n"]
+    x = syn.fp8_inputs(n, device=dev)
+    wsb = fq.fq_workspace_bytes(n)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    q4 = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
+    sb = torch.empty((n + 15) // 16, dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    fqn = torch.empty(n, dtype=torch.float32, device=dev)
+    ops.append(Op("block.nvfp4", "k_reduce_partial+k_amax_final+k_nvfp4_vec",
+                  lambda: fq.fq_nvfp4(x, n, ws, wsb, q4, sb, g, fqn),
+                  4 * n + 4 * n + (n + 1) // 2 + (n + 15) // 16 + 4 * n))
+    return ops
+
+
 NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols,
-                  "percentile": ops_next_percentile, "group_wise": ops_next_groups}
+                  "percentile": ops_next_percentile, "group_wise": ops_next_groups,
+                  "block_formats": ops_next_block_formats}
 
 
 def build_next_ops(fq, syn, torch, dev="cuda"):

@@ -95,4 +95,8 @@ inline unsigned reduce_blocks(int64_t n) {
 int params_from_partials(const void* workspace, unsigned nparts, int bits, int scheme, fq_int_params* params,
                          uint32_t* flags, hipStream_t stream);
 
+// Finite amax of x[n] (float32; 0 when no element is finite), left as binary32
+// bits in word 0 of the workspace (fq_workspace_bytes(n) bytes) by two launches.
+int tensor_amax(const float* x, int64_t n, void* workspace, hipStream_t stream);
+
 }  // namespace fqh

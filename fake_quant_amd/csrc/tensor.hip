@@ -221,6 +221,28 @@ __global__ __launch_bounds__(kFT) void k_fp8_scale_final(const uint32_t* __restr
     if (flags && zero) atomicOr(flags, FQ_FLAG_DEGENERATE);
 }
 
+// Pass 2 that keeps the finite amax itself: its bits go to word 0 of the
+// workspace (every partial has been read by then; this block is their only
+// reader).
+__global__ __launch_bounds__(kFT) void k_amax_final(uint32_t* __restrict__ part, int nparts) {
+    uint32_t p[kFinalLoads];
+#pragma unroll
+    for (int u = 0; u < kFinalLoads; ++u) {
+        const int i = threadIdx.x + u * kFT;
+        p[u] = i < nparts ? part[i] : 0u;
+    }
+    uint32_t a = 0;
+#pragma unroll
+    for (int u = 0; u < kFinalLoads; ++u) a = max(a, p[u]);
+    __shared__ uint32_t lds[kFW];
+    a = wave_max_u(a);
+    if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = a;
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    for (int i = 1; i < kFW; ++i) a = max(a, lds[i]);
+    part[0] = a;
+}
+
 // ---------------------------------------------------------------------------
 // Integer quantize / fake-quant with one parameter set ([QAT] fake_quant_int)
 // ---------------------------------------------------------------------------
@@ -418,6 +440,12 @@ int params_from_partials(const void* workspace, unsigned nparts, int bits, int s
                          uint32_t* flags, hipStream_t stream) {
     k_params_int_final<<<1, kFT, 0, stream>>>((const float4*)workspace, (int)nparts, bits,
                                               scheme == FQ_AFFINE ? 1 : 0, params, flags);
+    return launched();
+}
+
+int tensor_amax(const float* x, int64_t n, void* workspace, hipStream_t stream) {
+    const unsigned G = launch_partial<kAmax>(x, n, workspace, stream);
+    k_amax_final<<<1, kFT, 0, stream>>>((uint32_t*)workspace, (int)G);
     return launched();
 }
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG, "libfq.so")
 OK, E_INVALID, E_UNSUPPORTED, E_DIM, E_HIP = 0, -1, -2, -3, -4
 FLAG_NONFINITE, FLAG_DEGENERATE = 1, 2
 SYM, AFFINE = 0, 1
-E4M3, E5M2 = 0, 1
+E4M3, E5M2, E2M1, E2M3, E3M2 = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
 
@@ -73,6 +73,8 @@ _SIGS = {
     "fq_quant_cols": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "fq_quant_groups": (_INT, [_P, _INT, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P]),
     "fq_percentile_workspace_bytes": (_SZ, [_I64]),
+    "fq_mx_rows": (_INT, [_P, _INT, _I64, _I64, _INT, _P, _P, _P, _P]),
+    "fq_nvfp4": (_INT, [_P, _I64, _P, _SZ, _P, _P, _P, _P, _P]),
     "fq_tensor_params_percentile": (_INT, [_P, _I64, _INT, _INT, ctypes.c_double, _P, _SZ, _P, _P, _P]),
     "fq_qat_step_int": (_INT, [_P, _P, _P, _P, _I64, _P, _I64, _INT, _INT, _INT, _U64, _U64, _P, _SZ, _P, _P, _P,
                                _P, _P]),
@@ -382,6 +384,27 @@ def fq_quant_groups(x, dtype, rows, cols, group, bits, scheme, codes, fq, scale,
                                     _ptr(scale), _ptr(zero_point), _ptr(flags), _stream(stream)))
 
 
+def fq_mx_rows(x, dtype, rows, cols, elem, q, e8m0, fq=None, stream=None):
+    nm = "fq_mx_rows"
+    _need(nm, "x", x, rows * cols * (2 if dtype == BF16 else 4))
+    _need(nm, "q", q, rows * ((cols + 1) // 2 if elem == E2M1 else cols))
+    _need(nm, "e8m0", e8m0, rows * ((cols + 31) // 32))
+    _need(nm, "fq", fq, 4 * rows * cols)
+    _check(nm, _lib.fq_mx_rows(_ptr(x), dtype, rows, cols, elem, _ptr(q), _ptr(e8m0), _ptr(fq), _stream(stream)))
+
+
+def fq_nvfp4(x, n, workspace, workspace_bytes, q, scales, tensor_scale, fq=None, stream=None):
+    nm = "fq_nvfp4"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "q", q, (n + 1) // 2)
+    _need(nm, "scales", scales, (n + 15) // 16)
+    _need(nm, "tensor_scale", tensor_scale, 4)
+    _need(nm, "fq", fq, 4 * n)
+    _check(nm, _lib.fq_nvfp4(_ptr(x), n, _ptr(workspace), workspace_bytes, _ptr(q), _ptr(scales), _ptr(tensor_scale),
+                             _ptr(fq), _stream(stream)))
+
+
 def fq_percentile_workspace_bytes(n) -> int:
     return int(_lib.fq_percentile_workspace_bytes(n))
 
@@ -585,6 +608,30 @@ def qat_step_fp8(master, grad, m, v, t, cfg, fmt=E4M3, rounding=ROUND_NEAREST, s
     view = _empty(n, torch.float32, master)
     fq_qat_step_fp8(master, grad, m, v, n, cfg, t, fmt, rounding, seed, offset, q, view)
     return dict(q=q, view=view)
+
+
+def mx_rows(x, elem, want_fq=True):
+    """MXFP4 / MXFP6 (or MXFP8 with E4M3) blocks of 32 along the rows of a 2-D tensor."""
+    rows, cols = x.shape
+    dtype = BF16 if x.dtype == torch.bfloat16 else F32
+    q = _empty((rows, (cols + 1) // 2) if elem == E2M1 else (rows, cols), torch.uint8, x)
+    e8 = _empty((rows, (cols + 31) // 32), torch.uint8, x)
+    fq = _empty((rows, cols), torch.float32, x) if want_fq else None
+    fq_mx_rows(x, dtype, rows, cols, elem, q, e8, fq)
+    return dict(q=q, e8m0=e8, fq=fq)
+
+
+def nvfp4(x, want_fq=True):
+    """NVFP4 of a float32 tensor (flattened): E2M1 codes, E4M3 block scales, tensor scale."""
+    n = x.numel()
+    wsb = fq_workspace_bytes(n)
+    ws = _empty(max(wsb // 4, 4), torch.float32, x)
+    q = _empty((n + 1) // 2, torch.uint8, x)
+    sb = _empty((n + 15) // 16, torch.uint8, x)
+    g = _empty(1, torch.float32, x)
+    fq = _empty(n, torch.float32, x) if want_fq else None
+    fq_nvfp4(x, n, ws, ws.numel() * 4, q, sb, g, fq)
+    return dict(q=q, scales=sb, g=g, fq=fq)
 
 
 def quant_groups(x, group, bits=8, scheme=SYM, want_codes=True, want_fq=True):

@@ -66,8 +66,9 @@ extern "C" {
 /* [QAT] QuantScheme: symmetric (zero-point 0, restricted range -127..127 / -7..7)
  * or affine (full range -128..127 / -8..7, zero-point nudged so 0 is exact). */
 enum { FQ_SYM = 0, FQ_AFFINE = 1 };
-/* [QAT] Fp8Format */
-enum { FQ_E4M3 = 0, FQ_E5M2 = 1 };
+/* [QAT] Fp8Format, and the FP4 / FP6 element formats of [CS] demo 4 (every code
+ * finite: E2M1 max 6, E2M3 max 7.5, E3M2 max 28) */
+enum { FQ_E4M3 = 0, FQ_E5M2 = 1, FQ_E2M1 = 2, FQ_E2M3 = 3, FQ_E3M2 = 4 };
 /* element type of an input tensor */
 enum { FQ_F32 = 0, FQ_BF16 = 1 };
 
@@ -202,6 +203,34 @@ int fq_q4dq_dequantize(const uint8_t* packed, const uint8_t* qscale, const float
  * [rows, ceil(cols/32)]; fq (may be NULL): float32 [rows, cols]. */
 int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8m0,
                   float* fq, hipStream_t stream);
+
+/* ---- FP4 / FP6 block formats -------------------------------------------- */
+
+/* [CS] demo 4 block_scaled(x, elem, 32, "e8m0") along rows (MXFP4 / MXFP6):
+ * per block of 32 elements of a row (a short block at the row end), X = 2^(k - 1
+ * - emax) with k the frexp exponent of the block's finite amax (amax 0 taken as
+ * 1, exponent clamped below at -127); codes = elem(x / X) with ties to even and
+ * saturation (NaN -> +0, +-Inf -> +-max); fq = decode * X.  elem: FQ_E2M1
+ * (emax 2), FQ_E2M3 (emax 2), FQ_E3M2 (emax 4), or FQ_E4M3 (as fq_mxfp8_rows).
+ * x: [rows, cols] FQ_F32 or FQ_BF16; q: E2M1 packed two codes per byte,
+ * ceil(cols/2) bytes per row, even column in the high nibble; E2M3 / E3M2 one
+ * code per byte [rows, cols] (sign in bit 5); e8m0: u8 [rows, ceil(cols/32)]
+ * (exponent + 127); fq (may be NULL): float32 [rows, cols].  One launch. */
+int fq_mx_rows(const void* x, int dtype, int64_t rows, int64_t cols, int elem, uint8_t* q, uint8_t* e8m0,
+               float* fq, hipStream_t stream);
+
+/* [CS] demo 4 block_scaled(x, FP4_E2M1, 16, "e4m3") (NVFP4) over the flattened
+ * float32 x[n]: tensor scale g = amax(x) / (6 * 448) over the finite elements;
+ * per block of 16 (the last one short when n % 16 != 0), s = E4M3(amax_block /
+ * 6 / g) with saturation, X = s * g, or 1 where X is not > 0; codes =
+ * E2M1(x / X), fq = decode * X; binary32 throughout, in the page's order.
+ * q: packed E2M1 codes, ceil(n/2) bytes, even element in the high nibble;
+ * scales: the E4M3 byte of s per block, ceil(n/16) bytes; tensor_scale: one
+ * device float (g); fq (may be NULL): float32 [n].  workspace: device memory of
+ * fq_workspace_bytes(n), 16-byte aligned, contents not kept.  Three or four
+ * launches (the tensor amax in two, then the blocks). */
+int fq_nvfp4(const float* x, int64_t n, void* workspace, size_t workspace_bytes, uint8_t* q, uint8_t* scales,
+             float* tensor_scale, float* fq, hipStream_t stream);
 
 /* ---- per-column calibration --------------------------------------------- */
 

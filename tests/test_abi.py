@@ -42,7 +42,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 25
+    assert len(decl) == 27
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -70,6 +70,11 @@ def test_constants_match_header(fq):
                       ("FQ_E_DIM", fq.E_DIM), ("FQ_E_HIP", fq.E_HIP),
                       ("FQ_FLAG_NONFINITE", fq.FLAG_NONFINITE), ("FQ_FLAG_DEGENERATE", fq.FLAG_DEGENERATE)]:
         assert header_define(name) == val, name
+    text = open(HEADER).read()
+    for name, val in [("FQ_E4M3", fq.E4M3), ("FQ_E5M2", fq.E5M2), ("FQ_E2M1", fq.E2M1), ("FQ_E2M3", fq.E2M3),
+                      ("FQ_E3M2", fq.E3M2), ("FQ_F32", fq.F32), ("FQ_BF16", fq.BF16), ("FQ_SYM", fq.SYM),
+                      ("FQ_AFFINE", fq.AFFINE)]:
+        assert int(re.search(rf"\b{name} = (\d+)", text).group(1)) == val, name
     for st in (0, -1, -2, -3, -4):
         assert fq.lib().fq_status_string(st) != b"unknown status"
     assert fq.lib().fq_status_string(7) == b"unknown status"
@@ -149,6 +154,19 @@ def test_argument_checks(fq):
     assert L.fq_quant_cols(P, 0, 0, 4, 8, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_INVALID
     assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 16, P, P, P, P, None, None) == fq.E_INVALID
     assert L.fq_quant_cols(P, 0, 4, 4, 8, 0, P, 1 << 20, P, P, None, P, None, None) == fq.E_INVALID
+    # FP4 / FP6 block formats
+    assert L.fq_mx_rows(P, 2, 4, 64, fq.E2M1, P, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_mx_rows(P, 0, 4, 64, 5, P, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_mx_rows(P, 0, 4, 64, fq.E5M2, P, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_mx_rows(P, 0, 0, 64, fq.E2M1, P, P, P, None) == fq.E_INVALID
+    assert L.fq_mx_rows(P, 0, 4, 64, fq.E3M2, None, P, P, None) == fq.E_INVALID
+    assert L.fq_mx_rows(P + 2, 0, 4, 64, fq.E2M3, P, P, P, None) == fq.E_INVALID
+    ws16 = fq.fq_workspace_bytes(16)
+    assert L.fq_nvfp4(P, 0, P, 1 << 20, P, P, P, P, None) == fq.E_INVALID
+    assert L.fq_nvfp4(P, 16, P, 0, P, P, P, P, None) == fq.E_INVALID
+    assert L.fq_nvfp4(P, 16, None, ws16, P, P, P, P, None) == fq.E_INVALID
+    assert L.fq_nvfp4(P, 16, P, ws16, P, P, None, P, None) == fq.E_INVALID
+    assert L.fq_nvfp4(P + 2, 16, P, ws16, P, P, P, P, None) == fq.E_INVALID
     # group-wise calibration
     assert L.fq_quant_groups(P, 2, 4, 64, 32, 8, 0, P, P, P, P, None, None) == fq.E_UNSUPPORTED
     assert L.fq_quant_groups(P, 0, 4, 64, 32, 5, 0, P, P, P, P, None, None) == fq.E_UNSUPPORTED
