@@ -38,6 +38,13 @@ class FqError(RuntimeError):
         self.status = status
 
 
+class FqFlagError(FqError):
+    """A data-dependent condition that a call with check=True found in its device
+    flag word (status = the flag bits): the pages' InvalidState for a calibration
+    group holding a non-finite value (FLAG_NONFINITE) or no usable range
+    (FLAG_DEGENERATE).  The results are written all the same."""
+
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m fake_quant_amd.build` "
                       "(there is no non-HIP fallback)")
@@ -424,7 +431,16 @@ def _zeros_flags(like):
     return torch.zeros(1, dtype=torch.int32, device=like.device)
 
 
-def params_int(x, bits=8, scheme=SYM):
+def raise_on_flags(name: str, flags):
+    """Synchronise on the flag word and raise FqFlagError if any bit is set."""
+    f = int(flags.item())
+    if f:
+        what = [m for bit, m in ((FLAG_NONFINITE, "a calibration group held Inf or NaN"),
+                                 (FLAG_DEGENERATE, "a calibration group had no usable range")) if f & bit]
+        raise FqFlagError(name, f, "; ".join(what) or "unknown flag")
+
+
+def params_int(x, bits=8, scheme=SYM, check=False):
     """Per-tensor calibration -> (params int32[4] view of fq_int_params, flags)."""
     n = x.numel()
     wsb = fq_workspace_bytes(n)
@@ -432,10 +448,12 @@ def params_int(x, bits=8, scheme=SYM):
     params = _empty(4, torch.int32, x)
     flags = _zeros_flags(x)
     fq_tensor_params_int(x, n, bits, scheme, ws, wsb, params, flags)
+    if check:
+        raise_on_flags("params_int", flags)
     return params, flags
 
 
-def params_percentile(x, clip_fraction, bits=8, scheme=SYM):
+def params_percentile(x, clip_fraction, bits=8, scheme=SYM, check=False):
     """Per-tensor calibration on the clipped tails -> (params int32[4], flags)."""
     n = x.numel()
     wsb = fq_percentile_workspace_bytes(n)
@@ -443,6 +461,8 @@ def params_percentile(x, clip_fraction, bits=8, scheme=SYM):
     params = _empty(4, torch.int32, x)
     flags = _zeros_flags(x)
     fq_tensor_params_percentile(x, n, bits, scheme, clip_fraction, ws, wsb, params, flags)
+    if check:
+        raise_on_flags("params_percentile", flags)
     return params, flags
 
 
@@ -481,7 +501,7 @@ def ste_backward(grad, x, bounds):
     return out
 
 
-def quant_rows(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+def quant_rows(x, bits=8, scheme=SYM, want_codes=True, want_fq=True, check=False):
     rows, cols = x.shape
     dtype = BF16 if x.dtype == torch.bfloat16 else F32
     if want_codes:
@@ -493,6 +513,8 @@ def quant_rows(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):
     zp = _empty(rows, torch.int32, x)
     flags = _zeros_flags(x)
     fq_quant_rows(x, dtype, rows, cols, bits, scheme, codes, fq, scale, zp, flags)
+    if check:
+        raise_on_flags("quant_rows", flags)
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
 
 
@@ -502,13 +524,15 @@ def dequantize_rows(codes, rows, cols, scale, zp, bits=8):
     return out
 
 
-def fp8_tensor_scale(x):
+def fp8_tensor_scale(x, check=False):
     n = x.numel()
     wsb = fq_workspace_bytes(n)
     ws = _empty(max(wsb // 4, 1), torch.float32, x)
     s = _empty(2, torch.float32, x)
     flags = _zeros_flags(x)
     fq_fp8_tensor_scale(x, n, ws, wsb, s[0:1], s[1:2], flags)
+    if check:
+        raise_on_flags("fp8_tensor_scale", flags)
     return s, flags
 
 
@@ -534,7 +558,7 @@ def fp8_dequantize(q, fmt, scale):
     return out
 
 
-def q4dq_quantize(x, want_block_scale=True, want_recon=True):
+def q4dq_quantize(x, want_block_scale=True, want_recon=True, check=False):
     n = x.numel()
     npk, nb, ns = fq_q4dq_sizes(n)
     packed = _empty(npk, torch.uint8, x)
@@ -544,6 +568,8 @@ def q4dq_quantize(x, want_block_scale=True, want_recon=True):
     recon = _empty(n, torch.float32, x) if want_recon else None
     flags = _zeros_flags(x)
     fq_q4dq_quantize(x, n, packed, qscale, sup, bs, recon, flags)
+    if check:
+        raise_on_flags("q4dq_quantize", flags)
     return dict(packed=packed, qscale=qscale, super=sup, block_scale=bs, recon=recon, flags=flags)
 
 
@@ -584,7 +610,7 @@ def adamw_config(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
 
 
 def qat_step_int(master, grad, m, v, t, cfg, bits=8, scheme=SYM, rounding=ROUND_NEAREST, seed=0, offset=0,
-                 want_codes=True):
+                 want_codes=True, check=False):
     """One QAT step with an integer target; master / m / v are updated in place.
     Returns dict(params, codes, view, flags)."""
     n = master.numel()
@@ -597,6 +623,8 @@ def qat_step_int(master, grad, m, v, t, cfg, bits=8, scheme=SYM, rounding=ROUND_
     view = _empty(n, torch.float32, master)
     fq_qat_step_int(master, grad, m, v, n, cfg, t, bits, scheme, rounding, seed, offset, ws, wsb, params, codes,
                     view, flags)
+    if check:
+        raise_on_flags("qat_step_int", flags)
     return dict(params=params, codes=codes, view=view, flags=flags)
 
 
@@ -634,7 +662,7 @@ def nvfp4(x, want_fq=True):
     return dict(q=q, scales=sb, g=g, fq=fq)
 
 
-def quant_groups(x, group, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+def quant_groups(x, group, bits=8, scheme=SYM, want_codes=True, want_fq=True, check=False):
     """Group-wise calibration + quantize of a 2-D fp32 / bf16 tensor along its rows."""
     rows, cols = x.shape
     dtype = BF16 if x.dtype == torch.bfloat16 else F32
@@ -648,10 +676,12 @@ def quant_groups(x, group, bits=8, scheme=SYM, want_codes=True, want_fq=True):
     zp = _empty((rows, ng), torch.int32, x)
     flags = _zeros_flags(x)
     fq_quant_groups(x, dtype, rows, cols, group, bits, scheme, codes, fq, scale, zp, flags)
+    if check:
+        raise_on_flags("quant_groups", flags)
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
 
 
-def quant_cols(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):
+def quant_cols(x, bits=8, scheme=SYM, want_codes=True, want_fq=True, check=False):
     """Per-column calibration + quantize of a 2-D fp32 / bf16 tensor."""
     rows, cols = x.shape
     dtype = BF16 if x.dtype == torch.bfloat16 else F32
@@ -666,4 +696,6 @@ def quant_cols(x, bits=8, scheme=SYM, want_codes=True, want_fq=True):
     zp = _empty(cols, torch.int32, x)
     flags = _zeros_flags(x)
     fq_quant_cols(x, dtype, rows, cols, bits, scheme, ws, wsb, codes, fq, scale, zp, flags)
+    if check:
+        raise_on_flags("quant_cols", flags)
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)

@@ -100,3 +100,16 @@ def test_binding_guards_reject_bad_buffers():
     with pytest.raises(fq.FqError, match="not contiguous"):
         fq_need("f", "out", Fake(16, contig=False), 64)
     fq_need("f", "out", Fake(16), 64)
+
+
+def test_raise_on_flags_maps_bits_to_errors():
+    # the flag word read on the host: no bit -> no error; each bit -> FqFlagError
+    fq.raise_on_flags("op", torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(fq.FqFlagError, match="Inf or NaN") as e:
+        fq.raise_on_flags("op", torch.tensor([fq.FLAG_NONFINITE], dtype=torch.int32))
+    assert e.value.status == fq.FLAG_NONFINITE
+    with pytest.raises(fq.FqFlagError, match="no usable range"):
+        fq.raise_on_flags("op", torch.tensor([fq.FLAG_DEGENERATE], dtype=torch.int32))
+    with pytest.raises(fq.FqFlagError, match="Inf or NaN; .*no usable range"):
+        fq.raise_on_flags("op", torch.tensor([3], dtype=torch.int32))
+    assert issubclass(fq.FqFlagError, fq.FqError)
