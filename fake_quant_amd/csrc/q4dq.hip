@@ -45,7 +45,7 @@ constexpr int kQ4Threads = FQ_Q4_THREADS;            // threads per super-block 
 #define FQ_OCC_Q4DQ 1
 #endif
 #ifndef FQ_Q4_NSB
-#define FQ_Q4_NSB 2
+#define FQ_Q4_NSB 4
 #endif
 constexpr int kQuantNsb = FQ_Q4_NSB;  // super-blocks per workgroup of the quantize kernel
 #ifndef FQ_Q4DQ_NSB

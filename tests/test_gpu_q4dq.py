@@ -65,7 +65,7 @@ def test_full_size_workload_sampled(fqlib, orc):
     del x, r, deq
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 63, 64, 65, 127, 4099, 16383, 16384, 16385, 3 * SB + 100, 5 * SB + 1])
+@pytest.mark.parametrize("n", [1, 2, 3, 63, 64, 65, 127, 4099, 16383, 16384, 16385, 3 * SB + 100, 5 * SB + 1, 8 * SB, 11 * SB + 5])
 def test_ragged_sizes(fqlib, orc, n):
     x = synthetic.q4dq_inputs(n=n, device="cuda", seed=n)
     check_q4(fqlib, orc, x, what=f"ragged {n}")
