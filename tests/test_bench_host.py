@@ -50,6 +50,10 @@ def test_every_bench_op_passes_buffers_that_fit(monkeypatch):
     monkeypatch.setattr(fq, "_stream", lambda stream=None: None)
     ops = bench.build_ops(fq, synthetic, torch, None, dev="cpu")
     assert len(ops) == 16
+    # built largest first, timed in WORKLOADS order
+    assert sorted(bench.BUILD_ORDER) == sorted(bench.WORKLOADS)
+    groups = [op.name.split(".")[0] for op in ops]
+    assert [g for i, g in enumerate(groups) if i == 0 or groups[i - 1] != g] == list(bench.WORKLOADS)
     for op in ops:
         op.fn()
     assert len(recorder.calls) == 16
