@@ -124,6 +124,113 @@ __global__ __launch_bounds__(kB) void k_groups(const void* __restrict__ x, int64
                  make_float4(o[0] * cal.scale, o[1] * cal.scale, o[2] * cal.scale, o[3] * cal.scale));
 }
 
+// Wide path: sixteen consecutive elements per lane, so the per-group work
+// (reduction, calibration, reciprocal) is shared by four times as many elements.
+// A lane's sixteen fake-quant values are contiguous in memory; they leave through
+// a per-wave LDS transpose so that every store instruction writes one contiguous
+// run across the wave.
+constexpr int kW = 16;
+constexpr int kWPad = kW + 4;  // LDS floats per lane (keeps 16-byte alignment)
+
+template <int DT>
+__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, float (&e)[kW]) {
+    if constexpr (DT == FQ_F32) {
+        const float4* p = reinterpret_cast<const float4*>(x) + 4 * v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 q = p[j];
+            e[4 * j] = q.x;
+            e[4 * j + 1] = q.y;
+            e[4 * j + 2] = q.z;
+            e[4 * j + 3] = q.w;
+        }
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * v;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 q = p[j];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                e[8 * j + 2 * k] = bf16_lo(w[k]);
+                e[8 * j + 2 * k + 1] = bf16_hi(w[k]);
+            }
+        }
+    }
+}
+
+template <int DT, int BITS, int L>
+__global__ __launch_bounds__(kB) void k_groups_wide(const void* __restrict__ x, int64_t nvec, int affine,
+                                                    uint8_t* __restrict__ codes, float* __restrict__ fq,
+                                                    float* __restrict__ scale, int32_t* __restrict__ zp,
+                                                    uint32_t* __restrict__ flags) {
+    __shared__ float4 s_out[kB / kWave][kWave * kWPad / 4];
+    const int64_t v = (int64_t)blockIdx.x * kB + threadIdx.x;
+    const bool in = v < nvec;
+    float e[kW];
+    MinMax m;
+    if (in) {
+        load16<DT>(x, v, e);
+#pragma unroll
+        for (int i = 0; i < kW; ++i) m.add(e[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kW; ++i) e[i] = 0.0f;
+    }
+    group_reduce<L>(m);
+    const IntRange rg = int_range(BITS, affine != 0);
+    const IntCal cal = calibrate(m.mn, m.mx, rg, affine != 0);
+    const bool first = in && (v % L) == 0;
+    if (first) {
+        scale[v / L] = cal.scale;
+        zp[v / L] = cal.zp;
+    }
+    const uint32_t f = first ? ((m.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u))
+                             : 0u;
+    const uint32_t fw = (__ballot(f & FQ_FLAG_NONFINITE) ? FQ_FLAG_NONFINITE : 0u) |
+                        (__ballot(f & FQ_FLAG_DEGENERATE) ? FQ_FLAG_DEGENERATE : 0u);
+    if (flags && fw && (threadIdx.x % kWave) == 0) atomicOr(flags, fw);
+    const IntQ q(cal.scale, cal.zp, rg);
+    float o[kW];
+    int code[kW];
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+        o[i] = q.offset(e[i]);
+        code[i] = (int)o[i] + cal.zp;
+    }
+    if (in && codes) {
+        if (BITS == 8) {
+            reinterpret_cast<uint4*>(codes)[v] =
+                make_uint4(pack4(code[0], code[1], code[2], code[3]), pack4(code[4], code[5], code[6], code[7]),
+                           pack4(code[8], code[9], code[10], code[11]), pack4(code[12], code[13], code[14], code[15]));
+        } else {
+            uint32_t w[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                w[h] = nib2(code[8 * h], code[8 * h + 1]) | (nib2(code[8 * h + 2], code[8 * h + 3]) << 8) |
+                       (nib2(code[8 * h + 4], code[8 * h + 5]) << 16) | (nib2(code[8 * h + 6], code[8 * h + 7]) << 24);
+            reinterpret_cast<uint2*>(codes)[v] = make_uint2(w[0], w[1]);
+        }
+    }
+    if (fq) {  // uniform: every thread of the block reaches the barrier
+        const int lane = threadIdx.x % kWave;
+        float4* sw = s_out[threadIdx.x / kWave];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sw[lane * (kWPad / 4) + j] = make_float4(o[4 * j] * cal.scale, o[4 * j + 1] * cal.scale,
+                                                     o[4 * j + 2] * cal.scale, o[4 * j + 3] * cal.scale);
+        __syncthreads();
+        // float4 number idx of the wave's 256 belongs to lane idx / 4, part idx % 4
+        const int64_t wbase = (v - lane) * 4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int idx = k * kWave + lane;
+            const float4 val = sw[(idx / 4) * (kWPad / 4) + (idx % 4)];
+            if (wbase + idx < nvec * 4) store_nt(reinterpret_cast<float4*>(fq) + wbase + idx, val);
+        }
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ float elem(const void* __restrict__ x, int64_t i) {
     if constexpr (DT == FQ_F32) return reinterpret_cast<const float*>(x)[i];
@@ -212,12 +319,41 @@ bool try_fast(const void* x, int64_t nvec, int64_t lanes, int affine, uint8_t* c
     }
 }
 
+template <int DT, int BITS, int L>
+void launch_wide(const void* x, int64_t nvec, int affine, uint8_t* codes, float* fq, float* scale, int32_t* zp,
+                 uint32_t* flags, hipStream_t st) {
+    const unsigned G = (unsigned)((nvec + kB - 1) / kB);
+    k_groups_wide<DT, BITS, L><<<G, kB, 0, st>>>(x, nvec, affine, codes, fq, scale, zp, flags);
+}
+
+template <int DT, int BITS>
+bool try_wide(const void* x, int64_t nvec, int64_t lanes, int affine, uint8_t* codes, float* fq, float* scale,
+              int32_t* zp, uint32_t* flags, hipStream_t st) {
+    switch (lanes) {
+        case 1: launch_wide<DT, BITS, 1>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        case 2: launch_wide<DT, BITS, 2>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        case 4: launch_wide<DT, BITS, 4>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        case 8: launch_wide<DT, BITS, 8>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        case 16: launch_wide<DT, BITS, 16>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        case 32: launch_wide<DT, BITS, 32>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        case 64: launch_wide<DT, BITS, 64>(x, nvec, affine, codes, fq, scale, zp, flags, st); return true;
+        default: return false;
+    }
+}
+
 template <int DT, int BITS>
 int launch_groups(const void* x, int64_t rows, int64_t cols, int64_t group, int scheme, uint8_t* codes, float* fq,
                   float* scale, int32_t* zp, uint32_t* flags, hipStream_t st) {
     constexpr int N = kN;
     const int affine = scheme == FQ_AFFINE ? 1 : 0;
     if (cols % group == 0) {
+        const bool al_wide = fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, BITS == 8 ? 16 : 8);
+        if (group % kW == 0 && al_wide) {
+            const int64_t nvec = rows * (cols / kW);
+            if (nvec / 0x7FFFFFFFLL < kB && try_wide<DT, BITS>(x, nvec, group / kW, affine, codes, fq, scale, zp,
+                                                                 flags, st))
+                return fqh::launched();
+        }
         const bool al = fqh::aligned(x, DT == FQ_F32 ? 16 : 8) && fqh::aligned(fq, 16) &&
                         fqh::aligned(codes, BITS == 8 ? 4 : 2);
         if (group % N == 0 && al) {

@@ -112,3 +112,26 @@ def test_group_at_least_cols_is_per_row(fqlib, orc):
         torch.cuda.synchronize()
         assert_bits(to_np(r["codes"]), to_np(rr["codes"]), f"group {group} codes")
         assert_bits(to_np(r["scale"]).reshape(-1), to_np(rr["scale"]), f"group {group} scale")
+
+
+@pytest.mark.parametrize("group,bits", [(16, 8), (32, 8), (128, 8), (64, 4), (256, 4)])
+def test_four_element_path(fqlib, orc, group, bits):
+    # codes 4-byte (int8) / 2-byte (int4) but not 16 / 8-byte aligned: the groups run
+    # four elements per lane instead of sixteen
+    rng = np.random.default_rng(group + bits)
+    rows, cols = 24, 512
+    x = torch.from_numpy((rng.standard_normal((rows, cols)) * 2).astype(np.float32)).cuda()
+    nb = rows * cols if bits == 8 else rows * cols // 2
+    off = 4 if bits == 8 else 2
+    codes = torch.empty(nb + off, dtype=torch.uint8, device="cuda")[off:]
+    fqo = torch.empty(rows * cols, dtype=torch.float32, device="cuda")
+    ng = cols // group
+    scale = torch.empty(rows * ng, dtype=torch.float32, device="cuda")
+    zp = torch.empty(rows * ng, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fqlib.fq_quant_groups(x, fqlib.F32, rows, cols, group, bits, 1, codes, fqo, scale, zp, flags)
+    torch.cuda.synchronize()
+    ref = orc.quant_groups(to_np(x), group, bits, 1)
+    assert_bits(to_np(codes), ref["codes"].reshape(-1), "codes")
+    assert_bits(to_np(scale), ref["scale"].reshape(-1), "scale")
+    assert_f32(to_np(fqo), ref["fq"].reshape(-1), "fq")
