@@ -263,10 +263,11 @@ int fq_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits
  * codes (may be NULL): int8 [rows, cols] or, for 4 bits, packed nibbles
  * ceil(cols/2) bytes per row (even column in the high nibble); fq (may be NULL):
  * float32 [rows, cols]; scale, zero_point: [rows, ceil(cols / group)], group g of
- * row r at r * ceil(cols / group) + g.  One launch when group divides cols (four
- * elements per lane, a group of 4..256 elements = 1..64 lanes reduced in
- * registers; other dividing sizes run as the rows of the [rows * cols / group,
- * group] reshape); otherwise one thread per group. */
+ * row r at r * ceil(cols / group) + g.  One launch when group divides cols:
+ * groups of 16..1024 elements run sixteen elements per lane, a group being 1..64
+ * lanes reduced in registers (groups of 4 and 8, and buffers not 16-byte aligned,
+ * four elements per lane); other dividing sizes run as the rows of the
+ * [rows * cols / group, group] reshape; otherwise one thread per group. */
 int fq_quant_groups(const void* x, int dtype, int64_t rows, int64_t cols, int64_t group, int bits, int scheme,
                     void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags, hipStream_t stream);
 
