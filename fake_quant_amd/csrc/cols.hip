@@ -30,7 +30,8 @@ constexpr int kB = fqh::kBlock;
 constexpr int kWaves = kB / kWave;   // waves per block
 constexpr int64_t kMaxBands = 64;    // bands of the min / max pass (partials per column)
 constexpr int kQuantRows = 32;       // rows per band of the quantize pass
-constexpr int kU = 8;                // row loads in flight per thread
+constexpr int kU = 8;                // row loads in flight per thread (quantize pass)
+constexpr int kUm = 8;  // row loads in flight per thread (min / max pass); 4 and 16 time the same
 constexpr int64_t kMaxQuantBands = 65535;  // grid y limit; blocks loop over further bands
 
 int64_t minmax_bands(int64_t rows) { return rows < kMaxBands ? rows : kMaxBands; }
@@ -89,16 +90,16 @@ __global__ __launch_bounds__(kB) void k_cols_minmax(const void* __restrict__ x, 
     const int64_t r1 = r0 + rows_per_band < rows ? r0 + rows_per_band : rows;
     MinMax m[N];
     if (c0 < cols) {
-        for (int64_t r = r0 + w; r < r1; r += kWaves * kU) {
-            float v[kU][N];
+        for (int64_t r = r0 + w; r < r1; r += kWaves * kUm) {
+            float v[kUm][N];
             // rows past the band repeat the band's last row: min / max unchanged
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
+            for (int u = 0; u < kUm; ++u) {
                 const int64_t rr = r + u * kWaves;
                 load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);
             }
 #pragma unroll
-            for (int u = 0; u < kU; ++u)
+            for (int u = 0; u < kUm; ++u)
 #pragma unroll
                 for (int e = 0; e < N; ++e) m[e].add(v[u][e]);
         }
@@ -150,10 +151,15 @@ __global__ __launch_bounds__(kB) void k_cols_fold(const float4* __restrict__ par
     rec[c] = make_float4(m.mn, m.mx, as_f(m.nf), 0.0f);
 }
 
+// column record: (scale, reciprocal, zero-point bits, mode | kColFinite), mode
+// 0 zero scale, 1 divisor in the exact-quotient window, 2 true division;
+// kColFinite: the column holds no Inf or NaN
+constexpr uint32_t kColFinite = 4u;
+
 // code offset q - zp of x for one column's record (the per-element rule of
 // IntQ::offset: zero scale -> code 0, NaN -> code 0, +-Inf clamp, -0 -> +0)
 __device__ __forceinline__ float col_offset(float x, const float4& cp, float lo, float hi) {
-    const uint32_t mode = as_u(cp.w);
+    const uint32_t mode = as_u(cp.w) & 3u;
     const float zpf = (float)(-(int32_t)as_u(cp.z));
     if (mode == 0u) return zpf;
     const float t = mode == 1u ? ExactDiv(cp.x, cp.y).quick(x) : x / cp.x;  // +-Inf / NaN safe
@@ -215,20 +221,38 @@ __global__ __launch_bounds__(kB) void k_cols_quant(const void* __restrict__ x, i
                                                    uint32_t* __restrict__ flags) {
     constexpr int N = ColVec<DT>::N;
     constexpr int TC = kWave * N;  // columns of the tile
+    static_assert(kQuantRows == kWaves * kU, "one batch of row loads per wave covers a band");
     __shared__ float4 s_par[TC];
     const int64_t ct0 = (int64_t)blockIdx.x * TC;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t c0 = ct0 + (int64_t)lane * N;
+    const bool in = c0 < cols;
+    // the first band's rows are loaded before the column parameters are derived
+    // (they do not depend on them), so the loads overlap that work
+    int64_t band = blockIdx.y;
+    int64_t r0 = band * kQuantRows;
+    int64_t r1 = r0 + kQuantRows < rows ? r0 + kQuantRows : rows;
+    float v[kU][N];
+    auto load_band = [&]() {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t rr = r0 + w + u * kWaves;
+            load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);  // past the band: its last row again
+        }
+    };
+    if (in) load_band();
     const IntRange rg = int_range(BITS, affine != 0);
-    // (scale, reciprocal, zero-point bits, quotient mode: 0 zero scale, 1 exact fast, 2 true division)
     for (int j = threadIdx.x; j < TC; j += kB) {
         const int64_t c = ct0 + j;
         if (c >= cols) {
-            s_par[j] = make_float4(0.0f, 1.0f, 0.0f, 0.0f);
+            s_par[j] = make_float4(1.0f, 1.0f, 0.0f, as_f(1u | kColFinite));  // unused; keeps the fast test true
             continue;
         }
         const float4 k = rec[c];
         const IntCal cal = calibrate(k.x, k.y, rg, affine != 0);
         const ExactDiv d(cal.scale == 0.0f ? 1.0f : cal.scale);
-        const uint32_t mode = cal.scale == 0.0f ? 0u : (d.fast ? 1u : 2u);
+        const uint32_t mode = (cal.scale == 0.0f ? 0u : (d.fast ? 1u : 2u)) |
+                              (as_u(k.z) < 0x7F800000u ? kColFinite : 0u);
         s_par[j] = make_float4(cal.scale, d.y, as_f((uint32_t)cal.zp), as_f(mode));
         if (blockIdx.y == 0) {
             scale[c] = cal.scale;
@@ -239,45 +263,54 @@ __global__ __launch_bounds__(kB) void k_cols_quant(const void* __restrict__ x, i
         }
     }
     __syncthreads();
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    const int64_t c0 = ct0 + (int64_t)lane * N;
-    if (c0 >= cols) return;
+    if (!in) return;
     float4 cp[N];
     float lo[N], hi[N];
     int zpv[N];
+    bool lane_fast = true;
 #pragma unroll
     for (int e = 0; e < N; ++e) {
         cp[e] = s_par[lane * N + e];
         zpv[e] = (int)as_u(cp[e].z);
         lo[e] = (float)(rg.qmin - zpv[e]);
         hi[e] = (float)(rg.qmax - zpv[e]);
+        lane_fast = lane_fast && as_u(cp[e].w) == (1u | kColFinite);
     }
+    // every column of the wave finite with a divisor in the exact-quotient
+    // window: the bare quotient, a clamp, and the round-to-even of the magic-number
+    // add, whose low bits plus the zero-point are the code (the rule of col_offset
+    // for finite x, without its NaN / Inf fix-ups)
+    const bool fast = __all(lane_fast);
     const int64_t pstride = BITS == 8 ? cols : (cols + 1) / 2;
-    for (int64_t band = blockIdx.y; band * kQuantRows < rows; band += gridDim.y) {
-        const int64_t r0 = band * kQuantRows;
-        const int64_t r1 = r0 + kQuantRows < rows ? r0 + kQuantRows : rows;
-        for (int64_t rb = r0 + w; rb < r1; rb += kWaves * kU) {
-            float v[kU][N];
+    for (;;) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int64_t rr = rb + u * kWaves;
-                load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);
-            }
+        for (int u = 0; u < kU; ++u) {
+            const int64_t r = r0 + w + u * kWaves;
+            if (r >= r1) break;
+            int code[N];
+            float o[N];
+            if (fast) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int64_t r = rb + u * kWaves;
-                if (r >= r1) break;
-                int code[N];
-                float o[N];
+                for (int e = 0; e < N; ++e) {
+                    const float f = __builtin_amdgcn_fmed3f(quick_div(v[u][e], cp[e].x, cp[e].y), lo[e], hi[e]) + kMagic;
+                    code[e] = (int)(as_u(f) + (uint32_t)zpv[e]);
+                    o[e] = (f - kMagic) * cp[e].x;
+                }
+            } else {
 #pragma unroll
                 for (int e = 0; e < N; ++e) {
                     o[e] = col_offset(v[u][e], cp[e], lo[e], hi[e]);
                     code[e] = (int)o[e] + zpv[e];
                     o[e] *= cp[e].x;
                 }
-                store_row<N, BITS, AL>(code, o, r, cols, c0, pstride, codes, fq);
             }
+            store_row<N, BITS, AL>(code, o, r, cols, c0, pstride, codes, fq);
         }
+        band += gridDim.y;
+        if (band * kQuantRows >= rows) break;
+        r0 = band * kQuantRows;
+        r1 = r0 + kQuantRows < rows ? r0 + kQuantRows : rows;
+        load_band();
     }
 }
 

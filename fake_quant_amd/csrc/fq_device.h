@@ -237,11 +237,12 @@ struct MinMax {
     float mn = __builtin_inff();
     float mx = -__builtin_inff();
     uint32_t nf = 0;
+    // a non-finite v becomes a quiet NaN, which fminf / fmaxf pass over
     __device__ __forceinline__ void add(float v) {
-        uint32_t a = as_u(v) & 0x7FFFFFFFu;
-        bool fin = a < 0x7F800000u;
-        mn = fin ? fminf(mn, v) : mn;
-        mx = fin ? fmaxf(mx, v) : mx;
+        const uint32_t a = as_u(v) & 0x7FFFFFFFu;
+        const float vf = a < 0x7F800000u ? v : __builtin_nanf("");
+        mn = fminf(mn, vf);
+        mx = fmaxf(mx, vf);
         nf = max(nf, a);
     }
     __device__ __forceinline__ void merge(float omn, float omx, uint32_t onf) {
