@@ -53,10 +53,13 @@ __device__ __forceinline__ void fp8_quant_loop(const float* __restrict__ x, int6
             w = fp8_encode4_hw<FMT>(y0, y1, y2, y3);
         }
         if (q) reinterpret_cast<uint32_t*>(q)[cc] = w;
-        if (fq)
+        if (fq) {
+            // the codes above are never Inf codes; their NaN code decodes to NaN
+            float d[4];
+            fp8_decode4_hw<FMT>(w, d);
             store_nt(reinterpret_cast<float4*>(fq) + cc,
-                make_float4(fp8_value<FMT>(w & 0xFFu, scale), fp8_value<FMT>((w >> 8) & 0xFFu, scale),
-                            fp8_value<FMT>((w >> 16) & 0xFFu, scale), fp8_value<FMT>(w >> 24, scale)));
+                     make_float4(d[0] * scale, d[1] * scale, d[2] * scale, d[3] * scale));
+        }
     };
     if (AL) {
         const float4* xv = reinterpret_cast<const float4*>(x);
@@ -128,10 +131,11 @@ __global__ __launch_bounds__(kB) void k_fp8_dequant_w(const uint32_t* __restrict
     for (int u = 0; u < U; ++u) w[u] = base + u * kWave < nfull ? qw[base + u * kWave] : 0u;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-        if (base + u * kWave < nfull)
-            store_nt(out + base + u * kWave,
-                     make_float4(fp8_decode<FMT>(w[u] & 0xFFu) * s, fp8_decode<FMT>((w[u] >> 8) & 0xFFu) * s,
-                                 fp8_decode<FMT>((w[u] >> 16) & 0xFFu) * s, fp8_decode<FMT>(w[u] >> 24) * s));
+        if (base + u * kWave < nfull) {
+            float d[4];
+            fp8_decode4_hw<FMT>(w[u], d);
+            store_nt(out + base + u * kWave, make_float4(d[0] * s, d[1] * s, d[2] * s, d[3] * s));
+        }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
         const int64_t i = 4 * nfull + threadIdx.x;
         reinterpret_cast<float*>(out)[i] = fp8_decode<FMT>(reinterpret_cast<const uint8_t*>(qw)[i]) * s;

@@ -440,6 +440,28 @@ __device__ __forceinline__ float fp8_decode(uint32_t b) {
     return v;
 }
 
+// The four codes of w (code e in byte e) decoded by gfx950's conversion unit
+// (v_cvt_pk_f32_fp8 / v_cvt_pk_f32_bf8, two codes per instruction, OCP formats):
+// exact, and for every one of the 256 codes of either format the value of
+// fp8_decode (E4M3 S.1111.111 and E5M2 S.11111.xx with xx != 0 -> NaN, E5M2
+// S.11111.00 -> +-Inf).
+template <int FMT>
+__device__ __forceinline__ void fp8_decode4_hw(uint32_t w, float (&d)[4]) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    v2f lo, hi;
+    if constexpr (FMT == 0) {
+        lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    } else {
+        lo = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+    }
+    d[0] = lo.x;
+    d[1] = lo.y;
+    d[2] = hi.x;
+    d[3] = hi.y;
+}
+
 // ---------------------------------------------------------------------------
 // Stochastic rounding ([QAT] module docs "Rounding modes", RoundingMode::
 // Stochastic): the uniform variate of element index i is word i mod 4 of

@@ -71,9 +71,6 @@ __global__ __launch_bounds__(kB) void k_mx_vec(const void* __restrict__ x, int64
                                          __builtin_amdgcn_ldexpf(xe[e + 1], -xe_exp),
                                          __builtin_amdgcn_ldexpf(xe[e + 2], -xe_exp),
                                          __builtin_amdgcn_ldexpf(xe[e + 3], -xe_exp));
-        uint32_t b[N];
-#pragma unroll
-        for (int e = 0; e < N; ++e) b[e] = (w[e / 4] >> (8 * (e % 4))) & 0xFFu;
         if (DT == FQ_F32) {
             reinterpret_cast<uint32_t*>(q)[gv] = w[0];
         } else {
@@ -81,12 +78,15 @@ __global__ __launch_bounds__(kB) void k_mx_vec(const void* __restrict__ x, int64
         }
         if ((gv % L) == 0) e8[gv / L] = (uint8_t)(xe_exp + 127);
         if (fq) {
+            // decode * X = ldexp(decode, xe); the NaN code decodes to NaN
             float4* fv = reinterpret_cast<float4*>(fq) + gv * (N / 4);
-            store_nt(fv, make_float4(mx_value(b[0], xe_exp), mx_value(b[1], xe_exp), mx_value(b[2], xe_exp),
-                                     mx_value(b[3], xe_exp)));
-            if (N == 8)
-                store_nt(fv + 1, make_float4(mx_value(b[4], xe_exp), mx_value(b[5], xe_exp),
-                                             mx_value(b[6], xe_exp), mx_value(b[7], xe_exp)));
+#pragma unroll
+            for (int h = 0; h < N / 4; ++h) {
+                float d[4];
+                fp8_decode4_hw<0>(w[h], d);
+                store_nt(fv + h, make_float4(__builtin_amdgcn_ldexpf(d[0], xe_exp), __builtin_amdgcn_ldexpf(d[1], xe_exp),
+                                             __builtin_amdgcn_ldexpf(d[2], xe_exp), __builtin_amdgcn_ldexpf(d[3], xe_exp)));
+            }
         }
     }
 }

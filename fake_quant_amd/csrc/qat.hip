@@ -172,8 +172,7 @@ __global__ __launch_bounds__(kB) void k_adamw_fp8(float* __restrict__ w, const f
             for (int e = 0; e < 4; ++e) b[e] = (wd >> (8 * e)) & 0xFFu;
         }
         float vw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vw[e] = b[e] == 0x7Fu ? __builtin_nanf("") : fp8_decode_finite<FMT>(b[e]);
+        fp8_decode4_hw<FMT>(pack4(b[0], b[1], b[2], b[3]), vw);  // never an Inf code; NaN decodes to NaN
         if (vec) {
             store_nt(reinterpret_cast<float4*>(w) + c, make_float4(we[0], we[1], we[2], we[3]));
             store_nt(reinterpret_cast<float4*>(m) + c, make_float4(me[0], me[1], me[2], me[3]));

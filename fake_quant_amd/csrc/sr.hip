@@ -141,11 +141,15 @@ __device__ __forceinline__ void fp8_sr_loop(const float* __restrict__ x, int64_t
             }
         }
         if (AL && cnt == 4) {
-            if (q) reinterpret_cast<uint32_t*>(q)[c] = pack4(b[0], b[1], b[2], b[3]);
-            if (fq)
+            const uint32_t w = pack4(b[0], b[1], b[2], b[3]);
+            if (q) reinterpret_cast<uint32_t*>(q)[c] = w;
+            if (fq) {
+                // the codes above are never Inf codes; their NaN code decodes to NaN
+                float d[4];
+                fp8_decode4_hw<FMT>(w, d);
                 store_nt(reinterpret_cast<float4*>(fq) + c,
-                         make_float4(fp8_value_sr<FMT>(b[0], scale), fp8_value_sr<FMT>(b[1], scale),
-                                     fp8_value_sr<FMT>(b[2], scale), fp8_value_sr<FMT>(b[3], scale)));
+                         make_float4(d[0] * scale, d[1] * scale, d[2] * scale, d[3] * scale));
+            }
         } else {
             for (int e = 0; e < cnt; ++e) {
                 if (q) q[4 * c + e] = (uint8_t)b[e];
