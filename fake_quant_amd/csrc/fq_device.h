@@ -230,6 +230,66 @@ __device__ __forceinline__ void store_nt(float4* p, float4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide layout: sixteen consecutive elements per lane, so that per-block work
+// (reductions, scales, reciprocals) is shared by four times as many elements as
+// with one 16-byte vector per lane.  A lane's sixteen outputs are contiguous in
+// memory; they leave through a per-wave LDS transpose so that every store
+// instruction writes one contiguous run across the wave.
+// ---------------------------------------------------------------------------
+constexpr int kWide = 16;
+constexpr int kWidePad = kWide + 4;  // LDS floats per lane of the staging buffer (16-byte rows)
+
+// elements 16 v .. 16 v + 15 of x (binary32, or bf16 widened exactly)
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, float (&e)[kWide]) {
+    if constexpr (!BF16) {
+        const float4* p = reinterpret_cast<const float4*>(x) + 4 * v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 q = p[j];
+            e[4 * j] = q.x;
+            e[4 * j + 1] = q.y;
+            e[4 * j + 2] = q.z;
+            e[4 * j + 3] = q.w;
+        }
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * v;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 q = p[j];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                e[8 * j + 2 * k] = bf16_lo(w[k]);
+                e[8 * j + 2 * k + 1] = bf16_hi(w[k]);
+            }
+        }
+    }
+}
+
+// Stores the lane's sixteen values o as elements 16 v .. 16 v + 15 of out
+// (nontemporal) through sw, this wave's LDS staging buffer of kWave * kWidePad
+// floats.  v must be blockIdx.x * blockDim.x + threadIdx.x.  Every thread of the
+// workgroup calls it (it holds a barrier); float4s from index 4 nvec on are not
+// stored.
+__device__ __forceinline__ void store16_staged(float4* __restrict__ out, int64_t v, int64_t nvec,
+                                               const float (&o)[kWide], float4* sw) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        sw[lane * (kWidePad / 4) + j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+    __syncthreads();
+    // float4 number idx of the wave's 256 belongs to lane idx / 4, part idx % 4
+    const int64_t wbase = (v - lane) * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int idx = k * kWave + lane;
+        const float4 val = sw[(idx / 4) * (kWidePad / 4) + (idx % 4)];
+        if (wbase + idx < nvec * 4) store_nt(out + wbase + idx, val);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Finite min / max / non-finite accumulation over binary32 values.
 // `nf` collects max(|x| bits): it reaches 0x7F800000 iff an Inf or NaN was seen.
 // ---------------------------------------------------------------------------

@@ -124,53 +124,23 @@ __global__ __launch_bounds__(kB) void k_groups(const void* __restrict__ x, int64
                  make_float4(o[0] * cal.scale, o[1] * cal.scale, o[2] * cal.scale, o[3] * cal.scale));
 }
 
-// Wide path: sixteen consecutive elements per lane, so the per-group work
-// (reduction, calibration, reciprocal) is shared by four times as many elements.
-// A lane's sixteen fake-quant values are contiguous in memory; they leave through
-// a per-wave LDS transpose so that every store instruction writes one contiguous
-// run across the wave.
-constexpr int kW = 16;
-constexpr int kWPad = kW + 4;  // LDS floats per lane (keeps 16-byte alignment)
-
-template <int DT>
-__device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, float (&e)[kW]) {
-    if constexpr (DT == FQ_F32) {
-        const float4* p = reinterpret_cast<const float4*>(x) + 4 * v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 q = p[j];
-            e[4 * j] = q.x;
-            e[4 * j + 1] = q.y;
-            e[4 * j + 2] = q.z;
-            e[4 * j + 3] = q.w;
-        }
-    } else {
-        const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * v;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint4 q = p[j];
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                e[8 * j + 2 * k] = bf16_lo(w[k]);
-                e[8 * j + 2 * k + 1] = bf16_hi(w[k]);
-            }
-        }
-    }
-}
+// Wide path: sixteen consecutive elements per lane (the wide layout), so the
+// per-group work (reduction, calibration, reciprocal) is shared by four times as
+// many elements.
+constexpr int kW = kWide;
 
 template <int DT, int BITS, int L>
 __global__ __launch_bounds__(kB) void k_groups_wide(const void* __restrict__ x, int64_t nvec, int affine,
                                                     uint8_t* __restrict__ codes, float* __restrict__ fq,
                                                     float* __restrict__ scale, int32_t* __restrict__ zp,
                                                     uint32_t* __restrict__ flags) {
-    __shared__ float4 s_out[kB / kWave][kWave * kWPad / 4];
+    __shared__ float4 s_out[kB / kWave][kWave * kWidePad / 4];
     const int64_t v = (int64_t)blockIdx.x * kB + threadIdx.x;
     const bool in = v < nvec;
     float e[kW];
     MinMax m;
     if (in) {
-        load16<DT>(x, v, e);
+        load16<DT == FQ_BF16>(x, v, e);
 #pragma unroll
         for (int i = 0; i < kW; ++i) m.add(e[i]);
     } else {
@@ -213,21 +183,9 @@ __global__ __launch_bounds__(kB) void k_groups_wide(const void* __restrict__ x, 
         }
     }
     if (fq) {  // uniform: every thread of the block reaches the barrier
-        const int lane = threadIdx.x % kWave;
-        float4* sw = s_out[threadIdx.x / kWave];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sw[lane * (kWPad / 4) + j] = make_float4(o[4 * j] * cal.scale, o[4 * j + 1] * cal.scale,
-                                                     o[4 * j + 2] * cal.scale, o[4 * j + 3] * cal.scale);
-        __syncthreads();
-        // float4 number idx of the wave's 256 belongs to lane idx / 4, part idx % 4
-        const int64_t wbase = (v - lane) * 4;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int idx = k * kWave + lane;
-            const float4 val = sw[(idx / 4) * (kWPad / 4) + (idx % 4)];
-            if (wbase + idx < nvec * 4) store_nt(reinterpret_cast<float4*>(fq) + wbase + idx, val);
-        }
+        for (int i = 0; i < kW; ++i) o[i] *= cal.scale;
+        store16_staged(reinterpret_cast<float4*>(fq), v, nvec, o, s_out[threadIdx.x / kWave]);
     }
 }
 

@@ -14,11 +14,14 @@
 // E2M3 (max 7.5, emax 2), E3M2 (max 28, emax 4).  Their tables are not on the
 // pages; a NaN element becomes +0 (they have no NaN code), +-Inf saturates.
 //
-// MX: four elements per lane (a 16-byte fp32 or 8-byte bf16 load; one 16-byte
-// fake-quant store), a block of 32 = 8 lanes reduced with DPP; the power-of-two
-// scaling is exact, so x / X is a multiplication by 2^-e.
-// NVFP4: four elements per lane, a block of 16 = a DPP quad; the tensor amax
-// comes from the shared two-pass reduction; x / X is a true quotient (ExactDiv).
+// Both run in the wide layout (sixteen consecutive elements per lane, outputs
+// through an LDS transpose), so the per-block work is shared by sixteen
+// elements: measured against four elements per lane, MXFP4 150 -> 136 us,
+// MXFP6 155 -> 143 us, NVFP4 150 -> 137 us on [16384, 8192] bf16 / 2^26 fp32.
+// MX: a block of 32 = a lane pair, reduced with one DPP exchange; the
+// power-of-two scaling is exact, so x / X is a multiplication by 2^-e.
+// NVFP4: a block of 16 = one lane; the tensor amax comes from the shared
+// two-pass reduction; x / X is a true quotient (ExactDiv).
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -85,58 +88,51 @@ __device__ __forceinline__ int mx_exp(uint32_t am) {
     return max(__builtin_amdgcn_frexp_expf(A) - 1 - F::kEmax, -127);
 }
 
-template <int DT>
-__device__ __forceinline__ void load4(const void* __restrict__ x, int64_t v, float (&e)[4]) {
-    if constexpr (DT == FQ_F32) {
-        const float4 q = reinterpret_cast<const float4*>(x)[v];
-        e[0] = q.x;
-        e[1] = q.y;
-        e[2] = q.z;
-        e[3] = q.w;
-    } else {
-        const uint2 q = reinterpret_cast<const uint2*>(x)[v];
-        e[0] = bf16_lo(q.x);
-        e[1] = bf16_hi(q.x);
-        e[2] = bf16_lo(q.y);
-        e[3] = bf16_hi(q.y);
-    }
-}
-
-// four codes of one lane: FP4 as two bytes (even element in the high nibble),
-// FP6 as four bytes
-template <class F>
-__device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t v, const uint32_t (&c)[4]) {
-    if constexpr (F::kMaxCode == 7u) {
-        reinterpret_cast<uint16_t*>(q)[v] = (uint16_t)((c[0] << 4) | c[1] | (c[2] << 12) | (c[3] << 8));
-    } else {
-        reinterpret_cast<uint32_t*>(q)[v] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    }
-}
-
-// MX along rows, cols a multiple of 32, aligned buffers: lane v holds elements
-// 4v .. 4v+3 of the flattened tensor; a block is 8 lanes.  Every lane of the
-// grid takes part in the reduction.
+// MX in the wide layout (cols a multiple of 32, aligned buffers): lane v holds
+// elements 16 v .. 16 v + 15, a block is a lane pair.  FP4 codes leave as 8
+// bytes per lane, FP6 as 16; the fake-quant values through the LDS transpose.
+// Every thread of the grid reaches the reduction and the barrier.
 template <int DT, class F>
-__global__ __launch_bounds__(kB) void k_mxn_vec(const void* __restrict__ x, int64_t nvec, uint8_t* __restrict__ q,
-                                                uint8_t* __restrict__ e8, float* __restrict__ fq) {
+__global__ __launch_bounds__(kB) void k_mxn_wide(const void* __restrict__ x, int64_t nvec, uint8_t* __restrict__ q,
+                                                 uint8_t* __restrict__ e8, float* __restrict__ fq) {
+    __shared__ float4 s_out[kB / kWave][kWave * kWidePad / 4];
     const int64_t v = (int64_t)blockIdx.x * kB + threadIdx.x;
     const bool in = v < nvec;
-    float e[4] = {0.f, 0.f, 0.f, 0.f};
-    if (in) load4<DT>(x, v, e);
-    uint32_t am = max(max(fin_abs(e[0]), fin_abs(e[1])), max(fin_abs(e[2]), fin_abs(e[3])));
-    am = quad_max_u(am);
-    am = max(am, dpp_u<kHalfMirror>(am));
-    if (!in) return;
+    float e[kWide];
+    if (in) {
+        load16<DT == FQ_BF16>(x, v, e);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWide; ++i) e[i] = 0.0f;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < kWide; ++i) am = max(am, fin_abs(e[i]));
+    am = max(am, dpp_u<kQuadXor1>(am));
     const int xe = mx_exp<F>(am);
     const float X = __builtin_amdgcn_ldexpf(1.0f, xe), inv = __builtin_amdgcn_ldexpf(1.0f, -xe);
-    uint32_t c[4];
+    uint32_t c[kWide];
+    float o[kWide];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = F::encode(e[i] * inv);
-    store_codes<F>(q, v, c);
-    if ((v % (kMxBlock / 4)) == 0) e8[v / (kMxBlock / 4)] = (uint8_t)(xe + 127);
-    if (fq)
-        store_nt(reinterpret_cast<float4*>(fq) + v, make_float4(F::decode(c[0]) * X, F::decode(c[1]) * X,
-                                                                F::decode(c[2]) * X, F::decode(c[3]) * X));
+    for (int i = 0; i < kWide; ++i) {
+        c[i] = F::encode(e[i] * inv);
+        o[i] = F::decode(c[i]) * X;
+    }
+    if (in) {
+        if constexpr (F::kMaxCode == 7u) {
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) w[k / 4] |= ((c[2 * k] << 4) | c[2 * k + 1]) << (8 * (k % 4));
+            reinterpret_cast<uint2*>(q)[v] = make_uint2(w[0], w[1]);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = c[4 * k] | (c[4 * k + 1] << 8) | (c[4 * k + 2] << 16) | (c[4 * k + 3] << 24);
+            reinterpret_cast<uint4*>(q)[v] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        if ((v & 1) == 0) e8[v >> 1] = (uint8_t)(xe + 127);
+    }
+    if (fq) store16_staged(reinterpret_cast<float4*>(fq), v, nvec, o, s_out[threadIdx.x / kWave]);
 }
 
 template <int DT>
@@ -181,12 +177,11 @@ __global__ __launch_bounds__(kB) void k_mxn_any(const void* __restrict__ x, int6
 
 template <int DT, class F>
 int launch_mx(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8, float* fq, hipStream_t st) {
-    constexpr bool fp4 = F::kMaxCode == 7u;
-    const bool al = cols % kMxBlock == 0 && fqh::aligned(x, DT == FQ_F32 ? 16 : 8) && fqh::aligned(fq, 16) &&
-                    fqh::aligned(q, fp4 ? 2 : 4);
-    const int64_t nvec = rows * (cols / 4);
-    if (al && nvec / kB < 0x7FFFFFFFLL) {
-        k_mxn_vec<DT, F><<<(unsigned)((nvec + kB - 1) / kB), kB, 0, st>>>(x, nvec, q, e8, fq);
+    constexpr bool fp4 = F::kMaxCode == 7u;  // eight code bytes per lane, else sixteen
+    const bool al = cols % kMxBlock == 0 && fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(q, fp4 ? 8 : 16);
+    const int64_t nw = rows * (cols / kWide);
+    if (al && nw / kB < 0x7FFFFFFFLL) {
+        k_mxn_wide<DT, F><<<(unsigned)((nw + kB - 1) / kB), kB, 0, st>>>(x, nw, q, e8, fq);
     } else {
         const int64_t blocks = rows * ((cols + kMxBlock - 1) / kMxBlock);
         k_mxn_any<DT, F><<<fqh::grid_for(blocks, kB, 8), kB, 0, st>>>(x, rows, cols, q, e8, fq);
@@ -216,32 +211,47 @@ __device__ __forceinline__ float nv_scale(float amax, float tmax, uint32_t* sb) 
     return X > 0.0f ? X : 1.0f;
 }
 
-// full blocks of 16, aligned buffers: lane v holds elements 4v .. 4v+3, a block
-// is a DPP quad; workgroup 0's first lane also stores the tensor scale
-__global__ __launch_bounds__(kB) void k_nvfp4_vec(const float* __restrict__ x, int64_t nvec,
-                                                  const uint32_t* __restrict__ tmax_bits, uint8_t* __restrict__ q,
-                                                  uint8_t* __restrict__ sbytes, float* __restrict__ g_out,
-                                                  float* __restrict__ fq) {
+// full blocks of 16 in the wide layout, aligned buffers: lane v holds block v,
+// whose scale it derives alone; codes leave as 8 bytes per lane, the fake-quant
+// values through the LDS transpose; the first lane also stores the tensor scale.
+// Every thread of the grid reaches the barrier.
+__global__ __launch_bounds__(kB) void k_nvfp4_wide(const float* __restrict__ x, int64_t nblk,
+                                                   const uint32_t* __restrict__ tmax_bits, uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ sbytes, float* __restrict__ g_out,
+                                                   float* __restrict__ fq) {
+    __shared__ float4 s_out[kB / kWave][kWave * kWidePad / 4];
     const int64_t v = (int64_t)blockIdx.x * kB + threadIdx.x;
-    const bool in = v < nvec;
-    float e[4] = {0.f, 0.f, 0.f, 0.f};
-    if (in) load4<FQ_F32>(x, v, e);
-    uint32_t am = max(max(fin_abs(e[0]), fin_abs(e[1])), max(fin_abs(e[2]), fin_abs(e[3])));
-    am = quad_max_u(am);
-    if (!in) return;
+    const bool in = v < nblk;
+    float e[kWide];
+    if (in) {
+        load16<false>(x, v, e);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWide; ++i) e[i] = 0.0f;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < kWide; ++i) am = max(am, fin_abs(e[i]));
     const float tmax = as_f(*tmax_bits);
     if (v == 0) *g_out = tmax / (6.0f * 448.0f);
     uint32_t sb;
     const float X = nv_scale(as_f(am), tmax, &sb);
     const ExactDiv d(X);
-    uint32_t c[4];
+    uint32_t c[kWide];
+    float o[kWide];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = E2M1::encode(d(e[i]));
-    store_codes<E2M1>(q, v, c);
-    if ((v % (kNvBlock / 4)) == 0) sbytes[v / (kNvBlock / 4)] = (uint8_t)sb;
-    if (fq)
-        store_nt(reinterpret_cast<float4*>(fq) + v, make_float4(E2M1::decode(c[0]) * X, E2M1::decode(c[1]) * X,
-                                                                E2M1::decode(c[2]) * X, E2M1::decode(c[3]) * X));
+    for (int i = 0; i < kWide; ++i) {
+        c[i] = E2M1::encode(d(e[i]));
+        o[i] = E2M1::decode(c[i]) * X;
+    }
+    if (in) {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k / 4] |= ((c[2 * k] << 4) | c[2 * k + 1]) << (8 * (k % 4));
+        reinterpret_cast<uint2*>(q)[v] = make_uint2(w[0], w[1]);
+        sbytes[v] = (uint8_t)sb;
+    }
+    if (fq) store16_staged(reinterpret_cast<float4*>(fq), v, nblk, o, s_out[threadIdx.x / kWave]);
 }
 
 // blocks [b0, nblocks) of the flat tensor, any alignment: one thread per block
@@ -299,10 +309,8 @@ int fq_nvfp4(const float* x, int64_t n, void* workspace, size_t workspace_bytes,
     const uint32_t* tmax = reinterpret_cast<const uint32_t*>(workspace);
     const int64_t nfull = n / kNvBlock;  // whole blocks
     int64_t b0 = 0;
-    if (nfull > 0 && fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(q, 2) &&
-        nfull * (kNvBlock / 4) / kB < 0x7FFFFFFFLL) {
-        const int64_t nvec = nfull * (kNvBlock / 4);
-        k_nvfp4_vec<<<(unsigned)((nvec + kB - 1) / kB), kB, 0, stream>>>(x, nvec, tmax, q, scales, tensor_scale, fq);
+    if (nfull > 0 && fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(q, 8) && nfull / kB < 0x7FFFFFFFLL) {
+        k_nvfp4_wide<<<(unsigned)((nfull + kB - 1) / kB), kB, 0, stream>>>(x, nfull, tmax, q, scales, tensor_scale, fq);
         b0 = nfull;
     }
     const int64_t nb = (n + kNvBlock - 1) / kNvBlock;

@@ -1,8 +1,9 @@
 """GPU parity of the FP4 / FP6 block formats ([CS] demo 4 block_scaled) against
 the oracle, bit for bit: MXFP4 (E2M1) and MXFP6 (E2M3, E3M2) with E8M0 scales
 per 32 elements along rows -- codes, scale bytes and fake-quant values -- on the
-[4096, 4096] fp32 and [4096, 8192] bf16 shapes, ragged and odd row lengths,
-unaligned views and special values; and NVFP4 (E2M1, E4M3 block scales of 16,
+[4096, 4096] fp32 and [4096, 8192] bf16 shapes, short rows of multiples of 32
+(the wide layout ending mid-wave), ragged and odd row lengths, unaligned views
+and special values; and NVFP4 (E2M1, E4M3 block scales of 16,
 fp32 tensor scale) on the 2^20 tensor, the 2^26 fp8 workload with its NaN / Inf /
 zero elements, short and ragged lengths, an unaligned view and the zero tensor.
 """
@@ -61,6 +62,17 @@ def test_mx_ragged_rows(fqlib, orc, cols, elem):
     x = (rng.standard_t(5, (23, cols)) * 0.02).astype(np.float32)
     check_mx(fqlib, orc, torch.from_numpy(x).cuda(), elem, f"cols {cols}")
     check_mx(fqlib, orc, torch.from_numpy(x).to(torch.bfloat16).cuda(), elem, f"bf16 cols {cols}")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 32), (23, 64), (7, 96), (5, 160), (33, 1056)])
+@pytest.mark.parametrize("elem", list(ELEMS.values()), ids=list(ELEMS))
+def test_mx_wide_layout_shapes(fqlib, orc, rows, cols, elem):
+    # rows a multiple of 32 wide: sixteen elements per lane, a lane pair per block;
+    # these sizes end mid-wave and mid-workgroup
+    rng = np.random.default_rng(rows * 1000 + cols + elem)
+    x = (rng.standard_t(5, (rows, cols)) * np.exp(rng.standard_normal((rows, 1)))).astype(np.float32)
+    check_mx(fqlib, orc, torch.from_numpy(x).cuda(), elem, f"wide {rows}x{cols}")
+    check_mx(fqlib, orc, torch.from_numpy(x).to(torch.bfloat16).cuda(), elem, f"wide bf16 {rows}x{cols}")
 
 
 @pytest.mark.parametrize("elem", list(ELEMS.values()), ids=list(ELEMS))
