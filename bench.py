@@ -186,7 +186,7 @@ def ops_rows_bf16(fq, syn, torch, dev):
         Op("rows_bf16.int8_affine", "k_quant_rows",
            lambda: fq.fq_quant_rows(a, fq.BF16, r, c, 8, fq.AFFINE, codes, None, sc, zp, fl),
            2 * r * c + r * c + 8 * r),
-        Op("rows_bf16.mxfp8_e4m3", "k_mx_vec",
+        Op("rows_bf16.mxfp8_e4m3", "k_mx_wide",
            lambda: fq.fq_mxfp8_rows(a, fq.BF16, r, c, q, e8, None), 2 * r * c + r * c + r * c // 32),
     ]
 
@@ -342,7 +342,7 @@ def ops_next_block_formats(fq, syn, torch, dev):
     e8 = torch.empty(rb * ((cb + 31) // 32), dtype=torch.uint8, device=dev)
     for name, elem, qb in (("mxfp4_e2m1", fq.E2M1, rb * ((cb + 1) // 2)), ("mxfp6_e2m3", fq.E2M3, rb * cb)):
         q = torch.empty(qb, dtype=torch.uint8, device=dev)
-        ops.append(Op(f"block.{name}", "k_mxn_vec",
+        ops.append(Op(f"block.{name}", "k_mxn_wide",
                       lambda elem=elem, q=q: fq.fq_mx_rows(a, fq.BF16, rb, cb, elem, q, e8, fqo),
                       2 * rb * cb + qb + rb * ((cb + 31) // 32) + 4 * rb * cb))
     n = syn.FULL["fp8"]["n"]
@@ -353,7 +353,7 @@ def ops_next_block_formats(fq, syn, torch, dev):
     sb = torch.empty((n + 15) // 16, dtype=torch.uint8, device=dev)
     g = torch.empty(1, dtype=torch.float32, device=dev)
     fqn = torch.empty(n, dtype=torch.float32, device=dev)
-    ops.append(Op("block.nvfp4", "k_reduce_partial+k_amax_final+k_nvfp4_vec",
+    ops.append(Op("block.nvfp4", "k_reduce_partial+k_amax_final+k_nvfp4_wide",
                   lambda: fq.fq_nvfp4(x, n, ws, wsb, q4, sb, g, fqn),
                   4 * n + 4 * n + (n + 1) // 2 + (n + 15) // 16 + 4 * n))
     return ops

