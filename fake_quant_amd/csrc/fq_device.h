@@ -544,8 +544,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint64_t block, uint32_t k0, uint
         }
         const uint64_t p0 = (uint64_t)kM0 * c0;
         const uint64_t p1 = (uint64_t)kM1 * c2;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        // three-input xors in one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
