@@ -236,6 +236,20 @@ __device__ __forceinline__ void store_nt(float4* p, float4 v) {
 // memory; they leave through a per-wave LDS transpose so that every store
 // instruction writes one contiguous run across the wave.
 // ---------------------------------------------------------------------------
+// bits of |v| when v is finite, else 0: the key of a finite-amax reduction
+// (unsigned order of the bits is the order of the magnitudes)
+__device__ __forceinline__ uint32_t finite_abs_bits(float v) {
+    const uint32_t a = as_u(v) & 0x7FFFFFFFu;
+    return a < 0x7F800000u ? a : 0u;
+}
+
+// element i of a float32 or (BF16) bfloat16 tensor as binary32 (bf16 widens exactly)
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* __restrict__ x, int64_t i) {
+    if constexpr (!BF16) return reinterpret_cast<const float*>(x)[i];
+    else return as_f((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
+}
+
 constexpr int kWide = 16;
 constexpr int kWidePad = kWide + 4;  // LDS floats per lane of the staging buffer (16-byte rows)
 

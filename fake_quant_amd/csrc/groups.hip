@@ -189,12 +189,6 @@ __global__ __launch_bounds__(kB) void k_groups_wide(const void* __restrict__ x, 
     }
 }
 
-template <int DT>
-__device__ __forceinline__ float elem(const void* __restrict__ x, int64_t i) {
-    if constexpr (DT == FQ_F32) return reinterpret_cast<const float*>(x)[i];
-    else return as_f((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
-}
-
 // Groups [g0, g1) of row r, in order: calibrate, store the parameters, quantize.
 // 4-bit codes go out a byte at a time (the high nibble held until its partner),
 // so a caller that owns whole bytes owns every nibble it writes.
@@ -210,14 +204,14 @@ __device__ void quant_groups_of_row(const void* __restrict__ x, int64_t r, int64
         const int64_t c0 = g * group;
         const int64_t c1 = c0 + group < cols ? c0 + group : cols;
         MinMax m;
-        for (int64_t c = c0; c < c1; ++c) m.add(elem<DT>(x, r * cols + c));
+        for (int64_t c = c0; c < c1; ++c) m.add(load_elem<DT == FQ_BF16>(x, r * cols + c));
         const IntCal cal = calibrate(m.mn, m.mx, rg, affine);
         scale[r * ng + g] = cal.scale;
         zp[r * ng + g] = cal.zp;
         fl |= (m.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
         const IntQ q(cal.scale, cal.zp, rg);
         for (int64_t c = c0; c < c1; ++c) {
-            const float o = q.offset(elem<DT>(x, r * cols + c));
+            const float o = q.offset(load_elem<DT == FQ_BF16>(x, r * cols + c));
             const int code = (int)o + cal.zp;
             if (fq) fq[r * cols + c] = o * cal.scale;
             if (!codes) continue;

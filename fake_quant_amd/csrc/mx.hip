@@ -24,7 +24,6 @@ constexpr int kB = fqh::kBlock;
 constexpr int kMx = 32;
 constexpr int kE4M3Emax = 8;
 
-
 // exponent of X for a block whose finite amax has bits `am`
 __device__ __forceinline__ int mx_exp(uint32_t am) {
     float A = am == 0u ? 1.0f : as_f(am);
@@ -35,11 +34,6 @@ __device__ __forceinline__ int mx_exp(uint32_t am) {
 __device__ __forceinline__ float mx_value(uint32_t b, int xe) {
     float v = __builtin_amdgcn_ldexpf(fp8_decode_finite<0>(b), xe);
     return b == 0x7Fu ? __builtin_nanf("") : v;
-}
-
-__device__ __forceinline__ uint32_t fin_abs(float v) {
-    uint32_t a = as_u(v) & 0x7FFFFFFFu;
-    return a < 0x7F800000u ? a : 0u;
 }
 
 // Wide layout (cols a multiple of 32, aligned buffers): lane v holds elements
@@ -61,7 +55,7 @@ __global__ __launch_bounds__(kB) void k_mx_wide(const void* __restrict__ x, int6
     }
     uint32_t am = 0;
 #pragma unroll
-    for (int i = 0; i < kWide; ++i) am = max(am, fin_abs(xe[i]));
+    for (int i = 0; i < kWide; ++i) am = max(am, finite_abs_bits(xe[i]));
     am = max(am, dpp_u<kQuadXor1>(am));
     const int xe_exp = mx_exp(am);
     uint32_t w[4];
@@ -104,7 +98,7 @@ __global__ __launch_bounds__(kB) void k_mx_any(const void* __restrict__ x, int64
             return as_f((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
         };
         uint32_t am = 0;
-        for (int64_t c = c0; c < c1; ++c) am = max(am, fin_abs(ld(c)));
+        for (int64_t c = c0; c < c1; ++c) am = max(am, finite_abs_bits(ld(c)));
         const int xe_exp = mx_exp(am);
         e8[g] = (uint8_t)(xe_exp + 127);
         for (int64_t c = c0; c < c1; ++c) {

@@ -76,11 +76,6 @@ using E2M3 = Narrow<2, 3>;
 using E3M2 = Narrow<3, 2>;
 static_assert(E2M1::kMax == 6.0f && E2M3::kMax == 7.5f && E3M2::kMax == 28.0f, "format maxima");
 
-__device__ __forceinline__ uint32_t fin_abs(float v) {
-    const uint32_t a = as_u(v) & 0x7FFFFFFFu;
-    return a < 0x7F800000u ? a : 0u;
-}
-
 // exponent of X = 2^(k - 1 - emax) for a block whose finite amax has bits am
 template <class F>
 __device__ __forceinline__ int mx_exp(uint32_t am) {
@@ -107,7 +102,7 @@ __global__ __launch_bounds__(kB) void k_mxn_wide(const void* __restrict__ x, int
     }
     uint32_t am = 0;
 #pragma unroll
-    for (int i = 0; i < kWide; ++i) am = max(am, fin_abs(e[i]));
+    for (int i = 0; i < kWide; ++i) am = max(am, finite_abs_bits(e[i]));
     am = max(am, dpp_u<kQuadXor1>(am));
     const int xe = mx_exp<F>(am);
     const float X = __builtin_amdgcn_ldexpf(1.0f, xe), inv = __builtin_amdgcn_ldexpf(1.0f, -xe);
@@ -135,12 +130,6 @@ __global__ __launch_bounds__(kB) void k_mxn_wide(const void* __restrict__ x, int
     if (fq) store16_staged(reinterpret_cast<float4*>(fq), v, nvec, o, s_out[threadIdx.x / kWave]);
 }
 
-template <int DT>
-__device__ __forceinline__ float elem_at(const void* __restrict__ x, int64_t i) {
-    if constexpr (DT == FQ_F32) return reinterpret_cast<const float*>(x)[i];
-    else return as_f((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
-}
-
 // MX, any shape or alignment: one thread per block of a row (a short block at
 // the row end); FP4 codes go out a byte at a time, and a block starts on a byte.
 template <int DT, class F>
@@ -153,13 +142,13 @@ __global__ __launch_bounds__(kB) void k_mxn_any(const void* __restrict__ x, int6
         const int64_t r = g / nbr, c0 = (g % nbr) * kMxBlock;
         const int64_t c1 = c0 + kMxBlock < cols ? c0 + kMxBlock : cols;
         uint32_t am = 0;
-        for (int64_t c = c0; c < c1; ++c) am = max(am, fin_abs(elem_at<DT>(x, r * cols + c)));
+        for (int64_t c = c0; c < c1; ++c) am = max(am, finite_abs_bits(load_elem<DT == FQ_BF16>(x, r * cols + c)));
         const int xe = mx_exp<F>(am);
         const float X = __builtin_amdgcn_ldexpf(1.0f, xe), inv = __builtin_amdgcn_ldexpf(1.0f, -xe);
         e8[g] = (uint8_t)(xe + 127);
         uint32_t hold = 0;
         for (int64_t c = c0; c < c1; ++c) {
-            const uint32_t code = F::encode(elem_at<DT>(x, r * cols + c) * inv);
+            const uint32_t code = F::encode(load_elem<DT == FQ_BF16>(x, r * cols + c) * inv);
             if (fq) fq[r * cols + c] = F::decode(code) * X;
             if constexpr (F::kMaxCode == 7u) {
                 if ((c & 1) == 0) {
@@ -231,7 +220,7 @@ __global__ __launch_bounds__(kB) void k_nvfp4_wide(const float* __restrict__ x, 
     }
     uint32_t am = 0;
 #pragma unroll
-    for (int i = 0; i < kWide; ++i) am = max(am, fin_abs(e[i]));
+    for (int i = 0; i < kWide; ++i) am = max(am, finite_abs_bits(e[i]));
     const float tmax = as_f(*tmax_bits);
     if (v == 0) *g_out = tmax / (6.0f * 448.0f);
     uint32_t sb;
@@ -266,7 +255,7 @@ __global__ __launch_bounds__(kB) void k_nvfp4_any(const float* __restrict__ x, i
         if (b == 0) *g_out = tmax / (6.0f * 448.0f);
         const int64_t i0 = b * kNvBlock, i1 = i0 + kNvBlock < n ? i0 + kNvBlock : n;
         uint32_t am = 0;
-        for (int64_t i = i0; i < i1; ++i) am = max(am, fin_abs(x[i]));
+        for (int64_t i = i0; i < i1; ++i) am = max(am, finite_abs_bits(x[i]));
         uint32_t sb;
         const float X = nv_scale(as_f(am), tmax, &sb);
         const ExactDiv d(X);

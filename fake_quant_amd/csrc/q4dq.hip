@@ -86,10 +86,6 @@ __device__ __forceinline__ float recon_scale(uint32_t u, float S) { return (floa
 // A wave holding Inf / NaN takes the general per-element rule (finite absmax,
 // NaN -> 0, +-Inf -> +-7).
 __device__ __forceinline__ uint32_t abs_bits(float v) { return as_u(v) & 0x7FFFFFFFu; }
-__device__ __forceinline__ uint32_t fin_bits(float v) {
-    uint32_t a = abs_bits(v);
-    return a < 0x7F800000u ? a : 0u;
-}
 // two nibbles from two magic-rounded floats (low 4 bits of their patterns)
 __device__ __forceinline__ uint32_t nib_pair(float f0, float f1) {
     return __builtin_amdgcn_ubfe(as_u(f0), 0, 4) << 4 | __builtin_amdgcn_ubfe(as_u(f1), 0, 4);
@@ -147,7 +143,8 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
     if (wave_nf) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            uint32_t m = max(max(fin_bits(v[j].x), fin_bits(v[j].y)), max(fin_bits(v[j].z), fin_bits(v[j].w)));
+            uint32_t m = max(max(finite_abs_bits(v[j].x), finite_abs_bits(v[j].y)),
+                             max(finite_abs_bits(v[j].z), finite_abs_bits(v[j].w)));
             m = row16_max_u(m);
             my_am = (lrow == j) ? m : my_am;
         }

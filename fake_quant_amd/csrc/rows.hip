@@ -50,12 +50,6 @@ struct Vec<FQ_BF16> {
     }
 };
 
-template <int DT>
-__device__ __forceinline__ float elem(const void* row, int64_t c) {
-    if (DT == FQ_F32) return reinterpret_cast<const float*>(row)[c];
-    return as_f((uint32_t)reinterpret_cast<const uint16_t*>(row)[c] << 16);
-}
-
 // Load vector vi of a row: 16-byte load when aligned, else element loads with a
 // bound check against cols (missing elements read as 0 and are marked invalid by
 // the caller through the same bound).

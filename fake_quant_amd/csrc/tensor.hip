@@ -43,11 +43,6 @@ enum { kMinMax = 0, kAmax = 1 };
 constexpr int kRU = fqh::kReduceChunks;
 constexpr int kRT = fqh::kReduceThreads;
 
-__device__ __forceinline__ uint32_t fin_abs_bits(float v) {
-    uint32_t a = as_u(v) & 0x7FFFFFFFu;
-    return a < 0x7F800000u ? a : 0u;
-}
-
 template <int MODE, bool AL>
 __global__ __launch_bounds__(kRT) void k_reduce_partial(const float* __restrict__ x, int64_t n,
                                                        float4* __restrict__ part) {
@@ -71,10 +66,10 @@ __global__ __launch_bounds__(kRT) void k_reduce_partial(const float* __restrict_
                 v[u] = (c0 + u * kRT < nfull) ? ld(c0 + u * kRT) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < kRU; ++u)
-                acc[u] = max(acc[u], max(max(fin_abs_bits(v[u].x), fin_abs_bits(v[u].y)),
-                                         max(fin_abs_bits(v[u].z), fin_abs_bits(v[u].w))));
+                acc[u] = max(acc[u], max(max(finite_abs_bits(v[u].x), finite_abs_bits(v[u].y)),
+                                         max(finite_abs_bits(v[u].z), finite_abs_bits(v[u].w))));
         }
-        if (tail) acc[0] = max(acc[0], fin_abs_bits(x[4 * nfull + threadIdx.x]));
+        if (tail) acc[0] = max(acc[0], finite_abs_bits(x[4 * nfull + threadIdx.x]));
 #pragma unroll
         for (int u = 1; u < kRU; ++u) acc[0] = max(acc[0], acc[u]);
         r = make_float4(0.f, as_f(wave_max_u(acc[0])), 0.f, 0.f);
