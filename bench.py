@@ -24,7 +24,8 @@ op's share of the timed steps; `per_op_cold_warm` times each op on its own with
 its inputs evicted from the caches (cold) and back to back (warm);
 `copy_f32_ceiling` is a plain device copy timed the same ways; `next_rows`
 times the rows beyond the step (stochastic rounding, the QAT optimizer step,
-per-column calibration) the same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
+per-column, percentile and group-wise calibration, the FP4 / FP6 block formats)
+the same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -56,11 +57,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None,
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16 (step), "
-                         "stochastic_rounding qat_step per_column (beside the step)")
+                         "stochastic_rounding qat_step per_column percentile group_wise block_formats "
+                         "(beside the step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the rows beyond the step (stochastic rounding), timed cold / warm on their own")
+                    help="skip the rows beyond the step (stochastic rounding, QAT step, calibration variants, "
+                         "block formats), timed cold / warm on their own")
     ap.add_argument("--copy-ref", action="store_true",
                     help="only run COPY_REF_LAUNCHES plain device copies of COPY_REF_BYTES each (the known-size "
                          "reference that scales HBM counter readings) and exit")
@@ -564,7 +567,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1",
+        print("bench.py: measures one GPU only (there is no multi-GPU path); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
