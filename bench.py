@@ -22,7 +22,8 @@ output written once) / measured step time, in GB/s; `roofline` is the dominant
 kernel's achieved bandwidth against the 8 TB/s HBM peak; `kernels` gives every
 op's share of the timed steps; `per_op_cold_warm` times each op on its own with
 its inputs evicted from the caches (cold) and back to back (warm);
-`copy_f32_ceiling` is a plain device copy timed the same ways; `next_rows`
+`copy_f32_ceiling` is a plain device copy timed the same ways (also at the smaller
+workloads' input sizes, under `by_size`); `next_rows`
 times the rows beyond the step (stochastic rounding, the QAT optimizer step,
 per-column, percentile and group-wise calibration, the FP4 / FP6 block formats)
 the same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
@@ -120,7 +121,7 @@ def op_rows_f32(fq, torch, w, r, c, bits, scheme, sname, dev):
     sc = torch.empty(r, dtype=torch.float32, device=dev)
     zp = torch.empty(r, dtype=torch.int32, device=dev)
     fl = torch.zeros(1, dtype=torch.int32, device=dev)
-    return Op(f"rows_f32.int{bits}_{sname}", "k_quant_rows",
+    return Op(f"rows_f32.int{bits}_{sname}", "k_rows_wg",
               lambda: fq.fq_quant_rows(w, fq.F32, r, c, bits, scheme, codes, fqo, sc, zp, fl),
               4 * r * c + cb + 4 * r * c + 8 * r)
 
@@ -139,7 +140,7 @@ def ops_fp8_format(fq, torch, x, n, scales, fmt, fname, dev):
     s = scales[fmt:fmt + 1]
     return [Op(f"fp8.quantize_{fname}", "k_fp8_quant", lambda: fq.fq_fp8_quantize(x, n, fmt, s, q, fqo),
                4 * n + n + 4 * n),
-            Op(f"fp8.dequantize_{fname}", "k_fp8_dequant", lambda: fq.fq_fp8_dequantize(q, n, fmt, s, deq),
+            Op(f"fp8.dequantize_{fname}", "k_fp8_dequant_w", lambda: fq.fq_fp8_dequantize(q, n, fmt, s, deq),
                n + 4 * n)]
 
 
@@ -171,7 +172,7 @@ def ops_q4dq(fq, syn, torch, dev):
         Op("q4dq.quantize_recon", "k_q4dq_full",
            lambda: fq.fq_q4dq_quantize(x, n, packed, qs, sup, None, recon, flags),
            4 * n + npk + nb + 4 * ns + 4 * n),
-        Op("q4dq.dequantize", "k_q4dq_dequant",
+        Op("q4dq.dequantize", "k_q4dq_dequant_full",
            lambda: fq.fq_q4dq_dequantize(packed, qs, sup, n, deq), npk + nb + 4 * ns + 4 * n),
     ]
 
@@ -186,7 +187,7 @@ def ops_rows_bf16(fq, syn, torch, dev):
     q = torch.empty(r * c, dtype=torch.uint8, device=dev)
     e8 = torch.empty(r * ((c + 31) // 32), dtype=torch.uint8, device=dev)
     return [
-        Op("rows_bf16.int8_affine", "k_quant_rows",
+        Op("rows_bf16.int8_affine", "k_rows_wg",
            lambda: fq.fq_quant_rows(a, fq.BF16, r, c, 8, fq.AFFINE, codes, None, sc, zp, fl),
            2 * r * c + r * c + 8 * r),
         Op("rows_bf16.mxfp8_e4m3", "k_mx_wide",
@@ -297,7 +298,7 @@ def ops_next_percentile(fq, syn, torch, dev):
     for name, x, n in (("tensor_2^20", x1, n1), ("weights_2^24", w, r * c)):
         wsb = fq.fq_percentile_workspace_bytes(n)
         ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
-        ops.append(Op(f"percentile.{name}", "k_pct_first+k_pct_second+k_pct_third",
+        ops.append(Op(f"percentile.{name}", "k_pct_init+k_pct_first+k_pct_second+k_pct_third",
                       lambda x=x, n=n, ws=ws, wsb=wsb: fq.fq_tensor_params_percentile(
                           x, n, 8, fq.AFFINE, 0.001, ws, wsb, params, flags),
                       4 * n + 16))
@@ -325,7 +326,7 @@ def ops_next_groups(fq, syn, torch, dev):
         zp = torch.empty(rows * ng, dtype=torch.int32, device=dev)
         flags = torch.zeros(1, dtype=torch.int32, device=dev)
         esz = 4 if dt == fq.F32 else 2
-        ops.append(Op(f"groups.{name}", "k_groups",
+        ops.append(Op(f"groups.{name}", "k_groups_wide",
                       lambda x=x, dt=dt, rows=rows, cols=cols, group=group, bits=bits, codes=codes, fqo=fqo,
                       scale=scale, zp=zp, flags=flags: fq.fq_quant_groups(
                           x, dt, rows, cols, group, bits, fq.SYM, codes, fqo, scale, zp, flags),
@@ -454,6 +455,22 @@ def cold_warm(ops, fq, torch, stream, ceiling=True):
     ceiling = dict(kernel="fqb_copy_f32", bytes=nbytes, cold_gbs=round(nbytes / (cm * 1e-3) / 1e9, 1),
                    warm_gbs=round(nbytes / (wm * 1e-3) / 1e9, 1),
                    cold_frac=round(nbytes / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    # the same copy at the input sizes of the smaller workloads (2^20 f32 tensor,
+    # [4096, 4096] f32 rows, 2^26 f32 fp8 tensor): what a plain stream of that size
+    # reaches, launch and ramp included
+    by_size = {}
+    for k in (20, 24, 26):
+        m = 1 << k
+        copy_m = lambda m=m: fq.fqb_copy_f32(src, dst, m)
+        for _ in range(PRE_REPS):
+            copy_m()
+        (cm, _), (wm, _) = (_median_min(_timed_reps(copy_m, COLD_REPS, torch, stream, before=flush)),
+                            _median_min(_timed_reps(copy_m, WARM_REPS, torch, stream)))
+        nb = 8 * m
+        by_size[f"2^{k} f32"] = dict(bytes=nb, cold_us=round(cm * 1e3, 2), warm_us=round(wm * 1e3, 2),
+                                     cold_frac=round(nb / (cm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     warm_frac=round(nb / (wm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    ceiling["by_size"] = by_size
     del scratch, src, dst
     return res, ceiling
 

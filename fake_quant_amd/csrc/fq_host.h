@@ -73,12 +73,18 @@ inline unsigned grid_all(int64_t items, int64_t per_block) {
 // reduces tiles b, b + G, ... into one partial in the workspace, with G at most
 // kMaxReduceBlocks.
 #ifndef FQ_REDUCE_THREADS
-#define FQ_REDUCE_THREADS 256
+#define FQ_REDUCE_THREADS 512
+#endif
+#ifndef FQ_REDUCE_CHUNKS
+#define FQ_REDUCE_CHUNKS 4
+#endif
+#ifndef FQ_REDUCE_MAX_BLOCKS
+#define FQ_REDUCE_MAX_BLOCKS 16384
 #endif
 constexpr int kReduceThreads = FQ_REDUCE_THREADS;
-constexpr int kReduceChunks = 4;
+constexpr int kReduceChunks = FQ_REDUCE_CHUNKS;
 constexpr int64_t kReduceTile = (int64_t)kReduceChunks * kReduceThreads;
-constexpr int64_t kMaxReduceBlocks = 16384;
+constexpr int64_t kMaxReduceBlocks = FQ_REDUCE_MAX_BLOCKS;
 constexpr int kFinalThreads = 1024;
 inline unsigned reduce_blocks(int64_t n) {
     int64_t chunks = (n + 3) / 4;

@@ -39,7 +39,6 @@ using namespace fqk;
 namespace {
 
 constexpr int kPB = 512;  // threads per workgroup of the passes
-constexpr int kPW = kPB / kWave;
 constexpr int kPasses = 3;
 constexpr int kMaxBins = 2048;
 constexpr int kU = 4;       // 16-byte loads in flight per thread

@@ -19,7 +19,6 @@ using namespace fqk;
 namespace {
 
 constexpr int kB = fqh::kBlock;
-constexpr int kWaves = kB / kWave;
 
 __device__ __forceinline__ float4 ld4(const float* p, int64_t c) {
     return *reinterpret_cast<const float4*>(p + 4 * c);

@@ -83,7 +83,7 @@ def test_constants_match_header(fq):
 def test_host_sizes(fq):
     assert fq.fq_workspace_bytes(0) == 0
     assert fq.fq_workspace_bytes(1) == 16
-    assert fq.fq_workspace_bytes(1 << 20) == 256 * 16
+    assert fq.fq_workspace_bytes(1 << 20) == 128 * 16  # one partial per 8192 elements
     assert fq.fq_workspace_bytes(1 << 40) == 16384 * 16
     assert fq.fq_q4dq_sizes(1) == (1, 1, 1)
     assert fq.fq_q4dq_sizes(200) == (100, 4, 1)
