@@ -368,9 +368,11 @@ NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, 
                   "block_formats": ops_next_block_formats}
 
 
-def build_next_ops(fq, syn, torch, dev="cuda"):
-    """The rows beyond the step (measured on their own, not counted in `value`)."""
-    return {name: make(fq, syn, torch, dev) for name, make in NEXT_WORKLOADS.items()}
+def build_next_ops(fq, syn, torch, only=None, dev="cuda"):
+    """The rows beyond the step (measured on their own, not counted in `value`),
+    those named in `only` if given."""
+    return {name: make(fq, syn, torch, dev) for name, make in NEXT_WORKLOADS.items()
+            if only is None or name in only}
 
 
 # Workloads are built largest first: the 4-bit workload's 4 GiB buffers, placed
@@ -601,6 +603,14 @@ def main():
         return
     log("drawing inputs and allocating outputs")
     ops = build_ops(fq, syn, torch, args.only)
+    if not ops:
+        # only rows beyond the step were asked for
+        next_rows = {name: cold_warm(nops, fq, torch, torch.cuda.current_stream(), ceiling=False)[0]
+                     for name, nops in build_next_ops(fq, syn, torch, args.only).items()}
+        print(json.dumps({"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1,
+                          "config": {"workload": "only " + ",".join(args.only)}, "next_rows": next_rows}),
+              flush=True)
+        return
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     log(f"{len(ops)} ops per step; warmup {args.warmup}")
@@ -655,8 +665,7 @@ def main():
     if not args.no_next and (args.only is None or any(w in NEXT_WORKLOADS for w in args.only)):
         log("rows beyond the step, cold / warm")
         next_rows = {name: cold_warm(nops, fq, torch, stream, ceiling=False)[0]
-                     for name, nops in build_next_ops(fq, syn, torch).items()
-                     if args.only is None or name in args.only}
+                     for name, nops in build_next_ops(fq, syn, torch, args.only).items()}
         torch.cuda.synchronize()
 
     cpu = None

@@ -78,3 +78,41 @@ def test_unaligned_view(fqlib, orc):
     buf = synthetic.rows_f32_inputs(1, 100 * 64 + 3, device="cuda").reshape(-1)
     x = buf[3:].reshape(100, 64)
     check_cols(fqlib, orc, x, 8, 1, "unaligned")
+
+
+# fp32 shapes of the one-pass strip kernel (1024 < rows <= 4096, cols a multiple
+# of 16 with at least half as many 16-column strips as compute units): smallest
+# and largest row counts, rows that leave a partial 256-row load, a strip count
+# that is not a multiple of the eight XCDs, and more strips than compute units
+STRIP_SHAPES = [(1025, 2048), (4096, 2080), (2500, 4096), (4095, 8192), (1536, 2064)]
+
+
+@pytest.mark.parametrize("shape", STRIP_SHAPES)
+def test_strip_path_shapes(fqlib, orc, shape):
+    rows, cols = shape
+    w = synthetic.rows_f32_inputs(rows, cols, device="cuda", seed=rows + cols)
+    for bits, scheme in ((8, 0), (8, 1), (4, 0), (4, 1)):
+        check_cols(fqlib, orc, w, bits, scheme, f"strip {shape}")
+
+
+def test_strip_special_columns(fqlib, orc):
+    """Special columns spread over several strips of the one-pass kernel, with the
+    wave-uniform fast path taken by some strips and not by others."""
+    rng = np.random.default_rng(2)
+    rows, cols = 1100, 2048
+    x = (rng.standard_normal((rows, cols)) * np.exp(rng.normal(-3, 0.5, (1, cols)))).astype(np.float32)
+    x[:, 0] = 0.0
+    x[5, 17] = np.nan
+    x[1099, 40] = np.inf
+    x[:, 63] = np.nan
+    x[:, 100] *= np.float32(1e-33)
+    x[:, 129] = np.abs(x[:, 129]) + 1.0
+    x[:, 130] = -np.abs(x[:, 130]) - 1.0
+    x[:, 511] = -0.0
+    x[:, 777] *= np.float32(1e30)
+    x[::2, 1500] = -np.inf
+    x[:, 2047] = np.float32(3.0)
+    xt = torch.from_numpy(x).cuda()
+    for bits in (8, 4):
+        for scheme in (0, 1):
+            check_cols(fqlib, orc, xt, bits, scheme, "strip special columns")
