@@ -276,7 +276,7 @@ def ops_next_cols(fq, syn, torch, dev):
     for bits, scheme, name in ((8, fq.SYM, "int8_sym"), (4, fq.AFFINE, "int4_affine")):
         nb = r * c if bits == 8 else r * ((c + 1) // 2)
         codes = torch.empty(nb, dtype=torch.uint8, device=dev)
-        ops.append(Op(f"cols.{name}", "k_cols_minmax+k_cols_fold+k_cols_quant",
+        ops.append(Op(f"cols.{name}", "k_cols_strip",
                       lambda bits=bits, scheme=scheme, codes=codes: fq.fq_quant_cols(
                           w, fq.F32, r, c, bits, scheme, ws, wsb, codes, fqo, scale, zp, flags),
                       4 * r * c + nb + 4 * r * c + 8 * c))
