@@ -542,7 +542,21 @@ def cpu_baseline(orc, syn, torch, only):
         parts.append(f"rows_bf16: {rs} of {r} rows")
     return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample="; ".join(parts) + f" (single-threaded, {total_s:.1f} s of CPU work)",
-                seconds=round(total_s, 3))
+                seconds=round(total_s, 3), host=host_cpu())
+
+
+def host_cpu():
+    """The host the oracle ran on: cores this process may use, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(cores_available=len(os.sched_getaffinity(0)), cpu_model=model)
 
 
 def traffic_record(kernel):
