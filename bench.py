@@ -6,8 +6,8 @@
 One step runs every operation of the path once, each on the full-size synthetic
 input of its workload (all inputs resident in HBM before timing starts):
 
-  tensor    per-tensor symmetric int8 of 2^20 N(0,1) fp32: calibration, fake-quant
-            (codes + fq), STE backward
+  tensor    per-tensor symmetric int8 of 2^20 N(0,1) fp32: calibration and fake-quant
+            (codes + fq) in one call, STE backward
   rows_f32  per-row int8 / int4, symmetric / affine of a [4096, 4096] fp32 weight
             (codes + fq + scale + zero-point)
   fp8       finite-amax scale, E4M3 and E5M2 quantize (bytes + fq) and dequantize
@@ -24,8 +24,9 @@ op's share of the timed steps; `per_op_cold_warm` times each op on its own with
 its inputs evicted from the caches (cold) and back to back (warm);
 `copy_f32_ceiling` is a plain device copy timed the same ways (also at the smaller
 workloads' input sizes, under `by_size`); `next_rows`
-times the rows beyond the step (stochastic rounding, the QAT optimizer step,
-per-column, percentile and group-wise calibration, the FP4 / FP6 block formats)
+times the rows beyond the step (the per-tensor calibration and fake-quant as two
+separate calls, stochastic rounding, the QAT optimizer step, per-column,
+percentile and group-wise calibration, the FP4 / FP6 block formats)
 the same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
 Prints one JSON line.
 """
@@ -58,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", nargs="*", default=None,
                     help="restrict to workloads: tensor rows_f32 fp8 q4dq rows_bf16 (step), "
-                         "stochastic_rounding qat_step per_column percentile group_wise block_formats "
+                         "tensor_calls stochastic_rounding qat_step per_column percentile group_wise block_formats "
                          "(beside the step)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-cold", action="store_true", help="skip the per-op cold / warm timings")
@@ -105,12 +106,32 @@ def ops_tensor(fq, syn, torch, dev):
     fqo = torch.empty(n, dtype=torch.float32, device=dev)
     gin = torch.empty(n, dtype=torch.float32, device=dev)
     bounds = params.view(torch.float32)[2:4]
+    # calibration (reduction + parameters) and fake-quant in the one call that
+    # does both in two launches; the STE reads the bounds that call stores
+    return [
+        Op("tensor.calibrate_fake_quant_int8", "k_reduce_partial+k_fq_int_tensor_fold",
+           lambda: fq.fq_calibrate_fake_quant_int_tensor(x, n, 8, fq.SYM, ws, wsb, params, codes, fqo, flags),
+           4 * n + 16 + n + 4 * n),
+        Op("tensor.ste_backward", "k_ste", lambda: fq.fq_ste_backward(g, n, x, n, bounds, gin), 12 * n),
+    ]
+
+
+def ops_next_tensor_calls(fq, syn, torch, dev):
+    """The per-tensor calibration and fake-quant of the step as two separate calls
+    (three launches), measured beside the step."""
+    n = syn.FULL["tensor"]["n"]
+    x, _ = syn.tensor_inputs(n, device=dev)
+    wsb = fq.fq_workspace_bytes(n)
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    params = torch.empty(4, dtype=torch.int32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    codes = torch.empty(n, dtype=torch.int8, device=dev)
+    fqo = torch.empty(n, dtype=torch.float32, device=dev)
     return [
         Op("tensor.params_int8_sym", "k_reduce_partial+k_params_int_final",
            lambda: fq.fq_tensor_params_int(x, n, 8, fq.SYM, ws, wsb, params, flags), 4 * n + 16),
         Op("tensor.fake_quant_int8", "k_fq_int_tensor",
            lambda: fq.fq_fake_quant_int_tensor(x, n, 8, fq.SYM, params, codes, fqo), 4 * n + n + 4 * n),
-        Op("tensor.ste_backward", "k_ste", lambda: fq.fq_ste_backward(g, n, x, n, bounds, gin), 12 * n),
     ]
 
 
@@ -363,7 +384,7 @@ def ops_next_block_formats(fq, syn, torch, dev):
     return ops
 
 
-NEXT_WORKLOADS = {"stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols,
+NEXT_WORKLOADS = {"tensor_calls": ops_next_tensor_calls, "stochastic_rounding": ops_next_sr, "qat_step": ops_next_qat, "per_column": ops_next_cols,
                   "percentile": ops_next_percentile, "group_wise": ops_next_groups,
                   "block_formats": ops_next_block_formats}
 
@@ -691,7 +712,7 @@ def main():
         torch.cuda.empty_cache()
         cpu = cpu_baseline(orc, syn, torch, args.only)
 
-    workloads = "tensor 2^20 f32 int8 + STE; rows_f32 [4096,4096] int8/int4 sym/affine; fp8 2^26 E4M3/E5M2; " \
+    workloads = "tensor 2^20 f32 int8 calibrate + fake-quant + STE; rows_f32 [4096,4096] int8/int4 sym/affine; fp8 2^26 E4M3/E5M2; " \
                 "q4dq 2^30 f32 4-bit + double-quant; rows_bf16 [16384,8192] per-token int8 + 32-block E4M3/E8M0"
     if args.only:
         workloads = "only " + ",".join(args.only)

@@ -94,6 +94,10 @@ inline unsigned reduce_blocks(int64_t n) {
     return (unsigned)want;
 }
 
+// Tensors with at most this many reduction partials take the two-launch
+// calibration + fake-quant (every block of the second launch folds them all).
+constexpr int64_t kFoldMaxParts = 512;
+
 // Pass 2 of the tensor-scope min / max over `nparts` partial records (float4:
 // finite min, finite max, max |x| bits, -) that a fused kernel left in the
 // workspace: derives the integer parameters on the device ([QAT] from_minmax,

@@ -318,6 +318,68 @@ __global__ __launch_bounds__(kB) void k_fq_int_tensor(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Per-tensor calibration + fake-quant in two launches for small tensors: after
+// the reduction's first pass, every block of this kernel folds the (at most
+// kFoldMaxParts) partials itself and derives the parameters ([QAT] from_minmax),
+// so the one-block parameter pass and its launch drop out.  The fold is
+// order-free, so every block derives the same parameters; block 0 stores them.
+// Each thread's chunk of x is loaded before the partials, so the two loads
+// overlap.  One 16-byte chunk per thread over a grid covering the tensor; the
+// n % 4 elements after the last whole chunk go to thread 0 of block 0.
+// ---------------------------------------------------------------------------
+constexpr int kFoldMaxParts = (int)fqh::kFoldMaxParts;
+static_assert(kFoldMaxParts % kB == 0, "whole loads of partials per thread");
+
+template <int BITS>
+__global__ __launch_bounds__(kB) void k_fq_int_tensor_fold(const float* __restrict__ x, int64_t n, int affine,
+                                                           const float4* __restrict__ part, int nparts,
+                                                           fq_int_params* __restrict__ params,
+                                                           uint8_t* __restrict__ codes, float* __restrict__ fq,
+                                                           uint32_t* __restrict__ flags) {
+    const int64_t nfull = n >> 2;
+    const int t = threadIdx.x;
+    const int64_t c = (int64_t)blockIdx.x * kB + t;
+    const float4 v = c < nfull ? ld4(x, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    MinMax m;
+#pragma unroll
+    for (int k = 0; k < kFoldMaxParts / kB; ++k) {
+        const int i = t + k * kB;
+        if (i < nparts) {
+            const float4 p = part[i];
+            m.merge(p.x, p.y, as_u(p.z));
+        }
+    }
+    __shared__ float4 lds[kB / kWave];
+    const float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
+    if (t % kWave == 0) lds[t / kWave] = r;
+    __syncthreads();
+    MinMax g;
+#pragma unroll
+    for (int i = 0; i < kB / kWave; ++i) g.merge(lds[i].x, lds[i].y, as_u(lds[i].z));
+    const IntRange rg = int_range(BITS, affine != 0);
+    const IntCal cal = calibrate(g.mn, g.mx, rg, affine != 0);
+    if (blockIdx.x == 0 && t == 0) {
+        fq_int_params out;
+        out.scale = cal.scale;
+        out.zero_point = cal.zp;
+        out.real_min = (float)(rg.qmin - cal.zp) * cal.scale;
+        out.real_max = (float)(rg.qmax - cal.zp) * cal.scale;
+        *params = out;
+        const uint32_t f = (g.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+        if (flags && f) atomicOr(flags, f);
+    }
+    const IntQ q(cal.scale, cal.zp, rg);
+    auto run = [&](auto op) {
+        if (c < nfull) op.vector_chunk(c, v);
+        if (blockIdx.x == 0 && t == 0 && (n & 3)) op.scalar_chunk(x, nfull, (int)(n & 3));
+    };
+    // one uniform decision per launch, as in k_fq_int_tensor
+    if (q.zero) run(IntTensorOp<BITS, 0>{q, cal.scale, cal.zp, codes, fq});
+    else if (q.div.fast) run(IntTensorOp<BITS, 1>{q, cal.scale, cal.zp, codes, fq});
+    else run(IntTensorOp<BITS, 2>{q, cal.scale, cal.zp, codes, fq});
+}
+
+// ---------------------------------------------------------------------------
 // Integer dequantize ([QAT] dequant(q) = (q - zero_point) * scale)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int sext4(uint32_t nib) { return ((int)(nib << 28)) >> 28; }
@@ -480,6 +542,34 @@ int fq_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme,
         if (al) k_fq_int_tensor<4, true><<<G, kB, 0, stream>>>(x, n, aff, params, cd, fq);
         else k_fq_int_tensor<4, false><<<G, kB, 0, stream>>>(x, n, aff, params, cd, fq);
     }
+    return fqh::launched();
+}
+
+int fq_calibrate_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme, void* workspace,
+                                      size_t workspace_bytes, fq_int_params* params, void* codes, float* fq,
+                                      uint32_t* flags, hipStream_t stream) {
+    if (!fqh::valid_bits(bits) || !fqh::valid_scheme(scheme)) return FQ_E_UNSUPPORTED;
+    if (!x || n < 1 || !workspace || !params || (!codes && !fq)) return FQ_E_INVALID;
+    if (workspace_bytes < fq_workspace_bytes(n) || !fqh::aligned(workspace, 16)) return FQ_E_INVALID;
+    if (!fqh::aligned(params, 4) || !fqh::aligned(flags, 4) || !fqh::aligned(x, 4) || !fqh::aligned(fq, 4))
+        return FQ_E_INVALID;
+    const bool al = fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, bits == 8 ? 4 : 2);
+    if (!al || fqh::reduce_blocks(n) > fqh::kFoldMaxParts) {
+        // larger or unaligned tensors: the two calls (three launches)
+        int st = fq_tensor_params_int(x, n, bits, scheme, workspace, workspace_bytes, params, flags, stream);
+        if (st != FQ_OK) return st;
+        return fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes, fq, stream);
+    }
+    const unsigned G = launch_partial<kMinMax>(x, n, workspace, stream);
+    int st = fqh::launched();
+    if (st != FQ_OK) return st;
+    const unsigned Q = fqh::grid_all((n + 3) / 4, kB);
+    const int aff = scheme == FQ_AFFINE;
+    uint8_t* cd = (uint8_t*)codes;
+    if (bits == 8)
+        k_fq_int_tensor_fold<8><<<Q, kB, 0, stream>>>(x, n, aff, (const float4*)workspace, (int)G, params, cd, fq, flags);
+    else
+        k_fq_int_tensor_fold<4><<<Q, kB, 0, stream>>>(x, n, aff, (const float4*)workspace, (int)G, params, cd, fq, flags);
     return fqh::launched();
 }
 

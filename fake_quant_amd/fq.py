@@ -64,6 +64,7 @@ _SIGS = {
     "fq_q4dq_sizes": (_INT, [_I64, _P, _P, _P]),
     "fq_tensor_params_int": (_INT, [_P, _I64, _INT, _INT, _P, _SZ, _P, _P, _P]),
     "fq_fake_quant_int_tensor": (_INT, [_P, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "fq_calibrate_fake_quant_int_tensor": (_INT, [_P, _I64, _INT, _INT, _P, _SZ, _P, _P, _P, _P, _P]),
     "fq_dequantize_int_tensor": (_INT, [_P, _I64, _INT, _P, _P, _P]),
     "fq_ste_backward": (_INT, [_P, _I64, _P, _I64, _P, _P, _P]),
     "fq_quant_rows": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P]),
@@ -190,6 +191,20 @@ def fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes=None, fq=None, st
     _check("fq_fake_quant_int_tensor",
            _lib.fq_fake_quant_int_tensor(_ptr(x), n, bits, scheme, _ptr(params), _ptr(codes), _ptr(fq),
                                          _stream(stream)))
+
+
+def fq_calibrate_fake_quant_int_tensor(x, n, bits, scheme, workspace, workspace_bytes, params, codes=None,
+                                       fq=None, flags=None, stream=None):
+    nm = "fq_calibrate_fake_quant_int_tensor"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "workspace", workspace, workspace_bytes)
+    _need(nm, "params", params, 16)
+    _need(nm, "codes", codes, _codes_bytes(n, bits))
+    _need(nm, "fq", fq, 4 * n)
+    _need(nm, "flags", flags, 4)
+    _check(nm, _lib.fq_calibrate_fake_quant_int_tensor(_ptr(x), n, bits, scheme, _ptr(workspace), workspace_bytes,
+                                                       _ptr(params), _ptr(codes), _ptr(fq), _ptr(flags),
+                                                       _stream(stream)))
 
 
 def fq_cols_workspace_bytes(rows, cols) -> int:
@@ -479,6 +494,21 @@ def fake_quant_int_tensor(x, params, bits=8, scheme=SYM, want_codes=True, want_f
     fq = _empty(n, torch.float32, x) if want_fq else None
     fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes, fq)
     return codes, fq
+
+
+def calibrate_fake_quant_int_tensor(x, bits=8, scheme=SYM, want_codes=True, want_fq=True, check=False):
+    """Per-tensor calibration and fake-quant in one call -> (params int32[4], codes, fq, flags)."""
+    n = x.numel()
+    wsb = fq_workspace_bytes(n)
+    ws = _empty(max(wsb // 4, 1), torch.float32, x)
+    params = _empty(4, torch.int32, x)
+    flags = _zeros_flags(x)
+    codes = _empty(n if bits == 8 else (n + 1) // 2, torch.int8 if bits == 8 else torch.uint8, x) if want_codes else None
+    fq = _empty(n, torch.float32, x) if want_fq else None
+    fq_calibrate_fake_quant_int_tensor(x, n, bits, scheme, ws, wsb, params, codes, fq, flags)
+    if check:
+        raise_on_flags("calibrate_fake_quant_int_tensor", flags)
+    return params, codes, fq, flags
 
 
 def fake_quant_int_tensor_sr(x, params, seed, offset=0, bits=8, scheme=SYM, want_codes=True, want_fq=True):

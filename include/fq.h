@@ -124,6 +124,19 @@ int fq_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme,
                              const fq_int_params* params, void* codes, float* fq,
                              hipStream_t stream);
 
+/* Per-tensor calibration followed by fake-quant ([QAT] per_tensor_minmax,
+ * from_minmax, fake_quant_int): the results of fq_tensor_params_int followed by
+ * fq_fake_quant_int_tensor on the same arguments, bit for bit -- params, codes,
+ * fq and flags as those two calls define them.  Tensors of up to 2^22 elements
+ * with 16-byte aligned x / fq and 4-byte (int8) or 2-byte (int4) aligned codes
+ * take two launches instead of three: the reduction's first pass, then a
+ * fake-quant pass whose every block folds the partials and derives the
+ * parameters itself.  Others make the two calls.  `workspace` of at least
+ * fq_workspace_bytes(n) bytes, as for fq_tensor_params_int. */
+int fq_calibrate_fake_quant_int_tensor(const float* x, int64_t n, int bits, int scheme, void* workspace,
+                                      size_t workspace_bytes, fq_int_params* params, void* codes, float* fq,
+                                      uint32_t* flags, hipStream_t stream);
+
 /* [QAT] dequant(q) = (q - zero_point) * scale over stored codes (layout as
  * fq_fake_quant_int_tensor's `codes`). */
 int fq_dequantize_int_tensor(const void* codes, int64_t n, int bits, const fq_int_params* params,

@@ -49,14 +49,14 @@ def test_every_bench_op_passes_buffers_that_fit(monkeypatch):
     monkeypatch.setattr(fq, "_need", cpu_need)
     monkeypatch.setattr(fq, "_stream", lambda stream=None: None)
     ops = bench.build_ops(fq, synthetic, torch, None, dev="cpu")
-    assert len(ops) == 16
+    assert len(ops) == 15
     # built largest first, timed in WORKLOADS order
     assert sorted(bench.BUILD_ORDER) == sorted(bench.WORKLOADS)
     groups = [op.name.split(".")[0] for op in ops]
     assert [g for i, g in enumerate(groups) if i == 0 or groups[i - 1] != g] == list(bench.WORKLOADS)
     for op in ops:
         op.fn()
-    assert len(recorder.calls) == 16
+    assert len(recorder.calls) == 15
     assert sum(op.nbytes for op in ops) > 0
 
 
@@ -68,7 +68,7 @@ def test_next_rows_pass_buffers_that_fit(monkeypatch):
     monkeypatch.setattr(fq, "_stream", lambda stream=None: None)
     groups = bench.build_next_ops(fq, synthetic, torch, dev="cpu")
     ops = [op for g in groups.values() for op in g]
-    assert [op.name for op in ops] == ["sr.fake_quant_int8", "sr.fp8_quantize_e4m3", "sr.fp8_quantize_e5m2",
+    assert [op.name for op in ops] == ["tensor.params_int8_sym", "tensor.fake_quant_int8", "sr.fake_quant_int8", "sr.fp8_quantize_e4m3", "sr.fp8_quantize_e5m2",
                                        "qat.step_int8_sym", "qat.step_fp8_e4m3", "cols.int8_sym", "cols.int4_affine",
                                        "percentile.tensor_2^20", "percentile.weights_2^24",
                                        "groups.f32_int4_g128", "groups.f32_int8_g32", "groups.bf16_int8_g128",
@@ -76,7 +76,7 @@ def test_next_rows_pass_buffers_that_fit(monkeypatch):
     before = len(recorder.calls)
     for op in ops:
         op.fn()
-    assert recorder.calls[before:] == ["fq_fake_quant_int_tensor_sr", "fq_fp8_quantize_sr", "fq_fp8_quantize_sr",
+    assert recorder.calls[before:] == ["fq_tensor_params_int", "fq_fake_quant_int_tensor", "fq_fake_quant_int_tensor_sr", "fq_fp8_quantize_sr", "fq_fp8_quantize_sr",
                                        "fq_qat_step_int", "fq_qat_step_fp8", "fq_quant_cols", "fq_quant_cols",
                                        "fq_tensor_params_percentile", "fq_tensor_params_percentile",
                                        "fq_quant_groups", "fq_quant_groups", "fq_quant_groups",

@@ -46,6 +46,7 @@ def check_tensor(fq, orc, x_t, bits, scheme, g_t=None, what=""):
         assert to_np(codes)[-1] & 0xF == 0, what + " pad nibble"
     assert_f32(to_np(fqv), rf, what + " fq")
     assert_f32(to_np(deq), orc.dequantize_int(rc, float(ref["scale"]), ref["zp"]), what + " dequant")
+    check_calibrate_fake_quant(fq, x_t, bits, scheme, ref, rc, rf, what)
     if g_t is not None:
         bounds = params.view(torch.float32)[2:4]
         gi = fq.ste_backward(g_t, x_t, bounds)
@@ -55,6 +56,36 @@ def check_tensor(fq, orc, x_t, bits, scheme, g_t=None, what=""):
         want = orc.ste_backward(to_np(g_t), x, float(ref["lo"]), float(ref["hi"]))
         assert_bits(to_np(gi), want, what + " ste")
         assert_bits(to_np(gi2), want, what + " ste reversed bounds")
+
+
+def check_calibrate_fake_quant(fq, x_t, bits, scheme, ref, rc, rf, what):
+    """The one-call calibration + fake-quant against the oracle's two steps."""
+    n = x_t.numel()
+    params, codes, fqv, flags = fq.calibrate_fake_quant_int_tensor(x_t, bits, scheme)
+    torch.cuda.synchronize()
+    s, zp, lo, hi = fq.params_fields(params)
+    assert_bits(np.float32([s, lo, hi]), np.float32([ref["scale"], ref["lo"], ref["hi"]]), what + " one-call params")
+    assert zp == ref["zp"], what + " one-call zp"
+    assert int(flags.item()) == ref["flags"], what + " one-call flags"
+    got_codes = to_np(codes) if bits == 8 else unpack_nibbles(to_np(codes), n)
+    assert_bits(got_codes.astype(np.int8), rc, what + " one-call codes")
+    if bits == 4 and n % 2:
+        assert to_np(codes)[-1] & 0xF == 0, what + " one-call pad nibble"
+    assert_f32(to_np(fqv), rf, what + " one-call fq")
+
+
+@pytest.mark.parametrize("n", [(1 << 22) - 5, 1 << 22, (1 << 22) + 4, (1 << 22) + 8197])
+def test_one_call_fold_boundary(fqlib, orc, n):
+    """Around the largest tensor whose fake-quant blocks fold the reduction
+    partials themselves (512 partials of 8192 elements): that path at and below
+    it, the two-call sequence above."""
+    x, _ = synthetic.tensor_inputs(n=n, device="cuda", seed=n % 1000)
+    xn = to_np(x)
+    for bits, scheme in [(8, 0), (4, 1)]:
+        log(f"one-call boundary n={n} bits={bits} scheme={scheme}")
+        ref = orc.tensor_params_int(xn, bits, scheme)
+        rc, rf = orc.fake_quant_int(xn, bits, scheme, float(ref["scale"]), ref["zp"])
+        check_calibrate_fake_quant(fqlib, x, bits, scheme, ref, rc, rf, f"boundary {n}")
 
 
 @pytest.mark.parametrize("bits,scheme", [(8, 0), (8, 1), (4, 0), (4, 1)])
@@ -136,6 +167,10 @@ def test_deterministic(fqlib):
         params, _ = fqlib.params_int(x, 8, 1)
         codes, fqv = fqlib.fake_quant_int_tensor(x, params, 8, 1)
         outs.append((params.clone(), codes.clone(), fqv.clone()))
+    for _ in range(2):
+        params, codes, fqv, _ = fqlib.calibrate_fake_quant_int_tensor(x, 8, 1)
+        outs.append((params.clone(), codes.clone(), fqv.clone()))
     torch.cuda.synchronize()
-    for a, b in zip(outs[0], outs[1]):
-        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
