@@ -98,3 +98,34 @@ def test_mx_drawn(fqlib, orc, rows, cols, bf16, log_mag, seed):
     assert_bits(to_np(q), ref["q"], "q")
     assert_bits(to_np(e8), ref["e8m0"], "e8m0")
     assert_f32(to_np(fqv), ref["fq"], "fq")
+
+
+@SETTINGS
+@given(n=st.integers(1, 200000), bits=st.sampled_from([4, 8]), scheme=st.sampled_from([0, 1]),
+       log_mag=st.floats(-30, 30), seed=st.integers(0, 2**31), specials=st.booleans(),
+       offset=st.integers(0, 3))
+def test_tensor_one_call_drawn(fqlib, orc, n, bits, scheme, log_mag, seed, specials, offset):
+    """Per-tensor calibration + fake-quant in one call (the two-launch fold path for
+    aligned buffers, the two calls for offset views) against the oracle."""
+    log(f"hypothesis tensor one-call n={n} bits={bits} scheme={scheme} seed={seed} offset={offset}")
+    x = draw_array(n, log_mag, seed, specials)
+    buf = torch.zeros(n + 4, dtype=torch.float32, device="cuda")
+    buf[offset:offset + n] = torch.from_numpy(x).cuda()
+    xt = buf[offset:offset + n]
+    params, codes, fqv, flags = fqlib.calibrate_fake_quant_int_tensor(xt, bits, scheme)
+    torch.cuda.synchronize()
+    ref = orc.tensor_params_int(x, bits, scheme)
+    rc, rf = orc.fake_quant_int(x, bits, scheme, float(ref["scale"]), ref["zp"])
+    s, zp, lo, hi = fqlib.params_fields(params)
+    assert_bits(np.float32([s, lo, hi]), np.float32([ref["scale"], ref["lo"], ref["hi"]]), "params")
+    assert zp == ref["zp"]
+    assert int(flags.item()) == ref["flags"]
+    c = to_np(codes)
+    if bits == 4:
+        p = c.astype(np.uint8)
+        hi_n, lo_n = (p >> 4).astype(np.int16), (p & 0xF).astype(np.int16)
+        u = np.empty(2 * p.size, np.int16)
+        u[0::2], u[1::2] = hi_n, lo_n
+        c = np.where(u >= 8, u - 16, u)[:n]
+    assert_bits(c.astype(np.int8), rc, "codes")
+    assert_f32(to_np(fqv), rf, "fq")
