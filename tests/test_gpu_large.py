@@ -299,6 +299,37 @@ def test_cols_past_2_31(fqlib, orc, big):
         del r
 
 
+def test_cols_strip_past_2_31(fqlib, orc, big):
+    """The one-pass per-column kernel (4096 rows, 32776 strips of 16 columns, a
+    multiple of the eight XCDs) on 2^31 + 524288 elements; the planted maximum,
+    NaN and -Inf sit in its last row, past 2^31."""
+    rows, cols3 = 4096, 16 * 32776
+    assert I_NINF < rows * cols3 <= N
+    x3 = big[:rows * cols3].view(rows, cols3)
+    rng = np.random.default_rng(11)
+    cols = np.unique(np.concatenate([[0, 1, 15, 16, cols3 - 1, I_MAX % cols3, I_NAN % cols3, I_NINF % cols3],
+                                     rng.integers(0, cols3, 8)]))
+    ct = torch.from_numpy(cols).cuda()
+    xs = np.ascontiguousarray(to_np(x3.index_select(1, ct)))
+    for bits, scheme in ((8, 1), (4, 0)):
+        log(f"large cols strip bits={bits} scheme={scheme}")
+        r = fqlib.quant_cols(x3, bits, scheme)
+        ref = orc.quant_cols(xs, bits, scheme)
+        assert_bits(to_np(r["scale"])[cols], ref["scale"], "strip column scales")
+        assert_bits(to_np(r["zp"])[cols], ref["zp"], "strip column zero-points")
+        if bits == 8:
+            assert_bits(to_np(r["codes"].index_select(1, ct)), ref["codes"], "strip column codes")
+        else:
+            got = to_np(r["codes"].index_select(1, torch.from_numpy(cols // 2).cuda()))
+            got = np.where(cols % 2 == 0, got >> 4, got & 0xF).astype(np.uint8)
+            j = np.arange(len(cols))
+            want = np.where(j % 2 == 0, ref["codes"][:, j // 2] >> 4, ref["codes"][:, j // 2] & 0xF).astype(np.uint8)
+            assert_bits(got, want, "strip column int4 codes")
+        assert_f32(to_np(r["fq"].index_select(1, ct)), ref["fq"], "strip column fake-quant")
+        assert int(r["flags"].item()) == ref["flags"], "strip flags"
+        del r
+
+
 def test_qat_past_2_31(fqlib, orc, big):
     # the update moves no element by more than about lr, so the planted extremes
     # stay the extremes of the updated master and a sample holding them calibrates
