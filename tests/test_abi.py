@@ -135,6 +135,19 @@ def test_argument_checks(fq):
     assert L.fq_q4dq_dequantize(P, P, None, 8, P, None) == fq.E_INVALID
     assert L.fq_mxfp8_rows(P, 1, 1, 32, None, P, None, None) == fq.E_INVALID
     assert L.fq_mxfp8_rows(P, 1, 0, 32, P, P, None, None) == fq.E_INVALID
+    # the one-call calibration + fake-quant checks the union of its two calls' arguments
+    C = L.fq_calibrate_fake_quant_int_tensor
+    assert C(P, 8, 3, 0, P, 1 << 20, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert C(P, 8, 8, 2, P, 1 << 20, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert C(P, 0, 8, 0, P, 1 << 20, P, P, P, None, None) == fq.E_INVALID  # empty
+    assert C(None, 8, 8, 0, P, 1 << 20, P, P, P, None, None) == fq.E_INVALID
+    assert C(P, 8, 8, 0, None, 1 << 20, P, P, P, None, None) == fq.E_INVALID  # no workspace
+    assert C(P, 8, 8, 0, P, 0, P, P, P, None, None) == fq.E_INVALID  # workspace too small
+    assert C(P, 8, 8, 0, P + 4, 1 << 20, P, P, P, None, None) == fq.E_INVALID  # workspace misaligned
+    assert C(P, 8, 8, 0, P, 1 << 20, None, P, P, None, None) == fq.E_INVALID  # no params
+    assert C(P, 8, 8, 0, P, 1 << 20, P, None, None, None, None) == fq.E_INVALID  # no output
+    assert C(P + 1, 8, 8, 0, P, 1 << 20, P, P, P, None, None) == fq.E_INVALID  # misaligned f32
+    assert C(P, 8, 8, 0, P, 1 << 20, P, P, P + 2, None, None) == fq.E_INVALID  # misaligned fq
     # stochastic rounding entry points share the checks of their nearest-rounding twins
     assert L.fq_fake_quant_int_tensor_sr(P, 8, 3, 0, P, 1, 0, P, P, None) == fq.E_UNSUPPORTED
     assert L.fq_fake_quant_int_tensor_sr(P, 8, 8, 2, P, 1, 0, P, P, None) == fq.E_UNSUPPORTED
