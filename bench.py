@@ -301,6 +301,19 @@ def ops_next_cols(fq, syn, torch, dev):
                       lambda bits=bits, scheme=scheme, codes=codes: fq.fq_quant_cols(
                           w, fq.F32, r, c, bits, scheme, ws, wsb, codes, fqo, scale, zp, flags),
                       4 * r * c + nb + 4 * r * c + 8 * c))
+    # per-channel int8 of a bf16 activation: 4096 tokens of the [*, 8192] ReLU
+    # workload with its outlier channels
+    ra, ca = 4096, syn.FULL["rows_bf16"]["cols"]
+    a = syn.rows_bf16_inputs(ra, ca, device=dev)
+    wsba = fq.fq_cols_workspace_bytes(ra, ca)
+    wsa = torch.empty(max(wsba // 4, 1), dtype=torch.float32, device=dev)
+    fqa = torch.empty(ra * ca, dtype=torch.float32, device=dev)
+    sca = torch.empty(ca, dtype=torch.float32, device=dev)
+    zpa = torch.empty(ca, dtype=torch.int32, device=dev)
+    ca8 = torch.empty(ra * ca, dtype=torch.uint8, device=dev)
+    ops.append(Op("cols.bf16_int8_affine", "k_cols_minmax+k_cols_fold+k_cols_quant",
+                  lambda: fq.fq_quant_cols(a, fq.BF16, ra, ca, 8, fq.AFFINE, wsa, wsba, ca8, fqa, sca, zpa, flags),
+                  2 * ra * ca + ra * ca + 4 * ra * ca + 8 * ca))
     return ops
 
 

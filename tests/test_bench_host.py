@@ -70,6 +70,7 @@ def test_next_rows_pass_buffers_that_fit(monkeypatch):
     ops = [op for g in groups.values() for op in g]
     assert [op.name for op in ops] == ["tensor.params_int8_sym", "tensor.fake_quant_int8", "sr.fake_quant_int8", "sr.fp8_quantize_e4m3", "sr.fp8_quantize_e5m2",
                                        "qat.step_int8_sym", "qat.step_fp8_e4m3", "cols.int8_sym", "cols.int4_affine",
+                                       "cols.bf16_int8_affine",
                                        "percentile.tensor_2^20", "percentile.weights_2^24",
                                        "groups.f32_int4_g128", "groups.f32_int8_g32", "groups.bf16_int8_g128",
                                        "block.mxfp4_e2m1", "block.mxfp6_e2m3", "block.nvfp4"]
@@ -77,7 +78,7 @@ def test_next_rows_pass_buffers_that_fit(monkeypatch):
     for op in ops:
         op.fn()
     assert recorder.calls[before:] == ["fq_tensor_params_int", "fq_fake_quant_int_tensor", "fq_fake_quant_int_tensor_sr", "fq_fp8_quantize_sr", "fq_fp8_quantize_sr",
-                                       "fq_qat_step_int", "fq_qat_step_fp8", "fq_quant_cols", "fq_quant_cols",
+                                       "fq_qat_step_int", "fq_qat_step_fp8", "fq_quant_cols", "fq_quant_cols", "fq_quant_cols",
                                        "fq_tensor_params_percentile", "fq_tensor_params_percentile",
                                        "fq_quant_groups", "fq_quant_groups", "fq_quant_groups",
                                        "fq_mx_rows", "fq_mx_rows", "fq_nvfp4"]

@@ -95,6 +95,20 @@ def test_strip_path_shapes(fqlib, orc, shape):
         check_cols(fqlib, orc, w, bits, scheme, f"strip {shape}")
 
 
+# bf16 at the row counts the fp32 strip kernel takes (bf16 keeps the
+# three-launch path: a bf16 strip kernel measured slower), with 4096 or more
+# columns, a column count that is not a multiple of 256, a partial 256-row load
+STRIP_SHAPES_BF16 = [(1025, 4096), (4096, 4128), (2500, 8192), (4095, 4096)]
+
+
+@pytest.mark.parametrize("shape", STRIP_SHAPES_BF16)
+def test_strip_path_shapes_bf16(fqlib, orc, shape):
+    rows, cols = shape
+    w = synthetic.rows_f32_inputs(rows, cols, device="cuda", seed=rows + cols).to(torch.bfloat16)
+    for bits, scheme in ((8, 0), (8, 1), (4, 0), (4, 1)):
+        check_cols(fqlib, orc, w, bits, scheme, f"bf16 {shape}")
+
+
 def test_strip_special_columns(fqlib, orc):
     """Special columns spread over several strips of the one-pass kernel, with the
     wave-uniform fast path taken by some strips and not by others."""
@@ -116,3 +130,8 @@ def test_strip_special_columns(fqlib, orc):
     for bits in (8, 4):
         for scheme in (0, 1):
             check_cols(fqlib, orc, xt, bits, scheme, "strip special columns")
+    # the same columns in bf16, 4096 wide
+    xb = torch.from_numpy(np.concatenate([x, x[:, ::-1]], axis=1).copy()).cuda().to(torch.bfloat16)
+    for bits in (8, 4):
+        for scheme in (0, 1):
+            check_cols(fqlib, orc, xb, bits, scheme, "bf16 special columns")
