@@ -11,6 +11,8 @@
 // the whole tensor (many short workgroups sweeping memory in order stream best on
 // MI355X).  The last n % 4 elements (and every chunk when a buffer is not
 // vector-aligned) go through the scalar form of the same chunk code.
+#include <atomic>
+
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -508,6 +510,35 @@ int tensor_amax(const float* x, int64_t n, void* workspace, hipStream_t stream) 
 }  // namespace fqh
 
 // ---------------------------------------------------------------------------
+// Static device scratch of fq_calibrate_fake_quant_int_tensor_noalloc: the
+// reduction partials of one call (one 16-byte record per first-pass block, at
+// most kMaxReduceBlocks of them for any n, so every n >= 1 fits).  Each GPU holds
+// its own copy of the array from module load until the process ends.  Host code
+// never names the array itself: its device address is looked up once per device
+// and kept in scratch_addr.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)fqh::kMaxReduceBlocks * sizeof(float4);
+static_assert(kScratchBytes == FQ_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) float4 scratch[fqh::kMaxReduceBlocks];
+
+namespace {
+std::atomic<void*> scratch_addr[fqh::kMaxDevices];
+
+// Device address of `scratch` on the current device, or nullptr when it cannot
+// be had (device id beyond the cache, lookup failed).  The lookup is idempotent,
+// so threads racing on a device's first call store the same address.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= fqh::kMaxDevices) return nullptr;
+    void* p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
 extern "C" {
@@ -571,6 +602,21 @@ int fq_calibrate_fake_quant_int_tensor(const float* x, int64_t n, int bits, int 
     else
         k_fq_int_tensor_fold<4><<<Q, kB, 0, stream>>>(x, n, aff, (const float4*)workspace, (int)G, params, cd, fq, flags);
     return fqh::launched();
+}
+
+int fq_calibrate_fake_quant_int_tensor_noalloc(const float* x, int64_t n, int bits, int scheme,
+                                               fq_int_params* params, void* codes, float* fq, uint32_t* flags,
+                                               hipStream_t stream) {
+    // every argument check of the call below, before the first HIP call
+    if (!fqh::valid_bits(bits) || !fqh::valid_scheme(scheme)) return FQ_E_UNSUPPORTED;
+    if (!x || n < 1 || !params || (!codes && !fq)) return FQ_E_INVALID;
+    if (!fqh::aligned(params, 4) || !fqh::aligned(flags, 4) || !fqh::aligned(x, 4) || !fqh::aligned(fq, 4))
+        return FQ_E_INVALID;
+    if (fq_workspace_bytes(n) > kScratchBytes) return FQ_E_INVALID;  // beyond the static scratch
+    void* ws = scratch_ptr();
+    if (!ws) return FQ_E_HIP;
+    return fq_calibrate_fake_quant_int_tensor(x, n, bits, scheme, ws, kScratchBytes, params, codes, fq, flags,
+                                              stream);
 }
 
 int fq_dequantize_int_tensor(const void* codes, int64_t n, int bits, const fq_int_params* params,

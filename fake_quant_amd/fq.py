@@ -65,6 +65,7 @@ _SIGS = {
     "fq_tensor_params_int": (_INT, [_P, _I64, _INT, _INT, _P, _SZ, _P, _P, _P]),
     "fq_fake_quant_int_tensor": (_INT, [_P, _I64, _INT, _INT, _P, _P, _P, _P]),
     "fq_calibrate_fake_quant_int_tensor": (_INT, [_P, _I64, _INT, _INT, _P, _SZ, _P, _P, _P, _P, _P]),
+    "fq_calibrate_fake_quant_int_tensor_noalloc": (_INT, [_P, _I64, _INT, _INT, _P, _P, _P, _P, _P]),
     "fq_dequantize_int_tensor": (_INT, [_P, _I64, _INT, _P, _P, _P]),
     "fq_ste_backward": (_INT, [_P, _I64, _P, _I64, _P, _P, _P]),
     "fq_quant_rows": (_INT, [_P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P]),
@@ -205,6 +206,18 @@ def fq_calibrate_fake_quant_int_tensor(x, n, bits, scheme, workspace, workspace_
     _check(nm, _lib.fq_calibrate_fake_quant_int_tensor(_ptr(x), n, bits, scheme, _ptr(workspace), workspace_bytes,
                                                        _ptr(params), _ptr(codes), _ptr(fq), _ptr(flags),
                                                        _stream(stream)))
+
+
+def fq_calibrate_fake_quant_int_tensor_noalloc(x, n, bits, scheme, params, codes=None, fq=None, flags=None,
+                                               stream=None):
+    nm = "fq_calibrate_fake_quant_int_tensor_noalloc"
+    _need(nm, "x", x, 4 * n)
+    _need(nm, "params", params, 16)
+    _need(nm, "codes", codes, _codes_bytes(n, bits))
+    _need(nm, "fq", fq, 4 * n)
+    _need(nm, "flags", flags, 4)
+    _check(nm, _lib.fq_calibrate_fake_quant_int_tensor_noalloc(_ptr(x), n, bits, scheme, _ptr(params), _ptr(codes),
+                                                               _ptr(fq), _ptr(flags), _stream(stream)))
 
 
 def fq_cols_workspace_bytes(rows, cols) -> int:

@@ -137,6 +137,27 @@ int fq_calibrate_fake_quant_int_tensor(const float* x, int64_t n, int bits, int 
                                       size_t workspace_bytes, fq_int_params* params, void* codes, float* fq,
                                       uint32_t* flags, hipStream_t stream);
 
+/* fq_calibrate_fake_quant_int_tensor without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments minus
+ * workspace / workspace_bytes; same results, bit for bit, and the same launches.
+ * The reduction partials go to a static device array inside libfq.so of
+ * FQ_NOALLOC_SCRATCH_BYTES (256 KiB) that each GPU holds from module load until
+ * the process ends; every n >= 1 fits in it (the first pass never makes more
+ * than 16384 partials), and a tensor that needed more would be refused with
+ * FQ_E_INVALID.  The call allocates nothing and calls no allocating routine.
+ * Its first call on a device looks the array's device address up
+ * (hipGetSymbolAddress) and keeps it; a caller about to capture a graph makes
+ * one call before capturing.  FQ_E_HIP if the lookup fails or the device id is
+ * 64 or more.  All calls on one GPU share that GPU's array: calls that may
+ * overlap on one GPU (several streams, several host threads) race on it and
+ * must be serialised by the caller.  Nothing in the array needs to start at
+ * zero: every launch writes the partials it later reads. */
+#define FQ_NOALLOC_SCRATCH_BYTES (256u * 1024u)
+int fq_calibrate_fake_quant_int_tensor_noalloc(const float* x, int64_t n, int bits, int scheme,
+                                               fq_int_params* params, void* codes, float* fq, uint32_t* flags,
+                                               hipStream_t stream);
+
 /* [QAT] dequant(q) = (q - zero_point) * scale over stored codes (layout as
  * fq_fake_quant_int_tensor's `codes`). */
 int fq_dequantize_int_tensor(const void* codes, int64_t n, int bits, const fq_int_params* params,

@@ -10,6 +10,7 @@
 """
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -42,7 +43,7 @@ def header_define(name):
 
 def test_exports_every_declared_symbol(fq):
     decl = declared_functions()
-    assert len(decl) == 28
+    assert len(decl) == 29
     for name in decl:
         assert hasattr(fq.lib(), name), name
     assert sorted(fq.EXPORTS) == decl
@@ -127,6 +128,17 @@ def test_argument_checks(fq):
     assert L.fq_quant_rows(P, 0, 4, 4, 8, 0, P, P, None, P, None, None) == fq.E_INVALID
     assert L.fq_quant_rows(P + 1, 0, 4, 4, 8, 0, P, P, P, P, None, None) == fq.E_INVALID  # misaligned f32
     assert L.fq_fp8_tensor_scale(P, 8, P, 1 << 20, None, None, None, None) == fq.E_INVALID
+    # the workspace-free calibration + fake-quant: every argument error before any HIP call
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 3, 0, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 8, 2, P, P, P, None, None) == fq.E_UNSUPPORTED
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 0, 8, 0, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(None, 8, 8, 0, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 8, 0, None, P, P, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 8, 0, P, None, None, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 8, 0, P + 2, P, P, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P + 1, 8, 8, 0, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 8, 0, P, P, P + 2, None, None) == fq.E_INVALID
+    assert L.fq_calibrate_fake_quant_int_tensor_noalloc(P, 8, 8, 0, P, P, P, P + 1, None) == fq.E_INVALID
     assert L.fq_fp8_quantize(P, 8, 0, P, None, None, None) == fq.E_INVALID
     assert L.fq_fp8_quantize(P, 8, 0, None, P, P, None) == fq.E_INVALID
     assert L.fq_fp8_dequantize(P, 0, 0, P, P, None) == fq.E_INVALID
@@ -241,3 +253,15 @@ def test_oracle_and_product_share_no_code():
         text = open(os.path.join(ROOT, "oracle", p)).read()
         assert "fake_quant_amd" not in text and "libfq" not in text and "fq.h" not in text, p
         assert "fqk::" not in text and "fq_device" not in text, p
+
+
+def test_library_imports_no_allocator(fq):
+    """libfq.so never allocates, frees or clears device memory itself (callers own
+    every buffer; the workspace-free entry point uses a static device array): no
+    HIP allocator or memset routine is among its undefined dynamic symbols."""
+    lib = os.path.join(ROOT, "fake_quant_amd", "libfq.so")
+    res = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True, check=True)
+    syms = [ln.split()[-1].split("@")[0] for ln in res.stdout.splitlines() if ln.strip()]
+    assert "hipLaunchKernel" in syms
+    bad = [s for s in syms if re.match(r"hip(Ext)?(Malloc|Free|HostAlloc|HostMalloc|MemAlloc|Memset|MallocAsync)", s)]
+    assert bad == []
