@@ -27,7 +27,10 @@ workloads' input sizes, under `by_size`); `next_rows`
 times the rows beyond the step (the per-tensor calibration and fake-quant as two
 separate calls, stochastic rounding, the QAT optimizer step, per-column,
 percentile and group-wise calibration, the FP4 / FP6 block formats)
-the same ways, outside `value`; `cpu_baseline` is the CPU oracle on a bounded sample of the same work.
+the same ways, outside `value`; `cpu_baseline` is the CPU oracle over every step
+workload at full size on the host's cores (the per-tensor and per-row ones also on
+one thread), and `parity` compares every step op's GPU outputs with its results
+(`value` is null when any differs).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -91,8 +94,12 @@ def copy_reference(torch):
 
 
 class Op:
-    def __init__(self, name, kernel, fn, nbytes):
+    """One timed call: `fn` enqueues it, `nbytes` are its algorithmic bytes; `ins`
+    and `outs` name its GPU input and output tensors (the parity check reads
+    them after the timings)."""
+    def __init__(self, name, kernel, fn, nbytes, ins=None, outs=None):
         self.name, self.kernel, self.fn, self.nbytes = name, kernel, fn, nbytes
+        self.ins, self.outs = ins or {}, outs or {}
 
 
 def ops_tensor(fq, syn, torch, dev):
@@ -111,8 +118,9 @@ def ops_tensor(fq, syn, torch, dev):
     return [
         Op("tensor.calibrate_fake_quant_int8", "k_reduce_partial+k_fq_int_tensor_fold",
            lambda: fq.fq_calibrate_fake_quant_int_tensor(x, n, 8, fq.SYM, ws, wsb, params, codes, fqo, flags),
-           4 * n + 16 + n + 4 * n),
-        Op("tensor.ste_backward", "k_ste", lambda: fq.fq_ste_backward(g, n, x, n, bounds, gin), 12 * n),
+           4 * n + 16 + n + 4 * n, ins=dict(x=x), outs=dict(params=params, codes=codes, fq=fqo, flags=flags)),
+        Op("tensor.ste_backward", "k_ste", lambda: fq.fq_ste_backward(g, n, x, n, bounds, gin), 12 * n,
+           ins=dict(x=x, g=g), outs=dict(grad_in=gin)),
     ]
 
 
@@ -144,7 +152,8 @@ def op_rows_f32(fq, torch, w, r, c, bits, scheme, sname, dev):
     fl = torch.zeros(1, dtype=torch.int32, device=dev)
     return Op(f"rows_f32.int{bits}_{sname}", "k_rows_wg",
               lambda: fq.fq_quant_rows(w, fq.F32, r, c, bits, scheme, codes, fqo, sc, zp, fl),
-              4 * r * c + cb + 4 * r * c + 8 * r)
+              4 * r * c + cb + 4 * r * c + 8 * r, ins=dict(x=w),
+              outs=dict(codes=codes, fq=fqo, scale=sc, zp=zp, flags=fl))
 
 
 def ops_rows_f32(fq, syn, torch, dev):
@@ -160,9 +169,9 @@ def ops_fp8_format(fq, torch, x, n, scales, fmt, fname, dev):
     deq = torch.empty(n, dtype=torch.float32, device=dev)
     s = scales[fmt:fmt + 1]
     return [Op(f"fp8.quantize_{fname}", "k_fp8_quant", lambda: fq.fq_fp8_quantize(x, n, fmt, s, q, fqo),
-               4 * n + n + 4 * n),
+               4 * n + n + 4 * n, ins=dict(x=x), outs=dict(q=q, fq=fqo)),
             Op(f"fp8.dequantize_{fname}", "k_fp8_dequant_w", lambda: fq.fq_fp8_dequantize(q, n, fmt, s, deq),
-               n + 4 * n)]
+               n + 4 * n, outs=dict(out=deq))]
 
 
 def ops_fp8(fq, syn, torch, dev):
@@ -173,7 +182,8 @@ def ops_fp8(fq, syn, torch, dev):
     scales = torch.empty(2, dtype=torch.float32, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     ops = [Op("fp8.tensor_scale", "k_reduce_partial+k_fp8_scale_final",
-              lambda: fq.fq_fp8_tensor_scale(x, n, ws, wsb, scales[0:1], scales[1:2], flags), 4 * n + 8)]
+              lambda: fq.fq_fp8_tensor_scale(x, n, ws, wsb, scales[0:1], scales[1:2], flags), 4 * n + 8,
+              ins=dict(x=x), outs=dict(scales=scales, flags=flags))]
     for fmt, fname in ((fq.E4M3, "e4m3"), (fq.E5M2, "e5m2")):
         ops += ops_fp8_format(fq, torch, x, n, scales, fmt, fname, dev)
     return ops
@@ -192,9 +202,10 @@ def ops_q4dq(fq, syn, torch, dev):
     return [
         Op("q4dq.quantize_recon", "k_q4dq_full",
            lambda: fq.fq_q4dq_quantize(x, n, packed, qs, sup, None, recon, flags),
-           4 * n + npk + nb + 4 * ns + 4 * n),
+           4 * n + npk + nb + 4 * ns + 4 * n, ins=dict(x=x),
+           outs=dict(packed=packed, qscale=qs, super=sup, recon=recon, flags=flags)),
         Op("q4dq.dequantize", "k_q4dq_dequant_full",
-           lambda: fq.fq_q4dq_dequantize(packed, qs, sup, n, deq), npk + nb + 4 * ns + 4 * n),
+           lambda: fq.fq_q4dq_dequantize(packed, qs, sup, n, deq), npk + nb + 4 * ns + 4 * n, outs=dict(out=deq)),
     ]
 
 
@@ -210,9 +221,10 @@ def ops_rows_bf16(fq, syn, torch, dev):
     return [
         Op("rows_bf16.int8_affine", "k_rows_wg",
            lambda: fq.fq_quant_rows(a, fq.BF16, r, c, 8, fq.AFFINE, codes, None, sc, zp, fl),
-           2 * r * c + r * c + 8 * r),
+           2 * r * c + r * c + 8 * r, ins=dict(x=a), outs=dict(codes=codes, scale=sc, zp=zp, flags=fl)),
         Op("rows_bf16.mxfp8_e4m3", "k_mx_wide",
-           lambda: fq.fq_mxfp8_rows(a, fq.BF16, r, c, q, e8, None), 2 * r * c + r * c + r * c // 32),
+           lambda: fq.fq_mxfp8_rows(a, fq.BF16, r, c, q, e8, None), 2 * r * c + r * c + r * c // 32,
+           ins=dict(x=a), outs=dict(q=q, e8m0=e8)),
     ]
 
 
@@ -426,11 +438,6 @@ def build_ops(fq, syn, torch, only, dev="cuda"):
     return [op for name in WORKLOADS for op in built.get(name, [])]
 
 
-# The oracle runs over the first 1/CPU_SAMPLE_DIV of each large workload (the
-# whole step at 1: about 12 s of single-threaded CPU work).
-CPU_SAMPLE_DIV = 1
-
-
 FLUSH_BYTES = 1 << 30
 COLD_REPS, WARM_REPS, PRE_REPS = 20, 20, 5
 
@@ -511,72 +518,295 @@ def cold_warm(ops, fq, torch, stream, ceiling=True):
     return res, ceiling
 
 
-def cpu_baseline(orc, syn, torch, only):
-    """The oracle, single-threaded, on a bounded sample of every workload."""
-    import numpy as np
-    dev = "cuda"
-    total_bytes, total_s = 0, 0.0
-    parts = []
+def _ranges(n, parts, align=1):
+    """[lo, hi) ranges covering [0, n): at most `parts` of them, every boundary
+    but the last a multiple of `align`."""
+    step = -(-n // max(parts, 1))
+    step = max(align, -(-step // align) * align)
+    return [(lo, min(n, lo + step)) for lo in range(0, n, step)]
 
-    def timed(fn, nbytes):
-        nonlocal total_bytes, total_s
+
+def oracle_threads():
+    """Host cores the oracle leg uses: those this process may run on, at most 16
+    (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class OracleLeg:
+    """Runs the CPU oracle over the step's workloads and checks the GPU outputs
+    against it.  Work is split over `threads` host threads by rows, elements or
+    16384-element super-blocks: every output of the oracle depends only on its
+    own row, element or super-block (the per-tensor reductions are max / min, and
+    the max of the ranges' maxima is the maximum), so the split gives the serial
+    result; the per-tensor and per-row workloads also run on one thread and are
+    compared with the split run.  ctypes releases the GIL around each oracle
+    call, so the threads run in parallel."""
+
+    def __init__(self, orc, threads):
+        from concurrent.futures import ThreadPoolExecutor
+        self.orc, self.threads = orc, threads
+        self.pool = ThreadPoolExecutor(threads)
+        self.times = {}        # op -> dict(bytes, seconds[, seconds_1thread])
+        self.checks = {}       # op -> {output: mismatches}
+        self.serial_same = {}  # op -> split run identical to the single-thread run
+
+    def split(self, n, align, fn, threads=None):
+        T = threads or self.threads
+        rs = _ranges(n, T, align)
+        if T == 1:
+            return [fn(a, b) for a, b in rs]
+        return list(self.pool.map(lambda r: fn(*r), rs))
+
+    def timed(self, op, fn, key="seconds"):
         t0 = time.perf_counter()
-        fn()
-        total_s += time.perf_counter() - t0
-        total_bytes += nbytes
+        out = fn()
+        self.times.setdefault(op.name, dict(bytes=op.nbytes))[key] = time.perf_counter() - t0
+        return out
 
-    def want(w):
-        return only is None or w in only
+    # --- comparisons (the stated bars: bytes and integers bit-exact; binary32
+    # outputs within 1 ulp with +0 == -0 and NaN == NaN; the kernels aim at
+    # bit-exact, which is counted as well) ---
+    def _chunks(self, n, fn):
+        return sum(self.split(n, 1 << 22, fn))
 
-    if want("tensor"):
-        n = syn.FULL["tensor"]["n"]
-        x, g = (t.cpu().numpy() for t in syn.tensor_inputs(n, device=dev))
-        p = {}
-        timed(lambda: p.update(orc.tensor_params_int(x, 8, orc.SYM)), 4 * n)
-        timed(lambda: orc.fake_quant_int(x, 8, orc.SYM, float(p["scale"]), p["zp"]), 9 * n)
-        timed(lambda: orc.ste_backward(g, x, float(p["lo"]), float(p["hi"])), 12 * n)
-        parts.append("tensor: all 2^20")
-    if want("rows_f32"):
-        r, c = syn.FULL["rows_f32"]["rows"], syn.FULL["rows_f32"]["cols"]
-        rs = r // CPU_SAMPLE_DIV
-        w = syn.rows_f32_inputs(r, c, device=dev)[:rs].cpu().numpy()
-        for bits in (8, 4):
-            for scheme in (orc.SYM, orc.AFFINE):
-                cb = rs * c if bits == 8 else rs * ((c + 1) // 2)
-                timed(lambda bits=bits, scheme=scheme: orc.quant_rows(w, bits, scheme), 8 * rs * c + cb + 8 * rs)
-        parts.append(f"rows_f32: {rs} of {r} rows")
-    if want("fp8"):
-        n = syn.FULL["fp8"]["n"]
-        m = n // CPU_SAMPLE_DIV
-        x = syn.fp8_inputs(n, device=dev)[:m].cpu().numpy()
-        amax = [0.0]
-        timed(lambda: amax.__setitem__(0, orc.amax_finite(x)), 4 * m)
-        for fmt in (orc.E4M3, orc.E5M2):
-            s, _ = orc.fp8_scale(float(amax[0]), fmt)
-            qq = {}
-            timed(lambda fmt=fmt, s=s: qq.update(q=orc.fp8_quantize(x, fmt, float(s))[0]), 9 * m)
-            timed(lambda fmt=fmt, s=s: orc.fp8_dequantize(qq["q"], fmt, float(s)), 5 * m)
-        parts.append(f"fp8: first {m} of {n} elements")
-    if want("q4dq"):
-        n = syn.FULL["q4dq"]["n"]
-        m = n // CPU_SAMPLE_DIV
-        x = syn.q4dq_inputs(n, device=dev)[:m].cpu().numpy()
-        res = {}
-        npk, nb, ns = (m + 1) // 2, (m + 63) // 64, (m + 16383) // 16384
-        timed(lambda: res.update(orc.q4dq_quantize(x, want_block_scale=False)), 4 * m + npk + nb + 4 * ns + 4 * m)
-        timed(lambda: orc.q4dq_dequantize(res["packed"], res["qscale"], res["super"], m), npk + nb + 4 * ns + 4 * m)
-        del x, res
-        parts.append(f"q4dq: first {m} of {n} elements")
-    if want("rows_bf16"):
-        r, c = syn.FULL["rows_bf16"]["rows"], syn.FULL["rows_bf16"]["cols"]
-        rs = r // CPU_SAMPLE_DIV
-        a = syn.bf16_bits(syn.rows_bf16_inputs(r, c, device=dev)[:rs])
-        timed(lambda: orc.quant_rows(a, 8, orc.AFFINE, dtype=orc.BF16, want_fq=False), 3 * rs * c + 8 * rs)
-        timed(lambda: orc.mxfp8_rows(a, dtype=orc.BF16, want_fq=False), 3 * rs * c + rs * c // 32)
-        parts.append(f"rows_bf16: {rs} of {r} rows")
-    return dict(value=round(total_bytes / total_s / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample="; ".join(parts) + f" (single-threaded, {total_s:.1f} s of CPU work)",
-                seconds=round(total_s, 3), host=host_cpu())
+    def exact(self, op, what, gpu, ref):
+        import numpy as np
+        a = np.ascontiguousarray(gpu).reshape(-1).view(np.uint8)
+        e = np.ascontiguousarray(ref).reshape(-1).view(np.uint8)
+        if a.size != e.size:
+            bad = -1  # a size mismatch counts as a failure
+        else:
+            bad = self._chunks(a.size, lambda lo, hi: int(np.count_nonzero(a[lo:hi] != e[lo:hi])))
+        self.checks.setdefault(op.name, {})[what] = bad
+
+    def f32(self, op, what, gpu, ref):
+        import numpy as np
+        a = np.ascontiguousarray(gpu, dtype=np.float32).reshape(-1).view(np.uint32)
+        e = np.ascontiguousarray(ref, dtype=np.float32).reshape(-1).view(np.uint32)
+        if a.size != e.size:
+            self.checks.setdefault(op.name, {})[what] = -1
+            return
+
+        def count(lo, hi):
+            x, y = a[lo:hi], e[lo:hi]
+            xn = (x & 0x7FFFFFFF) > 0x7F800000
+            yn = (y & 0x7FFFFFFF) > 0x7F800000
+            diff = ~((x == y) | (xn & yn))
+            idx = np.nonzero(diff)[0]
+            if idx.size == 0:
+                return 0, 0
+            xi, yi = x[idx].astype(np.int64), y[idx].astype(np.int64)
+            ox = np.where(xi >= 1 << 31, (1 << 31) - xi, xi)  # order-preserving, +0 == -0
+            oy = np.where(yi >= 1 << 31, (1 << 31) - yi, yi)
+            far = (xn[idx] != yn[idx]) | (np.abs(ox - oy) > 1)
+            return int(idx.size), int(np.count_nonzero(far))
+
+        rs = self.split(a.size, 1 << 22, count)
+        not_exact, beyond = sum(r[0] for r in rs), sum(r[1] for r in rs)
+        rec = self.checks.setdefault(op.name, {})
+        rec[what] = beyond
+        if not_exact:
+            rec[what + "_not_bit_exact"] = not_exact
+
+    def ok(self, op):
+        return all(v == 0 for k, v in self.checks.get(op.name, {"missing": 1}).items()
+                   if not k.endswith("_not_bit_exact"))
+
+
+def _host(t):
+    return t.detach().cpu().numpy()
+
+
+def oracle_tensor(leg, ops):
+    import numpy as np
+    orc = leg.orc
+    opc, ops_ = ops["tensor.calibrate_fake_quant_int8"], ops["tensor.ste_backward"]
+    x, g = _host(opc.ins["x"]), _host(ops_.ins["g"])
+    n = x.size
+
+    def calibrate_fq(T):
+        p = orc.tensor_params_int(x, 8, orc.SYM)
+        codes, fqv = np.empty(n, np.int8), np.empty(n, np.float32)
+        leg.split(n, 1, lambda a, b: orc.fake_quant_int(x[a:b], 8, orc.SYM, float(p["scale"]), p["zp"],
+                                                         codes=codes[a:b], fq=fqv[a:b]), T)
+        return p, codes, fqv
+
+    def ste(p, T):
+        out = np.empty(n, np.float32)
+        leg.split(n, 1, lambda a, b: orc.ste_backward(g[a:b], x[a:b], float(p["lo"]), float(p["hi"]), out=out[a:b]), T)
+        return out
+
+    p, codes, fqv = leg.timed(opc, lambda: calibrate_fq(leg.threads))
+    p1, codes1, fqv1 = leg.timed(opc, lambda: calibrate_fq(1), key="seconds_1thread")
+    gin = leg.timed(ops_, lambda: ste(p, leg.threads))
+    gin1 = leg.timed(ops_, lambda: ste(p, 1), key="seconds_1thread")
+    leg.serial_same[opc.name] = bool(np.array_equal(codes, codes1) and np.array_equal(fqv.view(np.uint32),
+                                                                                       fqv1.view(np.uint32)))
+    leg.serial_same[ops_.name] = bool(np.array_equal(gin.view(np.uint32), gin1.view(np.uint32)))
+    want = np.array([np.float32(p["scale"]).view(np.int32), p["zp"], np.float32(p["lo"]).view(np.int32),
+                     np.float32(p["hi"]).view(np.int32)], np.int32)
+    leg.exact(opc, "params", _host(opc.outs["params"]), want)
+    leg.exact(opc, "flags", _host(opc.outs["flags"]), np.array([p["flags"]], np.int32))
+    leg.exact(opc, "codes", _host(opc.outs["codes"]), codes)
+    leg.f32(opc, "fq", _host(opc.outs["fq"]), fqv)
+    leg.f32(ops_, "grad_in", _host(ops_.outs["grad_in"]), gin)
+
+
+def oracle_rows_f32(leg, ops):
+    import numpy as np
+    orc = leg.orc
+    names = [k for k in ops if k.startswith("rows_f32.")]
+    x = _host(ops[names[0]].ins["x"])
+    rows, cols = x.shape
+    for name in names:
+        op = ops[name]
+        bits = 8 if "int8" in name else 4
+        scheme = orc.SYM if name.endswith("_sym") else orc.AFFINE
+
+        def run(T, bits=bits, scheme=scheme):
+            cw = cols if bits == 8 else (cols + 1) // 2
+            codes = np.empty((rows, cw), np.int8 if bits == 8 else np.uint8)
+            fqv = np.empty((rows, cols), np.float32)
+            sc, zp = np.empty(rows, np.float32), np.empty(rows, np.int32)
+            fl = leg.split(rows, 1, lambda a, b: orc.quant_rows(x[a:b], bits, scheme, codes=codes[a:b], fq=fqv[a:b],
+                                                                 scale=sc[a:b], zp=zp[a:b])["flags"], T)
+            return codes, fqv, sc, zp, int(np.bitwise_or.reduce(fl))
+
+        codes, fqv, sc, zp, fl = leg.timed(op, lambda: run(leg.threads))
+        r1 = leg.timed(op, lambda: run(1), key="seconds_1thread")
+        leg.serial_same[name] = bool(all(np.array_equal(u.view(np.uint8), v.view(np.uint8))
+                                         for u, v in zip((codes, fqv, sc, zp), r1[:4])) and fl == r1[4])
+        leg.exact(op, "codes", _host(op.outs["codes"]), codes)
+        leg.f32(op, "fq", _host(op.outs["fq"]), fqv)
+        leg.exact(op, "scale", _host(op.outs["scale"]), sc)
+        leg.exact(op, "zp", _host(op.outs["zp"]), zp)
+        leg.exact(op, "flags", _host(op.outs["flags"]), np.array([fl], np.int32))
+
+
+def oracle_fp8(leg, ops):
+    import numpy as np
+    orc = leg.orc
+    ops_ = ops["fp8.tensor_scale"]
+    x = _host(ops_.ins["x"])
+    n = x.size
+
+    def scales():
+        amax = max(leg.split(n, 1, lambda a, b: float(orc.amax_finite(x[a:b]))))
+        return [orc.fp8_scale(amax, fmt) for fmt in (orc.E4M3, orc.E5M2)]
+
+    sc = leg.timed(ops_, scales)
+    leg.exact(ops_, "scales", _host(ops_.outs["scales"]), np.array([sc[0][0], sc[1][0]], np.float32))
+    leg.exact(ops_, "flags", _host(ops_.outs["flags"]), np.array([sc[0][1] | sc[1][1]], np.int32))
+    for fmt, fname in ((orc.E4M3, "e4m3"), (orc.E5M2, "e5m2")):
+        s = float(sc[fmt][0])
+        opq, opd = ops[f"fp8.quantize_{fname}"], ops[f"fp8.dequantize_{fname}"]
+        q, fqv, deq = np.empty(n, np.uint8), np.empty(n, np.float32), np.empty(n, np.float32)
+        leg.timed(opq, lambda: leg.split(n, 1, lambda a, b: orc.fp8_quantize(x[a:b], fmt, s, q=q[a:b], fq=fqv[a:b])))
+        leg.timed(opd, lambda: leg.split(n, 1, lambda a, b: orc.fp8_dequantize(q[a:b], fmt, s, out=deq[a:b])))
+        leg.exact(opq, "q", _host(opq.outs["q"]), q)
+        leg.f32(opq, "fq", _host(opq.outs["fq"]), fqv)
+        leg.f32(opd, "out", _host(opd.outs["out"]), deq)
+        del q, fqv, deq
+
+
+def oracle_q4dq(leg, ops):
+    import numpy as np
+    orc = leg.orc
+    opq, opd = ops["q4dq.quantize_recon"], ops["q4dq.dequantize"]
+    x = _host(opq.ins["x"])
+    n = x.size
+    npk, nb, ns = orc.q4dq_sizes(n)
+    packed, qs = np.empty(npk, np.uint8), np.empty(nb, np.uint8)
+    sup, recon = np.empty(ns, np.float32), np.empty(n, np.float32)
+    SB = 16384  # a super-block: 256 blocks of 64
+
+    def quant(a, b):
+        return orc.q4dq_quantize(x[a:b], want_block_scale=False, packed=packed[a // 2:(b + 1) // 2],
+                                 qscale=qs[a // 64:(b + 63) // 64], sup=sup[a // SB:(b + SB - 1) // SB],
+                                 recon=recon[a:b])["flags"]
+
+    fl = leg.timed(opq, lambda: leg.split(n, SB, quant))
+    deq = np.empty(n, np.float32)
+    leg.timed(opd, lambda: leg.split(n, SB, lambda a, b: orc.q4dq_dequantize(
+        packed[a // 2:(b + 1) // 2], qs[a // 64:(b + 63) // 64], sup[a // SB:(b + SB - 1) // SB], b - a,
+        out=deq[a:b])))
+    leg.exact(opq, "packed", _host(opq.outs["packed"]), packed)
+    leg.exact(opq, "qscale", _host(opq.outs["qscale"]), qs)
+    leg.exact(opq, "super", _host(opq.outs["super"]), sup)
+    leg.exact(opq, "flags", _host(opq.outs["flags"]), np.array([int(np.bitwise_or.reduce(fl))], np.int32))
+    leg.f32(opq, "recon", _host(opq.outs["recon"]), recon)
+    del recon
+    leg.f32(opd, "out", _host(opd.outs["out"]), deq)
+
+
+def oracle_rows_bf16(leg, ops):
+    import numpy as np
+    import torch
+    orc = leg.orc
+    opr, opm = ops["rows_bf16.int8_affine"], ops["rows_bf16.mxfp8_e4m3"]
+    a = _host(opr.ins["x"].view(torch.int16)).view(np.uint16)
+    rows, cols = a.shape
+    codes, sc, zp = np.empty((rows, cols), np.int8), np.empty(rows, np.float32), np.empty(rows, np.int32)
+    fl = leg.timed(opr, lambda: leg.split(rows, 1, lambda lo, hi: orc.quant_rows(
+        a[lo:hi], 8, orc.AFFINE, dtype=orc.BF16, want_fq=False, codes=codes[lo:hi], scale=sc[lo:hi],
+        zp=zp[lo:hi])["flags"]))
+    leg.exact(opr, "codes", _host(opr.outs["codes"]), codes)
+    leg.exact(opr, "scale", _host(opr.outs["scale"]), sc)
+    leg.exact(opr, "zp", _host(opr.outs["zp"]), zp)
+    leg.exact(opr, "flags", _host(opr.outs["flags"]), np.array([int(np.bitwise_or.reduce(fl))], np.int32))
+    q, e8 = np.empty((rows, cols), np.uint8), np.empty((rows, (cols + 31) // 32), np.uint8)
+    leg.timed(opm, lambda: leg.split(rows, 1, lambda lo, hi: orc.mxfp8_rows(
+        a[lo:hi], dtype=orc.BF16, want_fq=False, q=q[lo:hi], e8m0=e8[lo:hi])))
+    leg.exact(opm, "q", _host(opm.outs["q"]), q)
+    leg.exact(opm, "e8m0", _host(opm.outs["e8m0"]), e8)
+
+
+ORACLE = {"tensor": oracle_tensor, "rows_f32": oracle_rows_f32, "fp8": oracle_fp8, "q4dq": oracle_q4dq,
+          "rows_bf16": oracle_rows_bf16}
+SINGLE_THREAD_ROWS = ("tensor", "rows_f32")
+
+
+def cpu_baseline_and_parity(orc, ops):
+    """The oracle over every step workload at full size (about 13 s of CPU work),
+    on the host's cores, and the parity of every step op's GPU outputs against
+    it.  Returns (cpu_baseline, parity)."""
+    leg = OracleLeg(orc, oracle_threads())
+    by_wl = {}
+    for op in ops:
+        by_wl.setdefault(op.name.split(".")[0], {})[op.name] = op
+    for wl, wops in by_wl.items():
+        log(f"oracle + parity: {wl}")
+        ORACLE[wl](leg, wops)
+    leg.pool.shutdown()
+    total_b = sum(t["bytes"] for t in leg.times.values())
+    total_s = sum(t["seconds"] for t in leg.times.values())
+    per_op = {}
+    for name, t in leg.times.items():
+        rec = dict(seconds=round(t["seconds"], 4), gbs=round(t["bytes"] / t["seconds"] / 1e9, 3))
+        if "seconds_1thread" in t:
+            rec.update(seconds_1thread=round(t["seconds_1thread"], 4),
+                       gbs_1thread=round(t["bytes"] / t["seconds_1thread"] / 1e9, 3))
+        per_op[name] = rec
+    per_wl = {}
+    for wl, wops in by_wl.items():
+        b = sum(leg.times[n]["bytes"] for n in wops)
+        sec = sum(leg.times[n]["seconds"] for n in wops)
+        per_wl[wl] = dict(seconds=round(sec, 4), gbs=round(b / sec / 1e9, 3))
+        if wl in SINGLE_THREAD_ROWS:
+            s1 = sum(leg.times[n]["seconds_1thread"] for n in wops)
+            per_wl[wl].update(seconds_1thread=round(s1, 4), gbs_1thread=round(b / s1 / 1e9, 3))
+    cpu = dict(value=round(total_b / total_s / 1e9, 4), unit="GB/s", cores=leg.threads, kind="oracle",
+               sample=f"every step workload at full size ({', '.join(by_wl)}), split over {leg.threads} host "
+                      f"threads by rows, elements or 16384-element super-blocks ({total_s:.1f} s wall); the "
+                      f"per-tensor and per-row workloads also on one thread",
+               seconds=round(total_s, 3), per_workload=per_wl, per_op=per_op,
+               split_equals_serial=all(leg.serial_same.values()), host=host_cpu())
+    parity = dict(ok=all(leg.ok(op) for op in ops),
+                  workloads={wl: all(leg.ok(op) for op in wops.values()) for wl, wops in by_wl.items()},
+                  mismatches=leg.checks,
+                  bar="codes, bytes, nibbles, u8 scales, params and flags bit-exact; float32 outputs within "
+                      "1 ulp (+0 == -0, NaN == NaN), counts of not bit-exact ones kept beside")
+    return cpu, parity
 
 
 def host_cpu():
@@ -716,14 +946,14 @@ def main():
                      for name, nops in build_next_ops(fq, syn, torch, args.only).items()}
         torch.cuda.synchronize()
 
-    cpu = None
+    cpu, parity = None, None
     n_ops = len(ops)
     if not args.no_cpu:
         from oracle import oracle as orc
-        log("timing the CPU oracle on a bounded sample")
-        del ops, dom
-        torch.cuda.empty_cache()
-        cpu = cpu_baseline(orc, syn, torch, args.only)
+        log("the CPU oracle over every step workload, and the parity of the GPU outputs against it")
+        cpu, parity = cpu_baseline_and_parity(orc, ops)
+        if not parity["ok"]:
+            log(f"PARITY FAILED: {parity['mismatches']}")
 
     workloads = "tensor 2^20 f32 int8 calibrate + fake-quant + STE; rows_f32 [4096,4096] int8/int4 sym/affine; fp8 2^26 E4M3/E5M2; " \
                 "q4dq 2^30 f32 4-bit + double-quant; rows_bf16 [16384,8192] per-token int8 + 32-block E4M3/E8M0"
@@ -731,7 +961,8 @@ def main():
         workloads = "only " + ",".join(args.only)
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        # a step whose outputs differ from the oracle's has no valid throughput
+        "value": round(value, 1) if parity is None or parity["ok"] else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -747,6 +978,7 @@ def main():
                    "wall_s_timed": round(t_wall, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "kernels": kernels,
         "per_op_cold_warm": per_op,
         "copy_f32_ceiling": copy_ceiling,

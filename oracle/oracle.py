@@ -124,6 +124,15 @@ def _scalar_out(ctype):
     return ctype()
 
 
+def _out(a, shape, dtype):
+    """A caller's output array (C-contiguous, of this shape and dtype), or a new one."""
+    if a is None:
+        return np.empty(shape, dtype)
+    shape = tuple(shape) if isinstance(shape, (tuple, list)) else (shape,)
+    assert a.dtype == np.dtype(dtype) and a.shape == shape and a.flags["C_CONTIGUOUS"], (a.dtype, a.shape, shape)
+    return a
+
+
 # --- scalar helpers -----------------------------------------------------------
 
 def q_range(bits: int, scheme: int):
@@ -175,10 +184,10 @@ def tensor_params_int(x, bits: int, scheme: int):
                 hi=np.float32(hi.value), flags=flags)
 
 
-def fake_quant_int(x, bits: int, scheme: int, scale: float, zp: int):
+def fake_quant_int(x, bits: int, scheme: int, scale: float, zp: int, codes=None, fq=None):
     x = _f32(x).ravel()
-    codes = np.empty(x.size, np.int8)
-    fq = np.empty(x.size, np.float32)
+    codes = _out(codes, x.size, np.int8)
+    fq = _out(fq, x.size, np.float32)
     lib().orc_fake_quant_int(_ptr(x), x.size, bits, scheme, scale, zp, _ptr(codes), _ptr(fq))
     return codes, fq
 
@@ -190,16 +199,17 @@ def dequantize_int(codes, scale: float, zp: int):
     return out
 
 
-def ste_backward(g, x, b0: float, b1: float):
+def ste_backward(g, x, b0: float, b1: float, out=None):
     g = _f32(g).ravel()
     x = _f32(x).ravel()
     assert g.size == x.size
-    out = np.empty(x.size, np.float32)
+    out = _out(out, x.size, np.float32)
     lib().orc_ste_backward(_ptr(g), _ptr(x), x.size, b0, b1, _ptr(out))
     return out
 
 
-def quant_rows(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True):
+def quant_rows(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True, codes=None, fq=None, scale=None,
+               zp=None):
     """x: [rows, cols] float32 array, or uint16 array of bfloat16 bits (dtype=BF16)."""
     if dtype == BF16:
         x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -207,12 +217,12 @@ def quant_rows(x, bits: int, scheme: int, dtype: int = F32, want_fq: bool = True
         x = _f32(x)
     rows, cols = x.shape
     if bits == 8:
-        codes = np.empty((rows, cols), np.int8)
+        codes = _out(codes, (rows, cols), np.int8)
     else:
-        codes = np.empty((rows, (cols + 1) // 2), np.uint8)
-    fq = np.empty((rows, cols), np.float32) if want_fq else None
-    scale = np.empty(rows, np.float32)
-    zp = np.empty(rows, np.int32)
+        codes = _out(codes, (rows, (cols + 1) // 2), np.uint8)
+    fq = _out(fq, (rows, cols), np.float32) if want_fq else None
+    scale = _out(scale, rows, np.float32)
+    zp = _out(zp, rows, np.int32)
     flags = lib().orc_quant_rows(_ptr(x), dtype, rows, cols, bits, scheme, _ptr(codes), _ptr(fq),
                                  _ptr(scale), _ptr(zp))
     return dict(codes=codes, fq=fq, scale=scale, zp=zp, flags=flags)
@@ -326,17 +336,17 @@ def fp8_scale(amax: float, fmt: int):
     return np.float32(s.value), flags
 
 
-def fp8_quantize(x, fmt: int, scale: float, want_q: bool = True, want_fq: bool = True):
+def fp8_quantize(x, fmt: int, scale: float, want_q: bool = True, want_fq: bool = True, q=None, fq=None):
     x = _f32(x).ravel()
-    q = np.empty(x.size, np.uint8) if want_q else None
-    fq = np.empty(x.size, np.float32) if want_fq else None
+    q = _out(q, x.size, np.uint8) if want_q else None
+    fq = _out(fq, x.size, np.float32) if want_fq else None
     lib().orc_fp8_quantize(_ptr(x), x.size, fmt, scale, _ptr(q), _ptr(fq))
     return q, fq
 
 
-def fp8_dequantize(q, fmt: int, scale: float):
+def fp8_dequantize(q, fmt: int, scale: float, out=None):
     q = np.ascontiguousarray(q, dtype=np.uint8).ravel()
-    out = np.empty(q.size, np.float32)
+    out = _out(out, q.size, np.float32)
     lib().orc_fp8_dequantize(_ptr(q), q.size, fmt, scale, _ptr(out))
     return out
 
@@ -346,39 +356,40 @@ def q4dq_sizes(n: int):
     return (n + 1) // 2, nb, (nb + 255) // 256
 
 
-def q4dq_quantize(x, want_block_scale: bool = True, want_recon: bool = True):
+def q4dq_quantize(x, want_block_scale: bool = True, want_recon: bool = True, packed=None, qscale=None, sup=None,
+                  recon=None):
     x = _f32(x).ravel()
     n = x.size
     npk, nb, ns = q4dq_sizes(n)
-    packed = np.empty(npk, np.uint8)
-    qscale = np.empty(nb, np.uint8)
-    sup = np.empty(ns, np.float32)
+    packed = _out(packed, npk, np.uint8)
+    qscale = _out(qscale, nb, np.uint8)
+    sup = _out(sup, ns, np.float32)
     bs = np.empty(nb, np.float32) if want_block_scale else None
-    recon = np.empty(n, np.float32) if want_recon else None
+    recon = _out(recon, n, np.float32) if want_recon else None
     flags = lib().orc_q4dq_quantize(_ptr(x), n, _ptr(packed), _ptr(qscale), _ptr(sup), _ptr(bs),
                                     _ptr(recon))
     return dict(packed=packed, qscale=qscale, super=sup, block_scale=bs, recon=recon, flags=flags)
 
 
-def q4dq_dequantize(packed, qscale, sup, n: int):
+def q4dq_dequantize(packed, qscale, sup, n: int, out=None):
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     qscale = np.ascontiguousarray(qscale, dtype=np.uint8)
     sup = _f32(sup)
-    out = np.empty(n, np.float32)
+    out = _out(out, n, np.float32)
     lib().orc_q4dq_dequantize(_ptr(packed), _ptr(qscale), _ptr(sup), n, _ptr(out))
     return out
 
 
-def mxfp8_rows(x, dtype: int = BF16, want_fq: bool = True):
+def mxfp8_rows(x, dtype: int = BF16, want_fq: bool = True, q=None, e8m0=None, fq=None):
     if dtype == BF16:
         x = np.ascontiguousarray(x, dtype=np.uint16)
     else:
         x = _f32(x)
     rows, cols = x.shape
     nbr = (cols + 31) // 32
-    q = np.empty((rows, cols), np.uint8)
-    e8 = np.empty((rows, nbr), np.uint8)
-    fq = np.empty((rows, cols), np.float32) if want_fq else None
+    q = _out(q, (rows, cols), np.uint8)
+    e8 = _out(e8m0, (rows, nbr), np.uint8)
+    fq = _out(fq, (rows, cols), np.float32) if want_fq else None
     lib().orc_mxfp8_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(e8), _ptr(fq))
     return dict(q=q, e8m0=e8, fq=fq)
 

@@ -118,3 +118,97 @@ def test_raise_on_flags_maps_bits_to_errors():
     with pytest.raises(fq.FqFlagError, match="Inf or NaN; .*no usable range"):
         fq.raise_on_flags("op", torch.tensor([3], dtype=torch.int32))
     assert issubclass(fq.FqFlagError, fq.FqError)
+
+
+def _fill_with_oracle(ops, orc):
+    """Write into every step op's output tensors what the oracle gives for its
+    inputs, one serial call per op (as a GPU that matches would have)."""
+    import numpy as np
+    by = {op.name: op for op in ops}
+
+    def put(op, key, arr):
+        t = by[op].outs[key]
+        t.view(-1).view(torch.uint8).copy_(torch.from_numpy(np.ascontiguousarray(arr).reshape(-1).view(np.uint8)))
+
+    x = by["tensor.calibrate_fake_quant_int8"].ins["x"].numpy()
+    g = by["tensor.ste_backward"].ins["g"].numpy()
+    p = orc.tensor_params_int(x, 8, orc.SYM)
+    c, f = orc.fake_quant_int(x, 8, orc.SYM, float(p["scale"]), p["zp"])
+    put("tensor.calibrate_fake_quant_int8", "params",
+        np.array([np.float32(p["scale"]).view(np.int32), p["zp"], np.float32(p["lo"]).view(np.int32),
+                  np.float32(p["hi"]).view(np.int32)], np.int32))
+    put("tensor.calibrate_fake_quant_int8", "flags", np.array([p["flags"]], np.int32))
+    put("tensor.calibrate_fake_quant_int8", "codes", c)
+    put("tensor.calibrate_fake_quant_int8", "fq", f)
+    put("tensor.ste_backward", "grad_in", orc.ste_backward(g, x, float(p["lo"]), float(p["hi"])))
+    for name in [k for k in by if k.startswith("rows_f32.")]:
+        w = by[name].ins["x"].numpy()
+        r = orc.quant_rows(w, 8 if "int8" in name else 4, orc.SYM if name.endswith("_sym") else orc.AFFINE)
+        for k in ("codes", "fq", "scale", "zp"):
+            put(name, k, r[k])
+        put(name, "flags", np.array([r["flags"]], np.int32))
+    y = by["fp8.tensor_scale"].ins["x"].numpy()
+    amax = float(orc.amax_finite(y))
+    sc = [orc.fp8_scale(amax, fmt) for fmt in (orc.E4M3, orc.E5M2)]
+    put("fp8.tensor_scale", "scales", np.array([sc[0][0], sc[1][0]], np.float32))
+    put("fp8.tensor_scale", "flags", np.array([sc[0][1] | sc[1][1]], np.int32))
+    for fmt, fname in ((orc.E4M3, "e4m3"), (orc.E5M2, "e5m2")):
+        q, fv = orc.fp8_quantize(y, fmt, float(sc[fmt][0]))
+        put(f"fp8.quantize_{fname}", "q", q)
+        put(f"fp8.quantize_{fname}", "fq", fv)
+        put(f"fp8.dequantize_{fname}", "out", orc.fp8_dequantize(q, fmt, float(sc[fmt][0])))
+    z = by["q4dq.quantize_recon"].ins["x"].numpy()
+    r = orc.q4dq_quantize(z)
+    for k in ("packed", "qscale", "super", "recon"):
+        put("q4dq.quantize_recon", k, r[k])
+    put("q4dq.quantize_recon", "flags", np.array([r["flags"]], np.int32))
+    put("q4dq.dequantize", "out", orc.q4dq_dequantize(r["packed"], r["qscale"], r["super"], z.size))
+    a = synthetic.bf16_bits(by["rows_bf16.int8_affine"].ins["x"])
+    r = orc.quant_rows(a, 8, orc.AFFINE, dtype=orc.BF16, want_fq=False)
+    for k in ("codes", "scale", "zp"):
+        put("rows_bf16.int8_affine", k, r[k])
+    put("rows_bf16.int8_affine", "flags", np.array([r["flags"]], np.int32))
+    m = orc.mxfp8_rows(a, dtype=orc.BF16, want_fq=False)
+    put("rows_bf16.mxfp8_e4m3", "q", m["q"])
+    put("rows_bf16.mxfp8_e4m3", "e8m0", m["e8m0"])
+
+
+def test_oracle_leg_checks_every_output(monkeypatch, orc):
+    """The bench's oracle leg, split over three threads, finds outputs equal to
+    the serial oracle's equal (parity ok, split == serial), and a single flipped
+    byte, a 2-ulp float and a wrong flag word each fail their own workload only."""
+    monkeypatch.setattr(synthetic, "FULL", TINY)
+    recorder = RecordingLib(fq.lib())
+    monkeypatch.setattr(fq, "_lib", recorder)
+    monkeypatch.setattr(fq, "_need", cpu_need)
+    monkeypatch.setattr(fq, "_stream", lambda stream=None: None)
+    monkeypatch.setattr(bench, "oracle_threads", lambda: 3)
+    ops = bench.build_ops(fq, synthetic, torch, None, dev="cpu")
+    assert all(op.outs for op in ops)
+    _fill_with_oracle(ops, orc)
+    cpu, parity = bench.cpu_baseline_and_parity(orc, ops)
+    assert parity["ok"], parity["mismatches"]
+    assert set(parity["workloads"]) == set(bench.WORKLOADS)
+    assert cpu["cores"] == 3 and cpu["split_equals_serial"]
+    assert set(cpu["per_op"]) == {op.name for op in ops}
+    assert all("seconds_1thread" in cpu["per_workload"][w] for w in bench.SINGLE_THREAD_ROWS)
+    by = {op.name: op for op in ops}
+    by["q4dq.quantize_recon"].outs["packed"][17] ^= 1
+    rec = by["fp8.quantize_e5m2"].outs["fq"].view(torch.int32)
+    rec[5] = rec[5] + 2 if rec[5] != 0 else 2
+    by["rows_f32.int4_affine"].outs["flags"][0] ^= 2
+    cpu, parity = bench.cpu_baseline_and_parity(orc, ops)
+    assert not parity["ok"]
+    bad = {w for w, ok in parity["workloads"].items() if not ok}
+    assert bad == {"q4dq", "fp8", "rows_f32"}
+    assert parity["mismatches"]["q4dq.quantize_recon"]["packed"] == 1
+    assert parity["mismatches"]["fp8.quantize_e5m2"]["fq"] == 1
+    assert parity["mismatches"]["rows_f32.int4_affine"]["flags"] == 1
+
+
+def test_ranges_cover_and_align():
+    for n, parts, align in [(1, 16, 1), (20001, 3, 16384), (1 << 20, 16, 1), (4096, 16, 1), (5, 16, 1)]:
+        rs = bench._ranges(n, parts, align)
+        assert rs[0][0] == 0 and rs[-1][1] == n and len(rs) <= parts
+        assert all(a[1] == b[0] for a, b in zip(rs, rs[1:]))
+        assert all(a % align == 0 for a, _ in rs)
