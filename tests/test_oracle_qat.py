@@ -130,3 +130,35 @@ def test_stochastic_view_brackets(orc, bits, scheme):
     rf = orc.qat_step_fp8(w, g, z, z, 0.01, 1, fmt=1, rounding=1, seed=11)
     near = orc.fp8_encode_n(rf["w"], 1)
     assert np.all(np.abs(rf["q"].astype(int) - near.astype(int)) <= 1)
+
+
+def test_page_association_of_the_update(orc):
+    """[QAT] QatOptimizer::step writes v = beta2 v + (1 - beta2) g g,
+    w -= lr weight_decay w and w -= lr m_hat / (sqrt(v_hat) + eps); Rust takes
+    a * b * c and a * b / c left to right.  On inputs where the other grouping
+    rounds differently in binary32, the oracle must give the page's grouping:
+    ((1 - beta2) g) g, (lr wd) w and (lr m_hat) / (sqrt(v_hat) + eps)."""
+    rng = np.random.default_rng(9)
+    n = 200_000
+    g = (rng.standard_normal(n) * np.exp(rng.uniform(-4, 4, n))).astype(np.float32)
+    lr = f32(0.0173)  # not a power of two, so lr * x rounds
+    z = np.zeros(n, np.float32)
+    # from w = 0, m = v = 0 at t = 1 the step itself is the new master (0 - s = -s exactly)
+    w1, m1, v1 = orc.adamw_update(z, g, z, z, float(lr), 1)
+    c2 = f32(1.0) - f32(0.999)
+    page_v, other_v = (c2 * g) * g, c2 * (g * g)
+    assert np.count_nonzero(page_v != other_v) > 1000
+    assert np.array_equal(v1.view(np.uint32), page_v.view(np.uint32))
+    bc1, bc2 = orc.adamw_bias_corrections(0.9, 0.999, 1)
+    m_hat, v_hat = m1 / bc1, v1 / bc2
+    d = np.sqrt(v_hat) + f32(1e-8)
+    page_w, other_w = -((lr * m_hat) / d), -(lr * (m_hat / d))
+    assert np.count_nonzero(page_w != other_w) > 1000
+    assert np.array_equal(w1.view(np.uint32), page_w.view(np.uint32))
+    # decoupled decay alone (zero gradient: m_hat = 0 and the Adam step is 0)
+    w0 = (rng.standard_normal(n) * 3).astype(np.float32)
+    wd = f32(0.0371)
+    wdec, _, _ = orc.adamw_update(w0, z, z, z, float(lr), 1, weight_decay=float(wd))
+    page_d, other_d = w0 - (lr * wd) * w0, w0 - lr * (wd * w0)
+    assert np.count_nonzero(page_d != other_d) > 10  # the subtraction from w absorbs most differences
+    assert np.array_equal(wdec.view(np.uint32), page_d.view(np.uint32))
