@@ -155,10 +155,9 @@ __device__ __forceinline__ void for_each_group(const float* __restrict__ x, int6
 }
 
 // Adds the non-zero counts of an LDS histogram (BINS bins, cnt(b) the count of
-// bin b) to the device histogram g: every add of the thread is issued before any
-// is awaited, and all have returned when this returns -- a count whose add has
-// returned is in device memory, visible to the device-scope loads of the
-// workgroup that selects.
+// bin b) to the device histogram g with agent-scope atomics: every add of the
+// thread is issued before any is awaited.  The selecting workgroup sees them
+// through the release / acquire pair of last_to_finish.
 template <int BINS, typename C>
 __device__ __forceinline__ void flush_bins(uint64_t* __restrict__ g, C&& cnt) {
     constexpr int PER = BINS / kPB;
@@ -176,17 +175,24 @@ __device__ __forceinline__ void flush_bins(uint64_t* __restrict__ g, C&& cnt) {
 }
 
 // Taken by every workgroup after its flushes: the one that finishes the pass
-// last gets true.  Each wave's flushes have returned before the barrier and the
-// counter is taken after it, so the workgroup that takes it last sees every
-// count with its later device-scope loads.  (No device-scope fence: on a
-// multi-die part it would write back and invalidate the die's L2, and the
-// counts are atomics, not plain stores.  One counter for the <= 256 workgroups:
-// a two-level counter over four replicas measured 1.5 us slower at 2^20.)
+// last gets true.  Memory order (HIP's scoped C++ model): the barrier orders
+// every wave's histogram adds before thread 0's increment, which is a release at
+// agent scope; the increments form one release sequence on `done`, so the acquire
+// fence that the last workgroup alone runs after its own increment makes every
+// other workgroup's adds happen-before its loads of the counts.  The release
+// writes back this die's dirty L2 lines once per workgroup; only the selecting
+// workgroup pays the acquire's L2 invalidation.  One counter for the <= 256
+// workgroups (a two-level counter over four replicas measured 1.5 us slower at
+// 2^20).
 __device__ __forceinline__ bool last_to_finish(uint32_t* done) {
     __shared__ bool s_last;
     __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    if (threadIdx.x == 0) {
+        const bool last =
+            __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = last;
+    }
     __syncthreads();
     return s_last;
 }

@@ -243,25 +243,40 @@ __device__ __forceinline__ void minmax_nan(const Vec<DT>& v, float& mn, float& m
     }
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// a code store: plain, or with the nontemporal hint
+template <bool NT, class V>
+__device__ __forceinline__ void st_code(V* p, V v) {
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// Codes of one vector (N = 4 fp32 or 8 bf16 elements).  fp32 rows (N = 4)
+// store them with the nontemporal hint: measured in the bench step, the fp8
+// amax pass that follows the [4096, 4096] fp32 row ops then finds fewer dirty
+// lines to write back (70.1 -> 64.9 us), while the row ops themselves lose
+// about 1 us in the step.  bf16 rows keep plain stores: with the hint the
+// per-token op itself slowed by more than the op after it gained.
 template <int BITS, int N>
 __device__ __forceinline__ void store_codes(uint8_t* crow, int64_t vi, const uint32_t (&cb)[N]) {
+    constexpr bool NT = N == 4;
     if (BITS == 8) {
         uint32_t w0 = pack4(cb[0], cb[1], cb[2], cb[3]);
         if (N == 4) {
-            reinterpret_cast<uint32_t*>(crow)[vi] = w0;
+            st_code<NT>(reinterpret_cast<uint32_t*>(crow) + vi, w0);
         } else {
             uint32_t w1 = pack4(cb[4 % N], cb[5 % N], cb[6 % N], cb[7 % N]);
-            reinterpret_cast<uint2*>(crow)[vi] = make_uint2(w0, w1);
+            st_code<NT>(reinterpret_cast<u32x2*>(crow) + vi, u32x2{w0, w1});
         }
     } else {
         uint32_t b01 = ((cb[0] & 0xFu) << 4) | (cb[1] & 0xFu);
         uint32_t b23 = ((cb[2] & 0xFu) << 4) | (cb[3] & 0xFu);
         if (N == 4) {
-            reinterpret_cast<uint16_t*>(crow)[vi] = (uint16_t)(b01 | (b23 << 8));
+            st_code<NT>(reinterpret_cast<uint16_t*>(crow) + vi, (uint16_t)(b01 | (b23 << 8)));
         } else {
             uint32_t b45 = ((cb[4 % N] & 0xFu) << 4) | (cb[5 % N] & 0xFu);
             uint32_t b67 = ((cb[6 % N] & 0xFu) << 4) | (cb[7 % N] & 0xFu);
-            reinterpret_cast<uint32_t*>(crow)[vi] = b01 | (b23 << 8) | (b45 << 16) | (b67 << 24);
+            st_code<NT>(reinterpret_cast<uint32_t*>(crow) + vi, b01 | (b23 << 8) | (b45 << 16) | (b67 << 24));
         }
     }
 }
