@@ -64,13 +64,14 @@ __device__ __forceinline__ void fp8_quant_loop(const float* __restrict__ x, int6
     if (AL) {
         const float4* xv = reinterpret_cast<const float4*>(x);
         for (; c + 3 * stride < nfull; c += 4 * stride) {
-            float4 v0 = xv[c], v1 = xv[c + stride], v2 = xv[c + 2 * stride], v3 = xv[c + 3 * stride];
+            float4 v0 = ld_f4<FQ_NT_LOADS_FP8 != 0>(xv + c), v1 = ld_f4<FQ_NT_LOADS_FP8 != 0>(xv + c + stride), v2 = ld_f4<FQ_NT_LOADS_FP8 != 0>(xv + c + 2 * stride),
+                   v3 = ld_f4<FQ_NT_LOADS_FP8 != 0>(xv + c + 3 * stride);
             chunk(c, v0);
             chunk(c + stride, v1);
             chunk(c + 2 * stride, v2);
             chunk(c + 3 * stride, v3);
         }
-        for (; c < nfull; c += stride) chunk(c, xv[c]);
+        for (; c < nfull; c += stride) chunk(c, ld_f4<FQ_NT_LOADS_FP8 != 0>(xv + c));
     } else {
         for (; c < nfull; c += stride) {
             for (int e = 0; e < 4; ++e) {

@@ -230,6 +230,72 @@ __device__ __forceinline__ void store_nt(float4* p, float4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming 16-byte loads of kernel inputs: plain, or with the nontemporal hint
+// (NT).  Which kernels take the hint is a measured choice: it changes what the
+// Infinity Cache holds for the kernels after them.  Measured over the bench step
+// on one box, two runs each (step ms): no hint 2.9602 / 2.9567; the hint on the
+// tensor-scope reduction, the wide-layout kernels and the fp8 quantize 2.9466 /
+// 2.9483 (the fp8 amax pass 65 -> 47 us, the MX blocks 69 -> 64 us, the fp8
+// quantize after the amax 94 -> 99 us, both fp8 dequantizes -2.5 us, the 4-bit
+// dequantize +10 us); on the reduction alone 2.9554 / 2.9509 (the fp8 quantize,
+// no longer finding x in the cache, 94 -> 104 us).  The per-row kernels keep
+// plain loads: with the hint the three row ops after the first, which find the
+// [4096, 4096] weight in the cache, lost 2.5 us each.
+// ---------------------------------------------------------------------------
+#ifndef FQ_NT_LOADS_REDUCE
+#define FQ_NT_LOADS_REDUCE 1
+#endif
+#ifndef FQ_NT_LOADS_WIDE
+#define FQ_NT_LOADS_WIDE 1
+#endif
+#ifndef FQ_NT_LOADS_FP8
+#define FQ_NT_LOADS_FP8 1
+#endif
+#ifndef FQ_NT_LOADS_ROWS
+#define FQ_NT_LOADS_ROWS 0
+#endif
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ float4 ld_f4(const float4* p) {
+    if constexpr (NT) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+template <bool NT>
+__device__ __forceinline__ uint4 ld_u4(const uint4* p) {
+    if constexpr (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Buffer loads and stores with explicit cache-policy bits (gfx950 CPol: sc0 = 1,
+// nt = 2, sc1 = 16) from a wave-uniform base address and a per-lane byte offset
+// below 2^31 (a raw buffer resource: offsets past num_records read 0 / are not
+// written, never fault).
+// ---------------------------------------------------------------------------
+enum { kCpSc0 = 1, kCpNt = 2, kCpSc1 = 16 };
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+template <int CP>
+__device__ __forceinline__ float4 buf_load16(const void* base, uint32_t off) {
+    const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(wave_rsrc(base), off, 0, CP);
+    return make_float4(as_f(r.x), as_f(r.y), as_f(r.z), as_f(r.w));
+}
+template <int CP>
+__device__ __forceinline__ void buf_store16(void* base, uint32_t off, float4 v) {
+    const u32x4 w = {as_u(v.x), as_u(v.y), as_u(v.z), as_u(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, wave_rsrc(base), off, 0, CP);
+}
+
+// ---------------------------------------------------------------------------
 // Wide layout: sixteen consecutive elements per lane, so that per-block work
 // (reductions, scales, reciprocals) is shared by four times as many elements as
 // with one 16-byte vector per lane.  A lane's sixteen outputs are contiguous in
@@ -260,7 +326,7 @@ __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, fl
         const float4* p = reinterpret_cast<const float4*>(x) + 4 * v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 q = p[j];
+            const float4 q = ld_f4<FQ_NT_LOADS_WIDE != 0>(p + j);
             e[4 * j] = q.x;
             e[4 * j + 1] = q.y;
             e[4 * j + 2] = q.z;
@@ -270,7 +336,7 @@ __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, fl
         const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * v;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint4 q = p[j];
+            const uint4 q = ld_u4<FQ_NT_LOADS_WIDE != 0>(p + j);
             const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

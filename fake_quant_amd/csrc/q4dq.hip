@@ -54,6 +54,30 @@ constexpr int kQuantNsb = FQ_Q4_NSB;  // super-blocks per workgroup of the quant
 constexpr int kDequantNsb = FQ_Q4DQ_NSB;  // super-blocks per workgroup of the dequantize kernel
 constexpr int kOccQuant = FQ_OCC_Q4;
 constexpr int kOccDequant = FQ_OCC_Q4DQ;
+// Cache policy of the full-super-block kernels, measured over the whole bench step
+// on one box (quantize + reconstruct / dequantize, us): plain loads and global
+// nontemporal stores 1561 / 827; nontemporal loads (CPol nt) of x, nontemporal
+// device-scope stores (nt sc1) of the reconstruction and nontemporal code stores
+// 1494 / 830; the same with plain code stores 1467 / 859 (the dequantize then
+// writes back the codes the quantize left dirty in the cache: the same total);
+// nt sc1 stores in the dequantize too 1496 / 864; the codes through buffer
+// stores (nt, or nt sc1) no faster than global nontemporal ones.
+#ifndef FQ_Q4_LD_CP
+#define FQ_Q4_LD_CP 2
+#endif
+#ifndef FQ_Q4_ST_CP
+#define FQ_Q4_ST_CP 18
+#endif
+#ifndef FQ_Q4DQ_ST_CP
+#define FQ_Q4DQ_ST_CP -1
+#endif
+#ifndef FQ_Q4_CODES_NT
+#define FQ_Q4_CODES_NT 1
+#endif
+constexpr int kLdCp = FQ_Q4_LD_CP;      // cache policy of the x loads (-1: plain global loads)
+constexpr int kStCp = FQ_Q4_ST_CP;      // cache policy of the reconstruction stores (-1: global nontemporal)
+constexpr int kDqStCp = FQ_Q4DQ_ST_CP;  // cache policy of the dequantize stores (-1: global nontemporal)
+constexpr bool kCodesNt = FQ_Q4_CODES_NT != 0;  // packed codes and u8 scales with the nontemporal hint
 constexpr int kQuantLds = 2048;
 constexpr int kDequantLds = 1024;
 
@@ -64,6 +88,15 @@ __device__ __forceinline__ float q4_code(const ExactDiv& d, float x) {
     return (t != t) ? 0.0f : r;
 }
 
+// code and scale-code stores, with the nontemporal hint when kCodesNt
+__device__ __forceinline__ void st_u16(uint16_t* p, uint16_t v) {
+    if constexpr (kCodesNt) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
+    if constexpr (kCodesNt) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 // [DQ] u8 scale code: clamp(round_half_away(s / S * 255), 0, 255)
 __device__ __forceinline__ uint32_t u8_scale(float s, float S) {
     float v = (s / S) * 255.0f;
@@ -110,11 +143,17 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
     const int t = threadIdx.x;
     const int lrow = t & 15;  // position inside the 16-lane row
     float4 v[J];
-    {
-        const float4* xv = reinterpret_cast<const float4*>(x + (int64_t)blockIdx.x * NSB * kSuperElems);
+    auto load_sb = [&](const float* base) {
+        if constexpr (kLdCp < 0) {
+            const float4* xv = reinterpret_cast<const float4*>(base);
 #pragma unroll
-        for (int j = 0; j < J; ++j) v[j] = xv[j * TPB + t];
-    }
+            for (int j = 0; j < J; ++j) v[j] = xv[j * TPB + t];
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[j] = buf_load16<kLdCp>(base, (uint32_t)(j * TPB + t) * 16u);
+        }
+    };
+    load_sb(x + (int64_t)blockIdx.x * NSB * kSuperElems);
 
     __shared__ float s_scale[kGroup];
     __shared__ uint32_t s_u8[kGroup / 4];
@@ -165,7 +204,7 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
             const float f2 = __builtin_amdgcn_fmed3f(quick_div(v[j].z, s, y), -7.0f, 7.0f) + kMagic;
             const float f3 = __builtin_amdgcn_fmed3f(quick_div(v[j].w, s, y), -7.0f, 7.0f) + kMagic;
             const uint32_t w = nib_pair(f0, f1) | (nib_pair(f2, f3) << 8);
-            pk[j * TPB + t] = (uint16_t)w;
+            st_u16(pk + j * TPB + t, (uint16_t)w);
             pc[j] = w;
         });
     } else {
@@ -176,7 +215,7 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
             const bool fast = fast_divisor(s);
             const uint32_t w = nib2(q4_general(v[j].x, s, y, fast), q4_general(v[j].y, s, y, fast)) |
                                (nib2(q4_general(v[j].z, s, y, fast), q4_general(v[j].w, s, y, fast)) << 8);
-            pk[j * TPB + t] = (uint16_t)w;
+            st_u16(pk + j * TPB + t, (uint16_t)w);
             pc[j] = w;
         });
     }
@@ -201,12 +240,8 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
     }
     const float my_sh = recon_scale(u8_scale(my_s, S), S);
     __syncthreads();
-    if (t < kGroup / 4) reinterpret_cast<uint32_t*>(qscale + sb * kGroup)[t] = s_u8[t];
-    if (isb + 1 < NSB) {
-        const float4* xn = reinterpret_cast<const float4*>(x + (sb + 1) * kSuperElems);
-#pragma unroll
-        for (int j = 0; j < J; ++j) v[j] = xn[j * TPB + t];
-    }
+    if (t < kGroup / 4) st_u32(reinterpret_cast<uint32_t*>(qscale + sb * kGroup) + t, s_u8[t]);
+    if (isb + 1 < NSB) load_sb(x + (sb + 1) * kSuperElems);
     if (recon) {
         float4* rv = reinterpret_cast<float4*>(recon + sb * kSuperElems);
         StaticFor<0, J>::run([&](auto jc) {
@@ -217,7 +252,9 @@ __global__ __launch_bounds__(TPB) void k_q4dq_full(const float* __restrict__ x, 
             const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)w, 0, 4);
             const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)w, 12, 4);
             const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)w, 8, 4);
-            store_nt(rv + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
+            const float4 o = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+            if constexpr (kStCp < 0) store_nt(rv + j * TPB + t, o);
+            else buf_store16<kStCp>(rv, (uint32_t)(j * TPB + t) * 16u, o);
         });
     }
     }  // super-blocks of this workgroup
@@ -327,7 +364,9 @@ __global__ __launch_bounds__(TPB) void k_q4dq_dequant_full(const uint8_t* __rest
             const float c1 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 0, 4);
             const float c2 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 12, 4);
             const float c3 = (float)(int)__builtin_amdgcn_sbfe((int)wc[j], 8, 4);
-            store_nt(o + j * TPB + t, make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh));
+            const float4 r = make_float4(c0 * sh, c1 * sh, c2 * sh, c3 * sh);
+            if constexpr (kDqStCp < 0) store_nt(o + j * TPB + t, r);
+            else buf_store16<kDqStCp>(o, (uint32_t)(j * TPB + t) * 16u, r);
         }
     }
 }

@@ -58,8 +58,8 @@ __device__ __forceinline__ Vec<DT> load_vec(const void* row, int64_t vi, int64_t
     Vec<DT> r;
     constexpr int N = Vec<DT>::N;
     if constexpr (AL) {
-        if constexpr (DT == FQ_F32) r.v = reinterpret_cast<const float4*>(row)[vi];
-        else r.v = reinterpret_cast<const uint4*>(row)[vi];
+        if constexpr (DT == FQ_F32) r.v = ld_f4<FQ_NT_LOADS_ROWS != 0>(reinterpret_cast<const float4*>(row) + vi);
+        else r.v = ld_u4<FQ_NT_LOADS_ROWS != 0>(reinterpret_cast<const uint4*>(row) + vi);
     } else {
         uint32_t w[4] = {0, 0, 0, 0};
         for (int e = 0; e < N; ++e) {

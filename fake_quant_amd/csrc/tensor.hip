@@ -25,6 +25,10 @@ constexpr int kB = fqh::kBlock;
 __device__ __forceinline__ float4 ld4(const float* p, int64_t c) {
     return *reinterpret_cast<const float4*>(p + 4 * c);
 }
+// the tensor-scope reduction's loads (nontemporal when FQ_NT_LOADS_REDUCE)
+__device__ __forceinline__ float4 ld4_reduce(const float* p, int64_t c) {
+    return ld_f4<FQ_NT_LOADS_REDUCE != 0>(reinterpret_cast<const float4*>(p + 4 * c));
+}
 __device__ __forceinline__ void st4(float* p, int64_t c, float4 v) {
     store_nt(reinterpret_cast<float4*>(p + 4 * c), v);
 }
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(kRT) void k_reduce_partial(const float* __restrict_
     const int64_t ntiles = (nfull + fqh::kReduceTile - 1) / fqh::kReduceTile;
     const bool tail = blockIdx.x == 0 && threadIdx.x < (n & 3);
     auto ld = [&](int64_t c) -> float4 {
-        if (AL) return ld4(x, c);
+        if (AL) return ld4_reduce(x, c);
         return make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
     };
     float4 r;
