@@ -70,8 +70,9 @@ def parse():
                     help="skip the rows beyond the step (stochastic rounding, QAT step, calibration variants, "
                          "block formats), timed cold / warm on their own")
     ap.add_argument("--copy-ref", action="store_true",
-                    help="only run COPY_REF_LAUNCHES plain device copies of COPY_REF_BYTES each (the known-size "
-                         "reference that scales HBM counter readings) and exit")
+                    help="only run COPY_REF_LAUNCHES plain device copies of COPY_REF_BYTES each, torch's and then "
+                         "the library's copy kernel (the known-size reference that scales HBM counter readings) "
+                         "and exit")
     return ap.parse_args()
 
 
@@ -79,10 +80,12 @@ COPY_REF_BYTES = 1 << 30
 COPY_REF_LAUNCHES = 3
 
 
-def copy_reference(torch):
-    """Plain torch copies of a known size: each launch reads and writes exactly
+def copy_reference(torch, fq):
+    """Plain copies of a known size: each launch reads and writes exactly
     COPY_REF_BYTES, so the FETCH_SIZE / WRITE_SIZE counters read for it give the
-    factor from counter units to bytes."""
+    factor from counter units to bytes.  First torch's device copy, then the
+    library's plain copy kernel (fqb_copy_f32, the achievable-bandwidth reference
+    that other counters of the kernels are compared with)."""
     src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -90,7 +93,12 @@ def copy_reference(torch):
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy {i} of {COPY_REF_BYTES} bytes done")
-    print(json.dumps({"copy_ref_bytes": COPY_REF_BYTES, "launches": COPY_REF_LAUNCHES}))
+    for i in range(COPY_REF_LAUNCHES):
+        fq.fqb_copy_f32(src, dst, COPY_REF_BYTES // 4)
+        torch.cuda.synchronize()
+        log(f"fqb_copy_f32 {i} of {COPY_REF_BYTES} bytes done")
+    print(json.dumps({"copy_ref_bytes": COPY_REF_BYTES, "launches": COPY_REF_LAUNCHES,
+                      "kernels": ["torch device copy", "fqb_copy_f32"]}))
 
 
 class Op:
@@ -877,7 +885,7 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     if args.copy_ref:
-        copy_reference(torch)
+        copy_reference(torch, fq)
         return
     log("drawing inputs and allocating outputs")
     ops = build_ops(fq, syn, torch, args.only)
