@@ -295,6 +295,26 @@ __device__ __forceinline__ void buf_store16(void* base, uint32_t off, float4 v) 
     __builtin_amdgcn_raw_buffer_store_b128(w, wave_rsrc(base), off, 0, CP);
 }
 
+// Stream store of float4 number i of `out`, for indices whose distance from the
+// wave's lane number is the same in every lane (i - lane wave-uniform, as in
+// every covering-grid layout here): CP < 0 is the global nontemporal store,
+// otherwise a buffer store with cache policy CP from the wave's base address.
+template <int CP>
+__device__ __forceinline__ void store_out(float4* out, int64_t i, float4 v) {
+    if constexpr (CP < 0) {
+        store_nt(out + i, v);
+    } else {
+        const int lane = (int)(threadIdx.x & (kWave - 1));
+        const uint64_t a = (uint64_t)(out + (i - lane));
+        // readfirstlane returns an int: both halves go back through uint32_t, so a
+        // low word with bit 31 set is not sign-extended into the high word
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+        const uint64_t ua = ((uint64_t)hi << 32) | (uint64_t)lo;
+        buf_store16<CP>(reinterpret_cast<void*>(ua), (uint32_t)lane * 16u, v);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Wide layout: sixteen consecutive elements per lane, so that per-block work
 // (reductions, scales, reciprocals) is shared by four times as many elements as
