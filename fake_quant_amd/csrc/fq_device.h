@@ -234,19 +234,20 @@ __device__ __forceinline__ void store_nt(float4* p, float4 v) {
 // (NT).  Which kernels take the hint is a measured choice: it changes what the
 // Infinity Cache holds for the kernels after them.  Measured over the bench step
 // on one box, two runs each (step ms): no hint 2.9602 / 2.9567; the hint on the
-// tensor-scope reduction, the wide-layout kernels and the fp8 quantize 2.9466 /
+// tensor-scope reduction, the MX fp8 blocks and the fp8 quantize 2.9466 /
 // 2.9483 (the fp8 amax pass 65 -> 47 us, the MX blocks 69 -> 64 us, the fp8
 // quantize after the amax 94 -> 99 us, both fp8 dequantizes -2.5 us, the 4-bit
 // dequantize +10 us); on the reduction alone 2.9554 / 2.9509 (the fp8 quantize,
 // no longer finding x in the cache, 94 -> 104 us).  The per-row kernels keep
 // plain loads: with the hint the three row ops after the first, which find the
-// [4096, 4096] weight in the cache, lost 2.5 us each.
+// [4096, 4096] weight in the cache, lost 2.5 us each.  Of the wide-layout kernels
+// only the MX fp8 blocks take it (load16's NT), on bf16 input: with the hint the
+// fp32 wide kernels (NVFP4, group-wise) fetched 10-12 % more than they read (a
+// lane's four consecutive 16-byte loads are four instructions whose lines the L2
+// must keep between them), and the FP4 blocks ran 4 % slower cold.
 // ---------------------------------------------------------------------------
 #ifndef FQ_NT_LOADS_REDUCE
 #define FQ_NT_LOADS_REDUCE 1
-#endif
-#ifndef FQ_NT_LOADS_WIDE
-#define FQ_NT_LOADS_WIDE 1
 #endif
 #ifndef FQ_NT_LOADS_FP8
 #define FQ_NT_LOADS_FP8 1
@@ -339,14 +340,15 @@ __device__ __forceinline__ float load_elem(const void* __restrict__ x, int64_t i
 constexpr int kWide = 16;
 constexpr int kWidePad = kWide + 4;  // LDS floats per lane of the staging buffer (16-byte rows)
 
-// elements 16 v .. 16 v + 15 of x (binary32, or bf16 widened exactly)
-template <bool BF16>
+// elements 16 v .. 16 v + 15 of x (binary32, or bf16 widened exactly); NT: bf16
+// loads with the nontemporal hint
+template <bool BF16, bool NT = false>
 __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, float (&e)[kWide]) {
     if constexpr (!BF16) {
         const float4* p = reinterpret_cast<const float4*>(x) + 4 * v;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 q = ld_f4<FQ_NT_LOADS_WIDE != 0>(p + j);
+            const float4 q = ld_f4<false>(p + j);
             e[4 * j] = q.x;
             e[4 * j + 1] = q.y;
             e[4 * j + 2] = q.z;
@@ -356,7 +358,7 @@ __device__ __forceinline__ void load16(const void* __restrict__ x, int64_t v, fl
         const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * v;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint4 q = ld_u4<FQ_NT_LOADS_WIDE != 0>(p + j);
+            const uint4 q = ld_u4<NT>(p + j);
             const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

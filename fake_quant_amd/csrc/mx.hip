@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kB) void k_mx_wide(const void* __restrict__ x, int6
     const bool in = v < nw;
     float xe[kWide];
     if (in) {
-        load16<DT == FQ_BF16>(x, v, xe);
+        load16<DT == FQ_BF16, true>(x, v, xe);
     } else {
 #pragma unroll
         for (int i = 0; i < kWide; ++i) xe[i] = 0.0f;
