@@ -18,7 +18,7 @@
 // contention -- and adds the non-zero bins to the workspace with 64-bit atomics
 // (integer counts: the result does not depend on their order).  Atomics on one
 // address serialise, so the device histogram has four replicas (workgroup b adds
-// into replica b mod 4) and the grid is capped at 256 workgroups of 512 threads
+// into replica b mod 4) and the grid is capped at 256 workgroups of 1024 threads
 // (grid-stride loop).  A counter names the last workgroup to finish the pass;
 // it sums the replicas, and one of
 // its waves narrows prefix and rank of both statistics; after the last pass it
@@ -38,7 +38,14 @@ using namespace fqk;
 
 namespace {
 
-constexpr int kPB = 512;  // threads per workgroup of the passes
+// 1024 threads per workgroup (one workgroup of 16 waves per CU at the 256-workgroup
+// cap): 39.0-39.5 / 63.8-64.4 us at 2^20 / 2^24, against 42.4-42.9 / 68.0-68.5 us
+// with 512 and 54.8-55.0 / 90.2-90.4 us with 256; with 1024 threads a cap of 128
+// or 512 workgroups was slower at 2^24 (71.4-71.9 / 81.8-81.9 us).
+#ifndef FQ_PCT_THREADS
+#define FQ_PCT_THREADS 1024
+#endif
+constexpr int kPB = FQ_PCT_THREADS;  // threads per workgroup of the passes
 constexpr int kPasses = 3;
 constexpr int kMaxBins = 2048;
 constexpr int kU = 4;       // 16-byte loads in flight per thread
