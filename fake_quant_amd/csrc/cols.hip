@@ -6,18 +6,20 @@
 // with axis = 1 (each column is a channel, calibrated on that column only).
 //
 // A column's elements are cols apart, so a block works on a tile of 64 column
-// vectors (N = 4 fp32 or 8 bf16 columns each: one 16-byte load per row, so each
-// wave reads one contiguous run of a row) over a band of rows, its four waves
-// taking every fourth row with several row loads in flight per thread.  Three
-// launches, none with a global atomic on the data path:
+// vectors over a band of rows (each wave reads or writes one contiguous run of a
+// row per instruction), its four waves taking every fourth row with several row
+// loads in flight per thread.  Three launches, none with a global atomic on the
+// data path:
 //   1. k_cols_minmax: finite min / max / non-finite of each column over each
-//      band of rows (at most 64 bands), waves merged through LDS, one partial
-//      record per (band, column);
+//      band of rows (at most 64 bands), vectors of 4 fp32 or 8 bf16 columns
+//      (16-byte loads), waves merged through LDS, one partial record per
+//      (band, column);
 //   2. k_cols_fold: four threads per column fold its band partials, merged
 //      through LDS into one record per column;
-//   3. k_cols_quant: each block derives the parameters of its tile's columns
-//      ([QAT] from_minmax) into LDS once, then quantizes its rows; the blocks of
-//      the first band also write the scales, zero-points and flags.
+//   3. k_cols_quant: vectors of four columns for either dtype; each block
+//      derives the parameters of its tile's columns ([QAT] from_minmax) into LDS
+//      once, then quantizes its rows; the blocks of the first band also write
+//      the scales, zero-points and flags.
 // x is read twice; the workspace holds the partials and the column records.
 // fp32 tensors of 1025..4096 rows with a multiple of 16 columns (at least half as
 // many 16-column strips as compute units) take one launch instead, k_cols_strip,
@@ -32,8 +34,10 @@ namespace {
 constexpr int kB = fqh::kBlock;
 constexpr int kWaves = kB / kWave;   // waves per block
 constexpr int64_t kMaxBands = 64;    // bands of the min / max pass (partials per column)
-constexpr int kQuantRows = 32;       // rows per band of the quantize pass
-constexpr int kU = 8;                // row loads in flight per thread (quantize pass)
+constexpr int kQuantVec = 4;         // columns per lane in the quantize pass
+constexpr int kU = 4;                // row loads in flight per thread (quantize pass); 8 and 16 measured slower
+constexpr int kQuantRows = kWaves * kU;  // rows per band of the quantize pass
+constexpr int kFoldU = 16;           // band partials in flight per thread of the fold
 constexpr int kUm = 8;  // row loads in flight per thread (min / max pass); 4 and 16 time the same
 constexpr int64_t kMaxQuantBands = 65535;  // grid y limit; blocks loop over further bands
 
@@ -45,13 +49,20 @@ struct ColVec {
 };
 
 // element e of the vector of N columns starting at column c0 of row r
-// (aligned: one 16-byte load; otherwise element loads, out-of-range as 0)
-template <int DT, bool AL>
+// (aligned: one 16-byte load, or 8 bytes for four bf16; otherwise element
+// loads, out-of-range as 0)
+template <int DT, int N, bool AL>
 __device__ __forceinline__ void load_cols(const void* __restrict__ x, int64_t r, int64_t cols, int64_t c0,
-                                          float (&v)[ColVec<DT>::N]) {
-    constexpr int N = ColVec<DT>::N;
+                                          float (&v)[N]) {
+    static_assert(N == ColVec<DT>::N || (DT == FQ_BF16 && N == 4), "a vector is 16 bytes, or four bf16");
     if constexpr (AL) {
-        if constexpr (DT == FQ_F32) {
+        if constexpr (DT == FQ_BF16 && N == 4) {
+            const uint2 q = reinterpret_cast<const uint2*>(x)[(r * cols + c0) / 4];
+            v[0] = bf16_lo(q.x);
+            v[1] = bf16_hi(q.x);
+            v[2] = bf16_lo(q.y);
+            v[3] = bf16_hi(q.y);
+        } else if constexpr (DT == FQ_F32) {
             const float4 q = reinterpret_cast<const float4*>(x)[(r * cols + c0) / 4];
             v[0] = q.x;
             v[1] = q.y;
@@ -99,7 +110,7 @@ __global__ __launch_bounds__(kB) void k_cols_minmax(const void* __restrict__ x, 
 #pragma unroll
             for (int u = 0; u < kUm; ++u) {
                 const int64_t rr = r + u * kWaves;
-                load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);
+                load_cols<DT, N, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);
             }
 #pragma unroll
             for (int u = 0; u < kUm; ++u)
@@ -128,22 +139,23 @@ __global__ __launch_bounds__(kB) void k_cols_minmax(const void* __restrict__ x, 
 }
 
 // record of column c: the fold of its band partials (finite min, finite max,
-// max |x| bits)
+// max |x| bits); with at most kWaves * kFoldU bands a thread loads all of its
+// partials in one round
 __global__ __launch_bounds__(kB) void k_cols_fold(const float4* __restrict__ part, int64_t nbands, int64_t cols,
                                                   float4* __restrict__ rec) {
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
     const int64_t c = (int64_t)blockIdx.x * kWave + lane;
     MinMax m;
     if (c < cols) {
-        for (int64_t b = w; b < nbands; b += kWaves * 4) {
-            float4 p[4];
+        for (int64_t b = w; b < nbands; b += kWaves * kFoldU) {
+            float4 p[kFoldU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kFoldU; ++u) {
                 const int64_t bb = b + u * kWaves;
                 p[u] = part[(bb < nbands ? bb : b) * cols + c];
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) m.merge(p[u].x, p[u].y, as_u(p[u].z));
+            for (int u = 0; u < kFoldU; ++u) m.merge(p[u].x, p[u].y, as_u(p[u].z));
         }
     }
     __shared__ float4 s[kWaves - 1][kWave];
@@ -216,15 +228,17 @@ __device__ __forceinline__ void store_row(const int (&code)[N], const float (&o)
     }
 }
 
+// Four columns per lane for either dtype, so that every store instruction of a
+// wave writes one contiguous run (1 KB of fake-quant values, 256 or 128 bytes of
+// codes); a bf16 row is read 8 bytes per lane.
 template <int DT, int BITS, bool AL>
 __global__ __launch_bounds__(kB) void k_cols_quant(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                    int affine, const float4* __restrict__ rec,
                                                    uint8_t* __restrict__ codes, float* __restrict__ fq,
                                                    float* __restrict__ scale, int32_t* __restrict__ zp,
                                                    uint32_t* __restrict__ flags) {
-    constexpr int N = ColVec<DT>::N;
+    constexpr int N = kQuantVec;
     constexpr int TC = kWave * N;  // columns of the tile
-    static_assert(kQuantRows == kWaves * kU, "one batch of row loads per wave covers a band");
     __shared__ float4 s_par[TC];
     const int64_t ct0 = (int64_t)blockIdx.x * TC;
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(kB) void k_cols_quant(const void* __restrict__ x, i
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t rr = r0 + w + u * kWaves;
-            load_cols<DT, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);  // past the band: its last row again
+            load_cols<DT, N, AL>(x, rr < r1 ? rr : r1 - 1, cols, c0, v[u]);  // past the band: its last row again
         }
     };
     if (in) load_band();
@@ -455,11 +469,15 @@ int launch_cols(const void* x, int64_t rows, int64_t cols, int affine, void* ws,
     const int64_t rpb = (rows + nb - 1) / nb;
     float4* part = reinterpret_cast<float4*>(ws);
     float4* rec = part + nb * cols;
-    const size_t code_align = BITS == 8 ? (N == 4 ? 4 : 8) : (N == 4 ? 2 : 4);
-    const bool al = (cols % N == 0) && fqh::aligned(x, 16) && fqh::aligned(fq, 16) && fqh::aligned(codes, code_align);
+    // min / max pass: 16-byte vectors of N columns; quantize pass: four columns
+    // (16 bytes of fp32 or 8 of bf16), codes 4 (int8) or 2 (int4) bytes per lane
+    const bool al = (cols % N == 0) && fqh::aligned(x, 16);
+    const bool alq = (cols % kQuantVec == 0) && fqh::aligned(x, DT == FQ_F32 ? 16 : 8) && fqh::aligned(fq, 16) &&
+                     fqh::aligned(codes, BITS == 8 ? 4 : 2);
     const int64_t tiles = (cols + kWave * N - 1) / (kWave * N);
-    if (tiles > 0x7FFFFFFF) return FQ_E_INVALID;
-    if (DT == FQ_F32 && al && rows > kStripRows / 4 && rows <= kStripRows && cols % kStripCols == 0 &&
+    const int64_t qtiles = (cols + kWave * kQuantVec - 1) / (kWave * kQuantVec);
+    if (qtiles > 0x7FFFFFFF) return FQ_E_INVALID;
+    if (DT == FQ_F32 && alq && rows > kStripRows / 4 && rows <= kStripRows && cols % kStripCols == 0 &&
         cols / kStripCols >= fqh::num_cus() / 2 && cols / kStripCols <= 0x7FFFFFFF) {
         k_cols_strip<BITS><<<(unsigned)(cols / kStripCols), kStripThreads, 0, st>>>(
             reinterpret_cast<const float*>(x), rows, cols, affine, codes, fq, scale, zp, flags);
@@ -471,8 +489,8 @@ int launch_cols(const void* x, int64_t rows, int64_t cols, int affine, void* ws,
     k_cols_fold<<<(unsigned)((cols + kWave - 1) / kWave), kB, 0, st>>>(part, nb, cols, rec);
     int64_t qb = (rows + kQuantRows - 1) / kQuantRows;
     qb = qb < kMaxQuantBands ? qb : kMaxQuantBands;
-    const dim3 g2((unsigned)tiles, (unsigned)qb);
-    if (al) k_cols_quant<DT, BITS, true><<<g2, kB, 0, st>>>(x, rows, cols, affine, rec, codes, fq, scale, zp, flags);
+    const dim3 g2((unsigned)qtiles, (unsigned)qb);
+    if (alq) k_cols_quant<DT, BITS, true><<<g2, kB, 0, st>>>(x, rows, cols, affine, rec, codes, fq, scale, zp, flags);
     else k_cols_quant<DT, BITS, false><<<g2, kB, 0, st>>>(x, rows, cols, affine, rec, codes, fq, scale, zp, flags);
     return fqh::launched();
 }

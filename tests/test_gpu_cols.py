@@ -80,6 +80,21 @@ def test_unaligned_view(fqlib, orc):
     check_cols(fqlib, orc, x, 8, 1, "unaligned")
 
 
+def test_bf16_quantize_vectors(fqlib, orc):
+    # the quantize pass reads four bf16 columns (8 bytes) per lane, the min / max
+    # pass eight (16 bytes): a column count that is a multiple of four but not of
+    # eight, and views 8-byte aligned (vector quantize, element min / max) and
+    # 4-byte aligned (element loads in both)
+    w = synthetic.rows_f32_inputs(300, 260, device="cuda", seed=260).to(torch.bfloat16)
+    for bits, scheme in ((8, 1), (4, 0), (4, 1)):
+        check_cols(fqlib, orc, w, bits, scheme, "bf16 cols % 8 == 4")
+    buf = synthetic.rows_f32_inputs(1, 130 * 512 + 8, device="cuda", seed=7).reshape(-1).to(torch.bfloat16)
+    for off in (4, 2):
+        x = buf[off:off + 130 * 512].reshape(130, 512)
+        for bits, scheme in ((8, 0), (4, 1)):
+            check_cols(fqlib, orc, x, bits, scheme, f"bf16 view at element {off}")
+
+
 # fp32 shapes of the one-pass strip kernel (1024 < rows <= 4096, cols a multiple
 # of 16 with at least half as many 16-column strips as compute units): smallest
 # and largest row counts, rows that leave a partial 256-row load, a strip count
