@@ -294,7 +294,7 @@ def ops_next_qat(fq, syn, torch, dev):
     view = torch.empty(n, dtype=torch.float32, device=dev)
     t = 10
     return [
-        Op("qat.step_int8_sym", "k_adamw_minmax+k_params_int_final+k_fq_int_tensor",
+        Op("qat.step_int8_sym", "k_adamw_minmax+k_fq_int_tensor_fold_gs",
            lambda: fq.fq_qat_step_int(w, g, m, v, n, cfg, t, 8, fq.SYM, fq.ROUND_NEAREST, 0, 0, ws, wsb, params,
                                       codes, view, flags), 33 * n),
         Op("qat.step_fp8_e4m3", "k_adamw_fp8",

@@ -105,6 +105,21 @@ constexpr int64_t kFoldMaxParts = 512;
 int params_from_partials(const void* workspace, unsigned nparts, int bits, int scheme, fq_int_params* params,
                          uint32_t* flags, hipStream_t stream);
 
+// Fake-quant of x[n] (16-byte aligned operands, at most kFoldGsMaxParts
+// partials) whose parameters every block derives itself from the `nparts`
+// partial records in the workspace (block 0 stores them and the flags): one
+// launch in place of params_from_partials + fq_fake_quant_int_tensor, which it
+// falls back to otherwise.  Measured on the 2^24-element QAT step (update pass
+// capped at this many workgroups): 512 partials and 16 workgroups per CU ran the
+// step in 99.3-100.6 us cold against 101.4-102.9 for three launches (two boxes,
+// interleaved runs); 2048
+// partials 104.8-105.9, 256 partials 112.9-114.6 (an update pass of one
+// workgroup per CU), 8 workgroups per CU 101.6-101.8.
+constexpr int kFoldGsMaxParts = 512;
+constexpr int kFoldGsBlocksPerCu = 16;
+int fake_quant_from_partials(const float* x, int64_t n, int bits, int scheme, const void* workspace, unsigned nparts,
+                             fq_int_params* params, void* codes, float* fq, uint32_t* flags, hipStream_t stream);
+
 // Finite amax of x[n] (float32; 0 when no element is finite), left as binary32
 // bits in word 0 of the workspace (fq_workspace_bytes(n) bytes) by two launches.
 int tensor_amax(const float* x, int64_t n, void* workspace, hipStream_t stream);

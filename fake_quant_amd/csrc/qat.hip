@@ -13,10 +13,11 @@
 // rounded once.
 //
 // Integer target: one pass updates w, m, v and leaves one finite min / max
-// partial per workgroup (the tiling of the tensor-scope reduction), a one-block
-// pass derives the parameters on the device, and the per-tensor fake-quant
-// re-reads the updated master (still in cache for tensors that fit).  fp8
-// target: the view needs no tensor-wide value, so update and cast are one pass.
+// partial per workgroup (the tiling of the tensor-scope reduction); with nearest
+// rounding every block of the requantize pass folds those partials itself and
+// re-reads the updated master (two launches), with stochastic rounding a
+// one-block pass derives the parameters first.  fp8 target: the view needs no
+// tensor-wide value, so update and cast are one pass.
 #include <cmath>
 
 #include "fq_device.h"
@@ -230,11 +231,17 @@ int fq_qat_step_int(float* master, const float* grad, float* m, float* v, int64_
     AdamStep a;
     int st = make_step(cfg, t, &a);
     if (st != FQ_OK) return st;
-    const unsigned G = fqh::reduce_blocks(n);
+    unsigned G = fqh::reduce_blocks(n);
     const bool al = fqh::aligned(master, 16) && fqh::aligned(grad, 16) && fqh::aligned(m, 16) && fqh::aligned(v, 16);
+    // nearest rounding: the requantize blocks fold the update pass's partials
+    // themselves (two launches), so the update grid is capped at the number of
+    // partials they take (its blocks loop over further tiles)
+    const bool fold = rounding == FQ_ROUND_NEAREST;
+    if (fold && G > (unsigned)fqh::kFoldGsMaxParts) G = (unsigned)fqh::kFoldGsMaxParts;
     if (al) k_adamw_minmax<true><<<G, kRT, 0, stream>>>(master, grad, m, v, n, a, (float4*)workspace);
     else k_adamw_minmax<false><<<G, kRT, 0, stream>>>(master, grad, m, v, n, a, (float4*)workspace);
     if ((st = fqh::launched()) != FQ_OK) return st;
+    if (fold) return fqh::fake_quant_from_partials(master, n, bits, scheme, workspace, G, params, codes, view, flags, stream);
     if ((st = fqh::params_from_partials(workspace, G, bits, scheme, params, flags, stream)) != FQ_OK) return st;
     if (rounding == FQ_ROUND_NEAREST) return fq_fake_quant_int_tensor(master, n, bits, scheme, params, codes, view, stream);
     return fq_fake_quant_int_tensor_sr(master, n, bits, scheme, params, seed, offset, codes, view, stream);

@@ -386,6 +386,81 @@ __global__ __launch_bounds__(kB) void k_fq_int_tensor_fold(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
+// The same fold ahead of a grid-stride fake-quant: every block first loads its
+// first four chunks of x, then folds up to MAXP partials (all of a thread's
+// partials loaded in one round, so the two loads overlap), derives the
+// parameters (block 0 stores them), then quantizes its share of the tensor four
+// chunks at a time.  The grid is capped at a few resident blocks per compute
+// unit, so the partials are read from L2 a few thousand times at most.  Serves
+// the integer QAT step: its update pass leaves the partials, so the step takes
+// two launches instead of three.
+// ---------------------------------------------------------------------------
+template <int BITS, int MODE>
+__device__ __forceinline__ void fq_int_gs_loop(const IntTensorOp<BITS, MODE>& op, const float* __restrict__ x,
+                                               int64_t n, int64_t c, int64_t stride, float4 (&v)[4]) {
+    const int64_t nfull = n >> 2;
+    for (;;) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (c + u * stride < nfull) op.vector_chunk(c + u * stride, v[u]);
+        c += 4 * stride;
+        if (c >= nfull) break;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (c + u * stride < nfull) v[u] = ld4(x, c + u * stride);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 3)) op.scalar_chunk(x, nfull, (int)(n & 3));
+}
+
+template <int BITS, int MAXP>
+__global__ __launch_bounds__(kB) void k_fq_int_tensor_fold_gs(const float* __restrict__ x, int64_t n, int affine,
+                                                              const float4* __restrict__ part, int nparts,
+                                                              fq_int_params* __restrict__ params,
+                                                              uint8_t* __restrict__ codes, float* __restrict__ fq,
+                                                              uint32_t* __restrict__ flags) {
+    static_assert(MAXP % kB == 0, "whole loads of partials per thread");
+    const int t = threadIdx.x;
+    const int64_t nfull = n >> 2;
+    const int64_t stride = (int64_t)gridDim.x * kB;
+    const int64_t c = (int64_t)blockIdx.x * kB + t;
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = c + u * stride < nfull ? ld4(x, c + u * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 p[MAXP / kB];
+#pragma unroll
+    for (int k = 0; k < MAXP / kB; ++k) {
+        const int i = t + k * kB;
+        p[k] = i < nparts ? part[i] : make_float4(__builtin_inff(), -__builtin_inff(), 0.f, 0.f);
+    }
+    MinMax m;
+#pragma unroll
+    for (int k = 0; k < MAXP / kB; ++k) m.merge(p[k].x, p[k].y, as_u(p[k].z));
+    __shared__ float4 lds[kB / kWave];
+    const float4 r = make_float4(wave_min_f(m.mn), wave_max_f(m.mx), as_f(wave_max_u(m.nf)), 0.f);
+    if (t % kWave == 0) lds[t / kWave] = r;
+    __syncthreads();
+    MinMax g;
+#pragma unroll
+    for (int i = 0; i < kB / kWave; ++i) g.merge(lds[i].x, lds[i].y, as_u(lds[i].z));
+    const IntRange rg = int_range(BITS, affine != 0);
+    const IntCal cal = calibrate(g.mn, g.mx, rg, affine != 0);
+    if (blockIdx.x == 0 && t == 0) {
+        fq_int_params out;
+        out.scale = cal.scale;
+        out.zero_point = cal.zp;
+        out.real_min = (float)(rg.qmin - cal.zp) * cal.scale;
+        out.real_max = (float)(rg.qmax - cal.zp) * cal.scale;
+        *params = out;
+        const uint32_t f = (g.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+        if (flags && f) atomicOr(flags, f);
+    }
+    const IntQ q(cal.scale, cal.zp, rg);
+    if (q.zero) fq_int_gs_loop<BITS, 0>(IntTensorOp<BITS, 0>{q, cal.scale, cal.zp, codes, fq}, x, n, c, stride, v);
+    else if (q.div.fast) fq_int_gs_loop<BITS, 1>(IntTensorOp<BITS, 1>{q, cal.scale, cal.zp, codes, fq}, x, n, c, stride, v);
+    else fq_int_gs_loop<BITS, 2>(IntTensorOp<BITS, 2>{q, cal.scale, cal.zp, codes, fq}, x, n, c, stride, v);
+}
+
+// ---------------------------------------------------------------------------
 // Integer dequantize ([QAT] dequant(q) = (q - zero_point) * scale)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int sext4(uint32_t nib) { return ((int)(nib << 28)) >> 28; }
@@ -502,6 +577,27 @@ int params_from_partials(const void* workspace, unsigned nparts, int bits, int s
                          uint32_t* flags, hipStream_t stream) {
     k_params_int_final<<<1, kFT, 0, stream>>>((const float4*)workspace, (int)nparts, bits,
                                               scheme == FQ_AFFINE ? 1 : 0, params, flags);
+    return launched();
+}
+
+int fake_quant_from_partials(const float* x, int64_t n, int bits, int scheme, const void* workspace, unsigned nparts,
+                             fq_int_params* params, void* codes, float* fq, uint32_t* flags, hipStream_t stream) {
+    const bool al = aligned(x, 16) && aligned(fq, 16) && aligned(codes, bits == 8 ? 4 : 2);
+    if (!al || nparts > (unsigned)kFoldGsMaxParts) {
+        int st = params_from_partials(workspace, nparts, bits, scheme, params, flags, stream);
+        if (st != FQ_OK) return st;
+        return fq_fake_quant_int_tensor(x, n, bits, scheme, params, codes, fq, stream);
+    }
+    const unsigned G = grid_for((n + 3) / 4, kBlock, kFoldGsBlocksPerCu);
+    const int aff = scheme == FQ_AFFINE;
+    const float4* part = (const float4*)workspace;
+    uint8_t* cd = (uint8_t*)codes;
+    if (bits == 8)
+        k_fq_int_tensor_fold_gs<8, kFoldGsMaxParts><<<G, kBlock, 0, stream>>>(x, n, aff, part, (int)nparts, params,
+                                                                             cd, fq, flags);
+    else
+        k_fq_int_tensor_fold_gs<4, kFoldGsMaxParts><<<G, kBlock, 0, stream>>>(x, n, aff, part, (int)nparts, params,
+                                                                             cd, fq, flags);
     return launched();
 }
 

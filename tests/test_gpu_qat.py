@@ -99,7 +99,9 @@ def test_fp8_steps(fqlib, orc, fmt, rounding, wd):
     run_fp8(fqlib, orc, w0, grads_for(n, 12, 4), 1e-2, fmt, rounding, wd=wd, seed=7, offset=2, what="steps")
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 1023, (1 << 22) + 5])
+# the last size has more reduction tiles (8192 elements each) than the 2048
+# partials the requantize blocks fold, so the update workgroups loop over tiles
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 1023, (1 << 22) + 5, (1 << 24) + 40 * 8192 + 7])
 def test_sizes(fqlib, orc, n):
     w0 = (np.random.default_rng(n).standard_normal(n)).astype(np.float32)
     g = grads_for(n, 2, n + 1)
