@@ -352,7 +352,7 @@ def ops_next_percentile(fq, syn, torch, dev):
     for name, x, n in (("tensor_2^20", x1, n1), ("weights_2^24", w, r * c)):
         wsb = fq.fq_percentile_workspace_bytes(n)
         ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
-        ops.append(Op(f"percentile.{name}", "k_pct_init+k_pct_first+k_pct_second+k_pct_third",
+        ops.append(Op(f"percentile.{name}", "k_pct_init+k_pct_first+k_pct_second+k_pct_third+k_pct_final",
                       lambda x=x, n=n, ws=ws, wsb=wsb: fq.fq_tensor_params_percentile(
                           x, n, 8, fq.AFFINE, 0.001, ws, wsb, params, flags),
                       4 * n + 16))

@@ -112,9 +112,8 @@ int params_from_partials(const void* workspace, unsigned nparts, int bits, int s
 // falls back to otherwise.  Measured on the 2^24-element QAT step (update pass
 // capped at this many workgroups): 512 partials and 16 workgroups per CU ran the
 // step in 99.3-100.6 us cold against 101.4-102.9 for three launches (two boxes,
-// interleaved runs); 2048
-// partials 104.8-105.9, 256 partials 112.9-114.6 (an update pass of one
-// workgroup per CU), 8 workgroups per CU 101.6-101.8.
+// interleaved runs); 2048 partials 104.8-105.9, 256 partials 112.9-114.6 (an
+// update pass of one workgroup per CU), 8 workgroups per CU 101.6-101.8.
 constexpr int kFoldGsMaxParts = 512;
 constexpr int kFoldGsBlocksPerCu = 16;
 int fake_quant_from_partials(const float* x, int64_t n, int bits, int scheme, const void* workspace, unsigned nparts,

@@ -19,16 +19,21 @@
 // (integer counts: the result does not depend on their order).  Atomics on one
 // address serialise, so the device histogram has four replicas (workgroup b adds
 // into replica b mod 4) and the grid is capped at 256 workgroups of 1024 threads
-// (grid-stride loop).  A counter names the last workgroup to finish the pass;
-// it sums the replicas, and one of
-// its waves narrows prefix and rank of both statistics; after the last pass it
-// derives the parameters.  No separate select launches.
+// (grid-stride loop).
+//
+// The digit a pass fixes is selected at the start of the next launch: every
+// workgroup of that launch sums the replicas and narrows prefix and rank of both
+// statistics itself (the same integer counts give every workgroup the same
+// selection; workgroup 0 stores it for the launches after), overlapping its first
+// loads of x.  The launch boundary orders the counts before those reads, so no
+// pass needs a counter or a fence.  A one-workgroup launch selects the last digit
+// and derives the parameters.
 //
 // The second pass also copies the keys that share either 11-bit prefix into a
 // per-workgroup slice of the workspace (sized for one key in 16 of the
 // workgroup's share; typically a few percent match); the third pass then reads
-// only those slices, or x again if any slice overflowed.  Four launches; x is
-// read twice (three times on overflow).
+// only those slices, or x again if any slice overflowed.  Five launches (zeroing,
+// three passes, the last selection); x is read twice (three times on overflow).
 #include <cmath>
 
 #include "fq_device.h"
@@ -39,9 +44,13 @@ using namespace fqk;
 namespace {
 
 // 1024 threads per workgroup (one workgroup of 16 waves per CU at the 256-workgroup
-// cap): 39.0-39.5 / 63.8-64.4 us at 2^20 / 2^24, against 42.4-42.9 / 68.0-68.5 us
-// with 512 and 54.8-55.0 / 90.2-90.4 us with 256; with 1024 threads a cap of 128
-// or 512 workgroups was slower at 2^24 (71.4-71.9 / 81.8-81.9 us).
+// cap): 34.4-35.6 / 55.8-56.5 us cold at 2^20 / 2^24.  Measured slower at 2^24:
+// 512 threads with 512 or 1024 workgroups (59.4-60.0 / 74.8-74.9 us), 1024 threads
+// with 512 workgroups (69.0), eight 16-byte loads in flight (61.4-61.6), eight
+// replicas (58.5-58.6); two replicas, eight LDS copies, copies picked by lane,
+// plain loads of the counts and zeroing the later histograms in the first pass
+// timed the same.  (The selection of a digit by the last workgroup of its own
+// pass, found with an agent-scope release counter, took 63.5-64.2 us at 2^24.)
 #ifndef FQ_PCT_THREADS
 #define FQ_PCT_THREADS 1024
 #endif
@@ -62,14 +71,19 @@ constexpr int64_t kMaxHistBlocks = FQ_PCT_MAX_BLOCKS;
 __host__ __device__ constexpr int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __host__ __device__ constexpr int digit_bins(int p) { return p == 2 ? 1024 : 2048; }
 
-struct PctState {
-    uint64_t hist[kPasses][kR][2][kMaxBins];  // zeroed by k_pct_init
+// the selection after a pass's digit: per statistic the key prefix fixed so far
+// and the rank among the keys that share it
+struct PctSel {
     uint64_t rank[2];
     uint64_t nfin;
     uint32_t prefix[2];
     uint32_t mask;
     uint32_t shared;  // the two prefixes agree: one histogram serves both
-    uint32_t done[kPasses];  // workgroups that finished each pass
+};
+
+struct PctState {
+    uint64_t hist[kPasses][kR][2][kMaxBins];  // zeroed by k_pct_init
+    PctSel sel[kPasses - 1];  // after the digits of passes 0 and 1 (block 0 of the next launch stores it)
     uint32_t overflow;  // a candidate slice overflowed: the third pass reads x
     uint32_t cnt[kMaxHistBlocks];  // candidates kept by each workgroup
 };
@@ -100,15 +114,7 @@ constexpr int kInitWords = kPasses * kR * 2 * kMaxBins;
 __global__ __launch_bounds__(256) void k_pct_init(PctState* __restrict__ st) {
     uint64_t* h = &st->hist[0][0][0][0];
     for (int i = blockIdx.x * 256 + threadIdx.x; i < kInitWords; i += gridDim.x * 256) h[i] = 0;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        st->rank[0] = st->rank[1] = 0;
-        st->nfin = 0;
-        st->prefix[0] = st->prefix[1] = 0;
-        st->mask = 0;
-        st->shared = 1;
-        for (int p = 0; p < kPasses; ++p) st->done[p] = 0;
-        st->overflow = 0;
-    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) st->overflow = 0;
 }
 
 // f(e) for each thread's group of 4 kU elements (kU 16-byte chunks), the loop
@@ -137,14 +143,16 @@ __device__ __forceinline__ void load_group(const float* __restrict__ x, int64_t 
     }
 }
 
-template <bool AL, typename F>
-__device__ __forceinline__ void for_each_group(const float* __restrict__ x, int64_t n, F&& f) {
+// pro() runs once, by every thread, after the first group's loads are issued
+template <bool AL, typename P, typename F>
+__device__ __forceinline__ void for_each_group(const float* __restrict__ x, int64_t n, P&& pro, F&& f) {
     const int64_t nfull = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * kPB;
     const int64_t step = stride * kU;
     float e[4 * kU];
     int64_t c0 = (int64_t)blockIdx.x * kPB;
     if (c0 < nfull) load_group<AL>(x, nfull, c0, stride, e);
+    pro();
     for (; c0 < nfull; c0 += step) {
         float nxt[4 * kU];
         load_group<AL>(x, nfull, c0 + step, stride, nxt);  // past the end: all NaN
@@ -162,46 +170,17 @@ __device__ __forceinline__ void for_each_group(const float* __restrict__ x, int6
 }
 
 // Adds the non-zero counts of an LDS histogram (BINS bins, cnt(b) the count of
-// bin b) to the device histogram g with agent-scope atomics: every add of the
-// thread is issued before any is awaited.  The selecting workgroup sees them
-// through the release / acquire pair of last_to_finish.
+// bin b) to the device histogram g with agent-scope atomics (no value returned);
+// the next launch reads the sums.
 template <int BINS, typename C>
 __device__ __forceinline__ void flush_bins(uint64_t* __restrict__ g, C&& cnt) {
-    constexpr int PER = BINS / kPB;
-    uint64_t r[PER];
+    static_assert(BINS % kPB == 0, "whole bins per thread");
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
+    for (int j = 0; j < BINS / kPB; ++j) {
         const int b = threadIdx.x + j * kPB;
         const uint32_t c = cnt(b);
-        r[j] = c ? __hip_atomic_fetch_add(&g[b], (uint64_t)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        if (c) __hip_atomic_fetch_add(&g[b], (uint64_t)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    uint64_t all = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) all |= r[j];
-    asm volatile("" ::"v"(all));
-}
-
-// Taken by every workgroup after its flushes: the one that finishes the pass
-// last gets true.  Memory order (HIP's scoped C++ model): the barrier orders
-// every wave's histogram adds before thread 0's increment, which is a release at
-// agent scope; the increments form one release sequence on `done`, so the acquire
-// fence that the last workgroup alone runs after its own increment makes every
-// other workgroup's adds happen-before its loads of the counts.  The release
-// writes back this die's dirty L2 lines once per workgroup; only the selecting
-// workgroup pays the acquire's L2 invalidation.  One counter for the <= 256
-// workgroups (a two-level counter over four replicas measured 1.5 us slower at
-// 2^20).
-__device__ __forceinline__ bool last_to_finish(uint32_t* done) {
-    __shared__ bool s_last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const bool last =
-            __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_last = last;
-    }
-    __syncthreads();
-    return s_last;
 }
 
 struct SelectArgs {
@@ -221,128 +200,134 @@ __device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t v) {
     return v;
 }
 
-// Run by the whole last workgroup of pass PASS.  The replicas are summed into
-// `sh` (LDS, 2 BINS counts); then the first wave, lane l holding bins
-// [l PER, (l + 1) PER), finds the bin holding each statistic's rank: it fixes the
-// next digit, and the rank becomes the rank within that bin.  After the last
-// pass the prefixes are the selected keys and the parameters follow.
+// The selection before any digit: both statistics start with the empty prefix.
+__device__ __forceinline__ PctSel no_selection() {
+    PctSel z;
+    z.rank[0] = z.rank[1] = 0;
+    z.nfin = 0;
+    z.prefix[0] = z.prefix[1] = 0;
+    z.mask = 0;
+    z.shared = 1;
+    return z;
+}
+
+// Run by every thread of a workgroup, after the launch that filled pass PASS's
+// histograms: the replicas are summed into `sh` (LDS, 2 BINS counts; loaded at
+// agent scope), then the first wave, lane l holding bins [l PER, (l + 1) PER),
+// finds the bin holding each statistic's rank: that bin fixes the next digit,
+// and the rank becomes the rank within the bin.  The first digit also yields the
+// count of finite values and the two ranks ([QAT] per_tensor_percentile:
+// floor(cf last), ceil((1 - cf) last) in f64).  The result is left in *out (LDS)
+// and returned to every thread; every workgroup of a launch derives the same one
+// from the same integer counts.
 template <int PASS>
-__device__ void select_digit(PctState* __restrict__ st, int64_t n, const SelectArgs& a, uint64_t* sh) {
+__device__ PctSel select_block(PctState* __restrict__ st, const PctSel& prev, double cf, uint64_t* sh,
+                               PctSel* out) {
     constexpr int BINS = digit_bins(PASS), SHIFT = digit_shift(PASS);
     constexpr int PER = BINS / kWave;
-    const bool shared = st->shared != 0;
+    static_assert(BINS % kPB == 0, "whole bins per thread");
+    const bool shared = prev.shared != 0;
     const int nstat = shared ? 1 : 2;
     for (int s = 0; s < nstat; ++s) {
+        uint64_t c[BINS / kPB][kR];
 #pragma unroll
-        for (int j = 0; j < BINS / kPB; ++j) {
-            const int b = threadIdx.x + j * kPB;
-            uint64_t c[kR];
-            // the counts were added by other workgroups: read them at device scope
+        for (int j = 0; j < BINS / kPB; ++j)
 #pragma unroll
             for (int r = 0; r < kR; ++r)
-                c[r] = __hip_atomic_load(&st->hist[PASS][r][s][b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                c[j][r] = __hip_atomic_load(&st->hist[PASS][r][s][threadIdx.x + j * kPB], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < BINS / kPB; ++j) {
             uint64_t t = 0;
 #pragma unroll
-            for (int r = 0; r < kR; ++r) t += c[r];
-            sh[s * BINS + b] = t;
+            for (int r = 0; r < kR; ++r) t += c[j][r];
+            sh[s * BINS + threadIdx.x + j * kPB] = t;
         }
     }
     __syncthreads();
-    if (threadIdx.x >= kWave) return;
-    const int lane = threadIdx.x;
-    uint64_t nfin = st->nfin;
-    uint64_t rank[2] = {st->rank[0], st->rank[1]};
-    uint32_t prefix[2] = {st->prefix[0], st->prefix[1]};
-    uint64_t hb[PER];
-    uint64_t sum = 0;
-    auto load = [&](int s) {
-        sum = 0;
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        uint64_t nfin = prev.nfin;
+        uint64_t rank[2] = {prev.rank[0], prev.rank[1]};
+        uint32_t prefix[2] = {prev.prefix[0], prev.prefix[1]};
+        uint64_t hb[PER];
+        uint64_t sum = 0;
+        auto load = [&](int s) {
+            sum = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            hb[j] = sh[s * BINS + lane * PER + j];
-            sum += hb[j];
+            for (int j = 0; j < PER; ++j) {
+                hb[j] = sh[s * BINS + lane * PER + j];
+                sum += hb[j];
+            }
+        };
+        load(0);
+        uint64_t incl = wave_inclusive_scan(sum);
+        if (PASS == 0) {
+            // every finite value lands in a bin of the first pass
+            nfin = __shfl(incl, kWave - 1);
+            if (nfin > 0) {
+                const uint64_t last = nfin - 1;
+                const uint64_t lo = (uint64_t)floor(cf * (double)last);
+                const uint64_t hi = (uint64_t)ceil((1.0 - cf) * (double)last);
+                rank[0] = lo < last ? lo : last;
+                rank[1] = hi < last ? hi : last;
+            }
         }
-    };
-    load(0);
-    uint64_t incl = wave_inclusive_scan(sum);
-    if (PASS == 0) {
-        // every finite value lands in a bin of the first pass: the count of
-        // finite values and the two ranks follow from the total
-        nfin = __shfl(incl, kWave - 1);
         if (nfin > 0) {
-            const uint64_t last = nfin - 1;
-            const uint64_t lo = (uint64_t)floor(a.cf * (double)last);
-            const uint64_t hi = (uint64_t)ceil((1.0 - a.cf) * (double)last);
-            rank[0] = lo < last ? lo : last;
-            rank[1] = hi < last ? hi : last;
-        }
-    }
-    if (nfin > 0) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            if (s == 1 && !shared) {
-                load(1);
-                incl = wave_inclusive_scan(sum);
-            }
-            const uint64_t excl = incl - sum, r = rank[s];
-            const bool mine = excl <= r && r < incl;
-            const uint64_t bal = __ballot(mine);
-            uint32_t digit = 0;
-            uint64_t within = 0;
-            if (mine) {
-                uint64_t below = excl;
-#pragma unroll
-                for (int j = 0; j < PER; ++j) {
-                    if (r < below + hb[j]) {
-                        digit = (uint32_t)(lane * PER + j);
-                        within = r - below;
-                        break;
-                    }
-                    below += hb[j];
+            for (int s = 0; s < 2; ++s) {
+                if (s == 1 && !shared) {
+                    load(1);
+                    incl = wave_inclusive_scan(sum);
                 }
+                const uint64_t excl = incl - sum, r = rank[s];
+                const bool mine = excl <= r && r < incl;
+                const uint64_t bal = __ballot(mine);
+                uint32_t digit = 0;
+                uint64_t within = 0;
+                if (mine) {
+                    uint64_t below = excl;
+#pragma unroll
+                    for (int j = 0; j < PER; ++j) {
+                        if (r < below + hb[j]) {
+                            digit = (uint32_t)(lane * PER + j);
+                            within = r - below;
+                            break;
+                        }
+                        below += hb[j];
+                    }
+                }
+                const int src = bal ? __builtin_ctzll(bal) : 0;
+                prefix[s] |= (uint32_t)__shfl((int)digit, src) << SHIFT;
+                rank[s] = __shfl(within, src);
             }
-            const int src = bal ? __builtin_ctzll(bal) : 0;
-            prefix[s] |= (uint32_t)__shfl((int)digit, src) << SHIFT;
-            rank[s] = __shfl(within, src);
+        }
+        if (lane == 0) {
+            PctSel r;
+            r.nfin = nfin;
+            r.rank[0] = rank[0];
+            r.rank[1] = rank[1];
+            r.prefix[0] = prefix[0];
+            r.prefix[1] = prefix[1];
+            r.mask = prev.mask | ((uint32_t)(BINS - 1) << SHIFT);
+            r.shared = prefix[0] == prefix[1] ? 1u : 0u;
+            *out = r;
         }
     }
-    if (lane != 0) return;
-    st->nfin = nfin;
-    st->rank[0] = rank[0];
-    st->rank[1] = rank[1];
-    st->prefix[0] = prefix[0];
-    st->prefix[1] = prefix[1];
-    st->mask |= (uint32_t)(BINS - 1) << SHIFT;
-    st->shared = prefix[0] == prefix[1] ? 1u : 0u;
-    if (PASS != kPasses - 1) return;
-    const float mn = nfin > 0 ? key_value(prefix[0]) : __builtin_inff();
-    const float mx = nfin > 0 ? key_value(prefix[1]) : -__builtin_inff();
-    const IntRange rg = int_range(a.bits, a.affine != 0);
-    const IntCal cal = calibrate(mn, mx, rg, a.affine != 0);
-    fq_int_params out;
-    out.scale = cal.scale;
-    out.zero_point = cal.zp;
-    out.real_min = (float)(rg.qmin - cal.zp) * cal.scale;
-    out.real_max = (float)(rg.qmax - cal.zp) * cal.scale;
-    *a.params = out;
-    const uint32_t f = ((int64_t)nfin < n ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
-    if (a.flags && f) atomicOr(a.flags, f);
+    __syncthreads();
+    return *out;
 }
 
 // first pass: the top 11 bits of every finite key, kCopies LDS histograms (waves
 // w and w + kCopies share one)
 template <bool AL>
-__global__ __launch_bounds__(kPB) void k_pct_first(const float* __restrict__ x, int64_t n, PctState* __restrict__ st,
-                                                   SelectArgs a) {
+__global__ __launch_bounds__(kPB) void k_pct_first(const float* __restrict__ x, int64_t n, PctState* __restrict__ st) {
     constexpr int BINS = digit_bins(0), SHIFT = digit_shift(0);
-    // the pass's u32 copies, then (after the flush) the select's u64 sums
-    __shared__ uint64_t lds[2 * BINS];
-    static_assert(kCopies * BINS * 4 <= sizeof(lds), "histogram copies fit the select buffer");
-    uint32_t* h = reinterpret_cast<uint32_t*>(lds);
+    __shared__ uint32_t h[kCopies * BINS];
     for (int i = threadIdx.x; i < kCopies * BINS; i += kPB) h[i] = 0;
     __syncthreads();
     uint32_t* hw = h + ((threadIdx.x / kWave) % kCopies) * BINS;
-    for_each_group<AL>(x, n, [&](const float (&e)[4 * kU]) {
+    for_each_group<AL>(x, n, [] {}, [&](const float (&e)[4 * kU]) {
 #pragma unroll
         for (int i = 0; i < 4 * kU; ++i)
             if (finite(e[i])) atomicAdd(&hw[sort_key(e[i]) >> SHIFT], 1u);
@@ -354,28 +339,39 @@ __global__ __launch_bounds__(kPB) void k_pct_first(const float* __restrict__ x, 
         for (int w = 0; w < kCopies; ++w) c += h[w * BINS + b];
         return c;
     });
-    if (last_to_finish(&st->done[0])) select_digit<0>(st, n, a, lds);
 }
 
-// second pass: the middle 11 bits of the keys that share a statistic's 11-bit
-// prefix; those keys are also kept in this workgroup's candidate slice
+// second pass: every workgroup first derives the first digit from the first
+// pass's histogram (while its first loads of x are in flight; workgroup 0 stores
+// the selection for the launches after it), then counts the middle 11 bits of the
+// keys that share a statistic's 11-bit prefix; those keys are also kept in this
+// workgroup's candidate slice
 template <bool AL>
 __global__ __launch_bounds__(kPB) void k_pct_second(const float* __restrict__ x, int64_t n,
                                                     PctState* __restrict__ st, uint32_t* __restrict__ cand,
-                                                    int64_t cap, SelectArgs a) {
+                                                    int64_t cap, double cf) {
     constexpr int BINS = digit_bins(1), SHIFT = digit_shift(1);
-    __shared__ uint64_t lds[2 * BINS];
+    __shared__ uint64_t sh[2 * digit_bins(0)];
+    __shared__ PctSel s_sel;
+    __shared__ uint32_t h[2 * BINS];
     __shared__ uint32_t s_cnt;
-    uint32_t* h0 = reinterpret_cast<uint32_t*>(lds);
-    uint32_t* h1 = h0 + BINS;
-    for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h0[i] = 0;
+    uint32_t* h0 = h;
+    uint32_t* h1 = h + BINS;
+    for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h[i] = 0;
     if (threadIdx.x == 0) s_cnt = 0;
-    const uint32_t mask = st->mask, p0 = st->prefix[0], p1 = st->prefix[1];
-    const bool shared = st->shared != 0;
+    uint32_t mask = 0, p0 = 0, p1 = 0;
+    bool shared = true;
     uint32_t* slice = cand + blockIdx.x * cap;
     const int lane = threadIdx.x % kWave;
-    __syncthreads();
-    for_each_group<AL>(x, n, [&](const float (&e)[4 * kU]) {
+    for_each_group<AL>(x, n, [&] {
+        // the barriers in select_block also order the zeroing above before the counts
+        const PctSel sel = select_block<0>(st, no_selection(), cf, sh, &s_sel);
+        if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[0] = sel;
+        mask = sel.mask;
+        p0 = sel.prefix[0];
+        p1 = sel.prefix[1];
+        shared = sel.shared != 0;
+    }, [&](const float (&e)[4 * kU]) {
         uint32_t keys[4 * kU];
         uint32_t mbits = 0;  // bit i: element i is a candidate
 #pragma unroll
@@ -418,30 +414,34 @@ __global__ __launch_bounds__(kPB) void k_pct_second(const float* __restrict__ x,
         st->cnt[blockIdx.x] = (int64_t)s_cnt < cap ? s_cnt : (uint32_t)cap;
         if ((int64_t)s_cnt > cap) atomicOr(&st->overflow, 1u);
     }
-    if (last_to_finish(&st->done[1])) select_digit<1>(st, n, a, lds);
 }
 
-// third pass: the last 10 bits of the keys that share a statistic's 22-bit
-// prefix, from this workgroup's candidates (or from x after an overflow)
+// third pass: every workgroup derives the second digit (workgroup 0 stores the
+// selection), then counts the last 10 bits of the keys that share a statistic's
+// 22-bit prefix, from this workgroup's candidates (or from x after an overflow)
 template <bool AL>
 __global__ __launch_bounds__(kPB) void k_pct_third(const float* __restrict__ x, int64_t n, PctState* __restrict__ st,
-                                                   const uint32_t* __restrict__ cand, int64_t cap, SelectArgs a) {
+                                                   const uint32_t* __restrict__ cand, int64_t cap) {
     constexpr int BINS = digit_bins(2), SHIFT = digit_shift(2);
-    __shared__ uint64_t lds[2 * BINS];
-    uint32_t* h0 = reinterpret_cast<uint32_t*>(lds);
-    uint32_t* h1 = h0 + BINS;
-    for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h0[i] = 0;
-    const uint32_t mask = st->mask, p0 = st->prefix[0], p1 = st->prefix[1];
-    const bool shared = st->shared != 0;
+    __shared__ uint64_t sh[2 * digit_bins(1)];
+    __shared__ PctSel s_sel;
+    __shared__ uint32_t h[2 * BINS];
+    uint32_t* h0 = h;
+    uint32_t* h1 = h + BINS;
+    for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h[i] = 0;
+    const PctSel prev = st->sel[0];
+    const PctSel sel = select_block<1>(st, prev, 0.0, sh, &s_sel);
+    if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[1] = sel;
+    const uint32_t mask = sel.mask, p0 = sel.prefix[0], p1 = sel.prefix[1];
+    const bool shared = sel.shared != 0;
     const bool from_x = st->overflow != 0;
-    __syncthreads();
     auto count = [&](uint32_t k) {
         const uint32_t bin = (k >> SHIFT) & (BINS - 1);
         if ((k & mask) == p0) atomicAdd(&h0[bin], 1u);
         if (!shared && (k & mask) == p1) atomicAdd(&h1[bin], 1u);
     };
     if (from_x) {
-        for_each_group<AL>(x, n, [&](const float (&e)[4 * kU]) {
+        for_each_group<AL>(x, n, [] {}, [&](const float (&e)[4 * kU]) {
 #pragma unroll
             for (int i = 0; i < 4 * kU; ++i)
                 if (finite(e[i])) count(sort_key(e[i]));
@@ -454,16 +454,39 @@ __global__ __launch_bounds__(kPB) void k_pct_third(const float* __restrict__ x, 
     __syncthreads();
     flush_bins<BINS>(st->hist[2][blockIdx.x % kR][0], [&](int b) { return h0[b]; });
     if (!shared) flush_bins<BINS>(st->hist[2][blockIdx.x % kR][1], [&](int b) { return h1[b]; });
-    if (last_to_finish(&st->done[2])) select_digit<2>(st, n, a, lds);
+}
+
+// one workgroup: the last digit fixes both keys, whose values are the clip
+// range ([QAT] from_minmax(sorted[lo], sorted[hi]))
+__global__ __launch_bounds__(kPB) void k_pct_final(PctState* __restrict__ st, int64_t n, SelectArgs a) {
+    __shared__ uint64_t sh[2 * digit_bins(2)];
+    __shared__ PctSel s_sel;
+    const PctSel prev = st->sel[1];
+    const PctSel sel = select_block<2>(st, prev, a.cf, sh, &s_sel);
+    if (threadIdx.x != 0) return;
+    const uint64_t nfin = sel.nfin;
+    const float mn = nfin > 0 ? key_value(sel.prefix[0]) : __builtin_inff();
+    const float mx = nfin > 0 ? key_value(sel.prefix[1]) : -__builtin_inff();
+    const IntRange rg = int_range(a.bits, a.affine != 0);
+    const IntCal cal = calibrate(mn, mx, rg, a.affine != 0);
+    fq_int_params out;
+    out.scale = cal.scale;
+    out.zero_point = cal.zp;
+    out.real_min = (float)(rg.qmin - cal.zp) * cal.scale;
+    out.real_max = (float)(rg.qmax - cal.zp) * cal.scale;
+    *a.params = out;
+    const uint32_t f = ((int64_t)nfin < n ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
+    if (a.flags && f) atomicOr(a.flags, f);
 }
 
 template <bool AL>
 void launch_passes(const float* x, int64_t n, PctState* st, uint32_t* cand, int64_t cap, const SelectArgs& a,
                    hipStream_t stream) {
     const unsigned G = (unsigned)hist_blocks(n);
-    k_pct_first<AL><<<G, kPB, 0, stream>>>(x, n, st, a);
-    k_pct_second<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap, a);
-    k_pct_third<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap, a);
+    k_pct_first<AL><<<G, kPB, 0, stream>>>(x, n, st);
+    k_pct_second<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap, a.cf);
+    k_pct_third<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap);
+    k_pct_final<<<1, kPB, 0, stream>>>(st, n, a);
 }
 
 }  // namespace
