@@ -325,10 +325,12 @@ size_t fq_percentile_workspace_bytes(int64_t n);
  * FQ_FLAG_DEGENERATE as well.  clip_fraction cf in [0, 0.5) (FQ_E_INVALID
  * otherwise; 0 gives the min / max calibration).  workspace: device memory of
  * fq_percentile_workspace_bytes(n), 16-byte aligned, cleared by the call itself,
- * contents not kept.  params, flags: device, as fq_tensor_params_int.  Four
- * launches (three passes that narrow both order statistics by 11, 11 and 10 bits
- * of an order-preserving key; x is read twice, the last pass reading only the
- * candidates the second one kept, or x once more if they did not fit); no host
+ * contents not kept.  params, flags: device, as fq_tensor_params_int.  Five
+ * launches (zeroing, three passes that narrow both order statistics by 11, 11
+ * and 10 bits of an order-preserving key, each pass's digit selected at the start
+ * of the next launch, and a one-workgroup launch for the last digit and the
+ * parameters; x is read twice, the third pass reading only the candidates the
+ * second one kept, or x once more if they did not fit); no host
  * synchronisation. */
 int fq_tensor_params_percentile(const float* x, int64_t n, int bits, int scheme, double clip_fraction,
                                 void* workspace, size_t workspace_bytes, fq_int_params* params, uint32_t* flags,
@@ -387,7 +389,9 @@ typedef struct {
  * fq_workspace_bytes(n)) and fake_quant_int with `rounding` (stochastic: the
  * stream of fq_fake_quant_int_tensor_sr at seed / offset).  codes (as
  * fq_fake_quant_int_tensor) and view (float32 [n], the fake-quant view) may each
- * be NULL, not both.  Four launches, no host synchronisation. */
+ * be NULL, not both.  Nearest rounding: two launches (the requantize folds the
+ * update pass's partials) when master, codes and view are 16-byte aligned, else
+ * three; stochastic rounding: three.  No host synchronisation. */
 int fq_qat_step_int(float* master, const float* grad, float* m, float* v, int64_t n, const fq_adamw_config* cfg,
                     int64_t t, int bits, int scheme, int rounding, uint64_t seed, uint64_t offset, void* workspace,
                     size_t workspace_bytes, fq_int_params* params, void* codes, float* view, uint32_t* flags,
