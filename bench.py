@@ -39,6 +39,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -851,9 +852,25 @@ def traffic_record(kernel):
         return None
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/|\s+', re.S)
+
+
+def code_only(text):
+    """C / C++ source with its comments removed and every run of whitespace
+    folded to one space (string and character literals kept as they are), so
+    that editing a comment does not count as a change of the kernel."""
+    def keep(m):
+        t = m.group(0)
+        if t[0] in "\"'":
+            return t
+        return "\0"
+    return re.sub("\0+", " ", _CODE_TOKENS.sub(keep, text)).strip()
+
+
 def sources_sha(kernel):
-    """sha256 over the sources `kernel` is built from: the .hip file(s) that
-    define it, every header of the package and the public header."""
+    """sha256 over the code (comments and layout left out) of the sources
+    `kernel` is built from: the .hip file(s) that define it, every header of the
+    package and the public header."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fake_quant_amd", "csrc")
     files = []
@@ -864,7 +881,7 @@ def sources_sha(kernel):
     files.append(os.path.join(ROOT, "include", "fq.h"))
     for p in files:
         h.update(os.path.basename(p).encode())
-        h.update(open(p, "rb").read())
+        h.update(code_only(open(p, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

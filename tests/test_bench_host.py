@@ -212,3 +212,16 @@ def test_ranges_cover_and_align():
         assert rs[0][0] == 0 and rs[-1][1] == n and len(rs) <= parts
         assert all(a[1] == b[0] for a, b in zip(rs, rs[1:]))
         assert all(a % align == 0 for a, _ in rs)
+
+
+def test_sources_sha_ignores_comments_only():
+    # editing a comment or the layout keeps the hash that ties the counter summary
+    # to the kernel sources; editing code changes it
+    import bench
+    base = 'int f(int a) { return a + 1; } // one\n/* two */ const char* s = "/* kept */";\n'
+    same = '// header\nint f(int a)\n{\n    return a + 1;  /* changed */\n}\nconst char* s = "/* kept */";'
+    other = 'int f(int a) { return a + 2; }\nconst char* s = "/* kept */";'
+    strv = 'int f(int a) { return a + 1; } const char* s = "/*  kept */";'
+    assert bench.code_only(base) == bench.code_only(same)
+    assert bench.code_only(base) != bench.code_only(other)
+    assert bench.code_only(base) != bench.code_only(strv)  # string contents are code
