@@ -832,6 +832,32 @@ def host_cpu():
     return dict(cores_available=len(os.sched_getaffinity(0)), cpu_model=model)
 
 
+SMI_KEYS = ("clock", "temperature", "power", "serial", "perf")
+
+
+def smi_snapshot():
+    """The GPU's clocks, temperatures, power limit and serial as rocm-smi reports
+    them (the fields of card 0 whose names mention one of SMI_KEYS), or None
+    where rocm-smi is missing or fails.  Read from sysfs by a child process; it
+    does not touch the GPU's queues."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showtemp", "--showmaxpower", "--showpower",
+                            "--showserial", "--showperflevel", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        card = json.loads(r.stdout).get("card0", {})
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    return {k: v for k, v in card.items() if any(w in k.lower() for w in SMI_KEYS)} or None
+
+
+def device_info(torch):
+    """Static properties of cuda:0 as torch reports them."""
+    p = torch.cuda.get_device_properties(0)
+    return dict(name=p.name, arch=getattr(p, "gcnArchName", None), compute_units=p.multi_processor_count,
+                total_memory=p.total_memory)
+
+
 def traffic_record(kernel):
     """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, scaled by the
     copy reference) from the committed rocprofv3 counter summary, if it was taken
@@ -921,6 +947,7 @@ def main():
         log(f"first call: {op.name}")
         op.fn()
         torch.cuda.synchronize()
+    smi_before = smi_snapshot()  # before the warm-up steps, which bring the clocks back up
     for _ in range(args.warmup):
         for op in ops:
             op.fn()
@@ -941,6 +968,7 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    smi_after = smi_snapshot()
     total_ms = start.elapsed_time(end)
     per_op_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
                  for i in range(len(ops))]
@@ -1008,6 +1036,8 @@ def main():
         "per_op_cold_warm": per_op,
         "copy_f32_ceiling": copy_ceiling,
         "next_rows": next_rows,
+        # what the box reported before the warm-up steps and right after the timed ones
+        "device": dict(device_info(torch), smi_before=smi_before, smi_after_timed=smi_after),
     }
     print(json.dumps(out), flush=True)
 
