@@ -123,11 +123,12 @@ def test_unaligned_view_and_dirty_workspace(fqlib, orc):
 
 
 def test_candidate_slice_overflow(fqlib, orc):
-    # 2^20 elements: 2^18 16-byte chunks over 256 histogram workgroups of 256
+    # 2^20 elements: 2^18 16-byte chunks over 64 histogram workgroups of 1024
     # threads, chunk c taken by thread c mod 65536, so workgroup 0 owns the chunks
-    # with c mod 65536 < 256.  Filling exactly those with the tensor's top value
-    # sends 4096 keys into workgroup 0's candidate slice (room for about 1 in 16)
-    # while the other slices stay small: the last pass must fall back to x.
+    # with c mod 65536 < 1024.  Filling those with c mod 65536 < 256 with the
+    # tensor's top value sends 4096 keys into workgroup 0's candidate slice (room
+    # for about 1 in 16) while the other slices stay small: the third pass must
+    # fall back to x.
     n = 1 << 20
     v = (np.random.default_rng(14).standard_normal(n) * 0.1).astype(np.float32)
     chunks = v.reshape(-1, 4)
@@ -135,3 +136,41 @@ def test_candidate_slice_overflow(fqlib, orc):
     x = torch.from_numpy(v).cuda()
     for cf, scheme in ((0.001, 1), (0.0001, 0), (0.01, 1)):
         check(fqlib, orc, x, 8, scheme, cf, "one slice overflows")
+
+
+def test_many_candidates_per_slice(fqlib, orc):
+    # values +-2^e (1 + u / 8) for 32 exponents e: each sign and exponent is one
+    # 11-bit prefix, so the two selected prefixes hold 1/32 of the elements, about
+    # 512 keys in each workgroup's candidate slice at 2^20 elements (many
+    # candidates, but fewer than a slice holds, 1088)
+    n = 1 << 20
+    rng = np.random.default_rng(21)
+    e = rng.integers(0, 32, n).astype(np.float64)
+    v = (np.exp2(e) * (1.0 + rng.random(n) / 8.0)).astype(np.float32)
+    v[rng.random(n) < 0.5] *= -1.0
+    x = torch.from_numpy(v).cuda()
+    for bits, scheme, cf in ((8, 1, 0.001), (4, 0, 0.01), (8, 0, 0.3)):
+        check(fqlib, orc, x, bits, scheme, cf, "many candidates per slice")
+
+
+def test_selected_bins_of_known_size(fqlib, orc):
+    # ranks lo and hi (cf 0.25) inside prefixes of exactly 128 keys in every
+    # workgroup's share: per 16384-element share of the 64 histogram workgroups at
+    # 2^20 elements, 4000 values in [0.5, 0.75), 128 in [1, 1.25) (the bin of rank
+    # lo), 8128 in [2, 2.5), 128 in [4, 5) (the bin of rank hi) and 4000 in [8, 10),
+    # so every candidate slice holds exactly 256 keys
+    n = 1 << 20
+    rng = np.random.default_rng(22)
+    wg = ((np.arange(n) // 4) % 65536) // 1024
+    v = np.empty(n, np.float32)
+    parts = ((4000, 0.5, 0.75), (128, 1.0, 1.25), (8128, 2.0, 2.5), (128, 4.0, 5.0), (4000, 8.0, 10.0))
+    for b in range(64):
+        idx = rng.permutation(np.flatnonzero(wg == b))
+        k = 0
+        for cnt, lo, hi in parts:
+            v[idx[k:k + cnt]] = rng.uniform(lo, hi, cnt).astype(np.float32)
+            k += cnt
+        assert k == idx.size
+    x = torch.from_numpy(v).cuda()
+    ref = check(fqlib, orc, x, 8, 1, 0.25, "selected bins of known size")
+    assert 1.0 <= ref["sel_min"] < 1.25 and 4.0 <= ref["sel_max"] < 5.0
