@@ -118,3 +118,51 @@ def test_nvfp4_drawn(fqlib, orc, n, log_mag, seed, specials):
     assert_bits(to_np(r["scales"]), ref["sbytes"], "block scales")
     assert_bits(to_np(r["q"]), ref["q"], "codes")
     assert_f32(to_np(r["fq"]), ref["fq"], "fq")
+
+
+@SETTINGS
+@given(n=st.integers(1, 300000), bits=st.sampled_from([4, 8]), scheme=st.sampled_from([0, 1]),
+       rounding=st.sampled_from([0, 0, 1]), wd=st.sampled_from([0.0, 0.01]), off=st.sampled_from([0, 0, 1, 3]),
+       log_mag=st.floats(-6, 3), seed=st.integers(0, 2**31))
+def test_qat_int_drawn(fqlib, orc, n, bits, scheme, rounding, wd, off, log_mag, seed):
+    # the integer QAT step over two steps: nearest rounding on aligned buffers
+    # takes the two-launch form (the requantize folds the update's partials),
+    # stochastic rounding or a misaligned view (off > 0) the three-launch one
+    log(f"qat drawn n={n} bits={bits} scheme={scheme} rounding={rounding} wd={wd} off={off}")
+    rng = np.random.default_rng(seed)
+    w0 = (rng.standard_normal(n) * 10.0 ** log_mag).astype(np.float32)
+    grads = [rng.standard_normal(n).astype(np.float32) for _ in range(2)]
+    lr = 1e-2
+    cfg = fqlib.adamw_config(lr, weight_decay=wd)
+    wb = torch.zeros(n + off, device="cuda")
+    mb = torch.zeros(n + off, device="cuda")
+    vb = torch.zeros(n + off, device="cuda")
+    w, m, v = wb[off:], mb[off:], vb[off:]
+    w.copy_(torch.from_numpy(w0))
+    ow, om, ov = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t, g in enumerate(grads, start=1):
+        r = fqlib.qat_step_int(w, torch.from_numpy(g).cuda(), m, v, t, cfg, bits, scheme, rounding, seed, 5)
+        torch.cuda.synchronize()
+        ref = orc.qat_step_int(ow, g, om, ov, lr, t, bits=bits, scheme=scheme, rounding=rounding, seed=seed,
+                               offset=5, weight_decay=wd)
+        ow, om, ov = ref["w"], ref["m"], ref["v"]
+        assert_f32(to_np(w), ow, f"master step {t}")
+        assert_f32(to_np(m), om, f"m step {t}")
+        assert_f32(to_np(v), ov, f"v step {t}")
+        s, zp, lo, hi = fqlib.params_fields(r["params"])
+        assert_bits(np.float32([s, lo, hi]), np.float32([ref["scale"], ref["lo"], ref["hi"]]), f"params step {t}")
+        assert zp == ref["zp"]
+        codes = to_np(r["codes"])
+        if bits == 4:
+            p = codes.astype(np.uint8)
+            hi4 = (p >> 4).astype(np.int16)
+            lo4 = (p & 0xF).astype(np.int16)
+            un = np.empty(2 * p.size, np.int16)
+            un[0::2] = np.where(hi4 >= 8, hi4 - 16, hi4)
+            un[1::2] = np.where(lo4 >= 8, lo4 - 16, lo4)
+            codes = un[:n].astype(np.int8)
+        else:
+            codes = codes.view(np.int8)
+        assert_bits(codes, ref["codes"], f"codes step {t}")
+        assert_f32(to_np(r["view"]), ref["view"], f"view step {t}")
+        assert int(r["flags"].item()) == ref["flags"]
