@@ -228,6 +228,23 @@ def test_argument_checks(fq):
     assert L.fq_qat_step_fp8(P, P, P, P, 8, ctypes.byref(cfg), 1, 3, 0, 0, 0, P, P, None) == fq.E_UNSUPPORTED
     assert L.fq_qat_step_fp8(P, P, P, P, 8, ctypes.byref(cfg), 1, 0, 0, 0, 0, None, None, None) == fq.E_INVALID
     assert L.fq_qat_step_fp8(P, None, P, P, 8, ctypes.byref(cfg), 1, 0, 0, 0, 0, P, P, None) == fq.E_INVALID
+    # empty inputs and missing buffers of the remaining entry points (no launch)
+    assert L.fq_dequantize_int_tensor(P, 0, 8, P, P, None) == fq.E_INVALID
+    assert L.fq_dequantize_int_tensor(P, 8, 6, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_dequantize_int_tensor(P, 8, 8, None, P, None) == fq.E_INVALID
+    assert L.fq_dequantize_rows(P, 0, 4, 8, P, P, P, None) == fq.E_INVALID
+    assert L.fq_dequantize_rows(P, 4, 0, 8, P, P, P, None) == fq.E_INVALID
+    assert L.fq_dequantize_rows(P, 4, 4, 2, P, P, P, None) == fq.E_UNSUPPORTED
+    assert L.fq_dequantize_rows(P, 4, 4, 8, P, None, P, None) == fq.E_INVALID
+    assert L.fq_fp8_tensor_scale(P, 0, P, 1 << 20, P, P, None, None) == fq.E_INVALID
+    assert L.fq_fp8_tensor_scale(P, 8, P, 1 << 20, None, None, None, None) == fq.E_INVALID
+    assert L.fq_fp8_tensor_scale(P, 8, P, 0, P, P, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_int(P, P, P, P, 0, ctypes.byref(cfg), 1, 8, 0, 0, 0, 0, P, ws, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_qat_step_fp8(P, P, P, P, 0, ctypes.byref(cfg), 1, 0, 0, 0, 0, P, P, None) == fq.E_INVALID
+    assert L.fq_quant_cols(P, 0, 4, 0, 8, 0, P, 1 << 20, P, P, P, P, None, None) == fq.E_INVALID
+    assert L.fq_mx_rows(P, 0, 4, 0, fq.E2M1, P, P, P, None) == fq.E_INVALID
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    assert L.fq_q4dq_sizes(0, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == fq.E_INVALID
     # STE: length mismatch, empty
     assert L.fq_ste_backward(P, 3, P, 2, P, P, None) == fq.E_DIM
     assert L.fq_ste_backward(P, 0, P, 0, P, P, None) == fq.E_INVALID
