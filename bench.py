@@ -332,7 +332,7 @@ def ops_next_cols(fq, syn, torch, dev):
     sca = torch.empty(ca, dtype=torch.float32, device=dev)
     zpa = torch.empty(ca, dtype=torch.int32, device=dev)
     ca8 = torch.empty(ra * ca, dtype=torch.uint8, device=dev)
-    ops.append(Op("cols.bf16_int8_affine", "k_cols_minmax+k_cols_fold+k_cols_quant",
+    ops.append(Op("cols.bf16_int8_affine", "k_cols_strip",
                   lambda: fq.fq_quant_cols(a, fq.BF16, ra, ca, 8, fq.AFFINE, wsa, wsba, ca8, fqa, sca, zpa, flags),
                   2 * ra * ca + ra * ca + 4 * ra * ca + 8 * ca))
     return ops

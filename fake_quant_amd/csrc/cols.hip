@@ -21,9 +21,9 @@
 //      once, then quantizes its rows; the blocks of the first band also write
 //      the scales, zero-points and flags.
 // x is read twice; the workspace holds the partials and the column records.
-// fp32 tensors of 1025..4096 rows with a multiple of 16 columns (at least half as
-// many 16-column strips as compute units) take one launch instead, k_cols_strip,
-// which reads x once (below).
+// Tensors of 1025..4096 rows whose column count is a multiple of the strip width
+// (16 fp32 or 32 bf16 columns), with at least half as many strips as compute
+// units, take one launch instead, k_cols_strip, which reads x once (below).
 #include "fq_device.h"
 #include "fq_host.h"
 
@@ -332,67 +332,132 @@ __global__ __launch_bounds__(kB) void k_cols_quant(const void* __restrict__ x, i
 }
 
 // ---------------------------------------------------------------------------
-// One-pass per-column path for fp32 tensors of at most kStripRows rows whose
-// column count is a multiple of kStripCols: a 1024-thread workgroup owns a strip
-// of kStripCols columns over all rows and keeps it in registers (thread t holds
-// one 16-byte vector of every 256th row: lane % 4 picks the vector of the
-// 64-byte row segment, lane / 4 + 16 * wave the row), so x is read once and the
-// strip's column statistics never leave the compute unit.  Column min / max:
-// per thread, across the lanes of a wave that share a vector (shuffles), across
-// the waves (LDS); one thread per column then derives the parameters.  Adjacent
-// strips share 128-byte lines, so the strips are dealt to workgroups such that
-// each XCD (workgroups go to the eight XCDs in turn) takes a contiguous run of
-// them and its L2 merges the halves: 36 us cold for [4096, 4096] against 51 us
-// with strip b on workgroup b, and against 46 us for the three-launch path.
+// One-pass per-column path for tensors of at most kStripRows rows whose column
+// count is a multiple of the strip width: a 1024-thread workgroup owns a strip of
+// columns whose row segment is 64 bytes (16 fp32 or 32 bf16 columns) over all
+// rows and keeps it in registers (64 VGPRs of x per thread), so x is read once
+// and the strip's column statistics never leave the compute unit.  Every lane
+// holds four columns of a row: lane % L picks the lane's piece of the row
+// segment (L = 4 pieces of 16 bytes for fp32, 8 of 8 bytes for bf16), lane / L
+// + (64 / L) * wave the row, so a load instruction covers 64 / L rows and a
+// thread holds every (1024 / L)-th row (16 rows for fp32, 32 for bf16).  Column
+// min / max: per thread, across the lanes of a wave that share a piece
+// (shuffles), across the waves (LDS); one thread per column then derives the
+// parameters.  Adjacent strips share 128-byte lines of x (and of the codes), so
+// the strips go to the XCDs (workgroups go to the eight XCDs in turn) in groups
+// of eight adjacent strips, whose shared lines one L2 then merges, and each XCD
+// takes groups from the whole width of the rows.  Cold (warm), interleaved, three
+// rounds on one box: fp32 [4096, 4096] int8 34.6-34.9 (28.6) us with groups of
+// eight, 35.2-35.4 (31.5) with a contiguous run of strips per XCD, 36.4-37.0
+// (29.9) with groups of four; bf16 [4096, 8192] int8 45.3-45.9 (38.8) with eight,
+// 47.2-47.4 (43.7) with a contiguous run, 47.1-48.3 (40.6) with four.  Groups of
+// two and of sixteen timed slower on another box.  The kernel this replaced (the
+// same layout for fp32 only, with a contiguous run per XCD and loads the
+// compiler had serialized two at a time) took 36.0-36.7 (33.0) us; the
+// three-launch path takes 46 us for that fp32 tensor and 57.8 (54.5) us for the
+// bf16 one, which it reads twice.
 // ---------------------------------------------------------------------------
 constexpr int kStripThreads = 1024;
-constexpr int kStripCols = 16;                               // 4 vectors of 4 fp32
-constexpr int kStripWaves = kStripThreads / kWave;           // 16
-constexpr int kStripRowsPerLoad = kStripThreads / 4;         // 256
-constexpr int kStripLoads = 16;                              // vectors per thread
-constexpr int64_t kStripRows = (int64_t)kStripRowsPerLoad * kStripLoads;  // 4096
+constexpr int kStripWaves = kStripThreads / kWave;  // 16
+constexpr int64_t kStripRows = 4096;                // rows a strip holds
 constexpr int kXcds = 8;
+constexpr int kStripGroup = 8;  // adjacent strips dealt to one XCD at a time
 
-template <int BITS>
-__global__ __launch_bounds__(kStripThreads) void k_cols_strip(const float* __restrict__ x, int64_t rows,
+template <int DT>
+struct Strip {
+    static constexpr int L = DT == FQ_F32 ? 4 : 8;             // lanes per 64-byte row segment
+    static constexpr int C = 4 * L;                            // columns of the strip
+    static constexpr int RPL = kStripThreads / L;              // rows per load instruction of the workgroup
+    static constexpr int LOADS = (int)(kStripRows / RPL);      // row pieces per thread
+    // loads issued per group before their min / max (cold, [4096, 4096] fp32 int8:
+    // 35.9-36.3 us with 2, 37.0-37.1 with 4, 38.6 with 8, 38.3-38.9 with all 16;
+    // [4096, 8192] bf16: 47.4-48.8 us with 4 or 8, 48.5-49.8 with 16 or 32)
+    static constexpr int DEPTH = DT == FQ_F32 ? 2 : 8;
+    // the raw 16 (fp32) or 8 (bf16) bytes of a lane's four columns
+    typedef uint32_t Piece __attribute__((ext_vector_type(DT == FQ_F32 ? 4 : 2)));
+    static_assert(LOADS * (int)sizeof(Piece) == 256, "64 VGPRs of x per thread");
+};
+
+// p as a wave-uniform (scalar) address: the readfirstlanes stop the compiler from
+// folding a lane offset into it, so base + lane offset becomes one load or store
+// with a scalar base and a 32-bit lane offset
+// (a global-memory pointer, so that the accesses stay global rather than flat)
+#define FQ_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ FQ_GLOBAL char* uniform_base(const void* p) {
+    const uint64_t a = (uint64_t)p;
+    // readfirstlane returns an int: both halves go back through uint32_t
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    return (FQ_GLOBAL char*)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// column e (0..3) of a lane's piece
+template <int DT>
+__device__ __forceinline__ float piece_col(const typename Strip<DT>::Piece& p, int e) {
+    if constexpr (DT == FQ_F32) {
+        return as_f(p[e]);
+    } else {
+        return (e & 1) ? bf16_hi(p[e >> 1]) : bf16_lo(p[e >> 1]);
+    }
+}
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(kStripThreads) void k_cols_strip(const void* __restrict__ x, int64_t rows,
                                                               int64_t cols, int affine,
                                                               uint8_t* __restrict__ codes, float* __restrict__ fq,
                                                               float* __restrict__ scale, int32_t* __restrict__ zp,
                                                               uint32_t* __restrict__ flags) {
+    using S = Strip<DT>;
+    using Piece = typename S::Piece;
+    // rows * cols < 2^31 and RPL <= rows on this path.  Load j covers the RPL
+    // rows from br(j) = min(j RPL, rows - RPL): a wave-uniform base address plus
+    // one 32-bit lane offset that is the same for every j.  A block clamped at
+    // the end loads some rows a second time, which leaves min / max unchanged;
+    // the store phase skips them.
     const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
-    const int vq = lane & 3;  // vector of the row segment
-    const int64_t nstrips = cols / kStripCols;
-    const int64_t b = blockIdx.x;
-    const int64_t strip = nstrips % kXcds == 0 ? (b % kXcds) * (nstrips / kXcds) + b / kXcds : b;
-    const int64_t c0 = strip * kStripCols + vq * 4;
-    const int64_t rbase = (int64_t)w * 16 + (lane >> 2);
+    const int vq = lane % S::L;  // piece of the row segment
+    const uint32_t nstrips = (uint32_t)(cols / S::C), ncols = (uint32_t)cols, nrows = (uint32_t)rows;
+    const uint32_t b = blockIdx.x;
+    // groups of kStripGroup adjacent strips go to the XCDs in turn (else a
+    // contiguous run per XCD, else strip b on workgroup b)
+    constexpr uint32_t Q = kStripGroup;
+    const uint32_t strip = nstrips % (kXcds * Q) == 0 ? ((b / kXcds) / Q * kXcds + b % kXcds) * Q + (b / kXcds) % Q
+                           : nstrips % kXcds == 0     ? (b % kXcds) * (nstrips / kXcds) + b / kXcds
+                                                      : b;
+    const uint32_t c0 = strip * S::C + vq * 4;
+    const uint32_t rbase = (uint32_t)w * (kWave / S::L) + (uint32_t)lane / S::L;
+    const uint32_t lane_el = rbase * ncols + c0;  // element offset of the lane in a block of rows
+    auto block_row = [&](int j) { return min((uint32_t)j * S::RPL, nrows - S::RPL); };
 
-    float4 v[kStripLoads];
-#pragma unroll
-    for (int j = 0; j < kStripLoads; ++j) {
-        const int64_t r = rbase + (int64_t)j * kStripRowsPerLoad;
-        v[j] = r < rows ? *reinterpret_cast<const float4*>(x + r * cols + c0) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    constexpr uint32_t ES = sizeof(Piece) / 4;  // bytes per element
+    Piece v[S::LOADS];
     MinMax m[4];
 #pragma unroll
-    for (int j = 0; j < kStripLoads; ++j) {
-        if (rbase + (int64_t)j * kStripRowsPerLoad >= rows) continue;
-        m[0].add(v[j].x);
-        m[1].add(v[j].y);
-        m[2].add(v[j].z);
-        m[3].add(v[j].w);
+    for (int g = 0; g < S::LOADS; g += S::DEPTH) {
+#pragma unroll
+        for (int j = g; j < g + S::DEPTH; ++j) {
+            const FQ_GLOBAL char* xb =
+                uniform_base(reinterpret_cast<const char*>(x) + (size_t)block_row(j) * ncols * ES);
+            v[j] = *reinterpret_cast<const FQ_GLOBAL Piece*>(xb + lane_el * ES);
+        }
+#pragma unroll
+        for (int j = g; j < g + S::DEPTH; ++j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e].add(piece_col<DT>(v[j], e));
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
 #pragma unroll
-        for (int k = 4; k < kWave; k <<= 1) {
+        for (int k = S::L; k < kWave; k <<= 1) {
             m[e].merge(__shfl_xor(m[e].mn, k), __shfl_xor(m[e].mx, k), (uint32_t)__shfl_xor((int)m[e].nf, k));
         }
     }
-    __shared__ float s_mn[kStripWaves][kStripCols], s_mx[kStripWaves][kStripCols];
-    __shared__ uint32_t s_nf[kStripWaves][kStripCols];
-    __shared__ float4 s_par[kStripCols];
-    if (lane < 4) {
+    __shared__ float s_mn[kStripWaves][S::C], s_mx[kStripWaves][S::C];
+    __shared__ uint32_t s_nf[kStripWaves][S::C];
+    __shared__ float4 s_par[S::C];
+    if (lane < S::L) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             s_mn[w][vq * 4 + e] = m[e].mn;
@@ -402,14 +467,14 @@ __global__ __launch_bounds__(kStripThreads) void k_cols_strip(const float* __res
     }
     __syncthreads();
     const IntRange rg = int_range(BITS, affine != 0);
-    if (t < kStripCols) {
+    if (t < S::C) {
         MinMax a;
         for (int k = 0; k < kStripWaves; ++k) a.merge(s_mn[k][t], s_mx[k][t], s_nf[k][t]);
         const IntCal cal = calibrate(a.mn, a.mx, rg, affine != 0);
         const ExactDiv d(cal.scale == 0.0f ? 1.0f : cal.scale);
         const uint32_t mode = (cal.scale == 0.0f ? 0u : (d.fast ? 1u : 2u)) | (a.nonfinite() ? 0u : kColFinite);
         s_par[t] = make_float4(cal.scale, d.y, as_f((uint32_t)cal.zp), as_f(mode));
-        const int64_t c = strip * kStripCols + t;
+        const uint32_t c = strip * S::C + t;
         scale[c] = cal.scale;
         zp[c] = cal.zp;
         const uint32_t f = (a.nonfinite() ? FQ_FLAG_NONFINITE : 0u) | (cal.degenerate ? FQ_FLAG_DEGENERATE : 0u);
@@ -431,12 +496,21 @@ __global__ __launch_bounds__(kStripThreads) void k_cols_strip(const float* __res
     // as k_cols_quant: a wave whose columns are all finite with divisors in the
     // exact-quotient window takes the bare quotient, clamp and magic rounding
     const bool fast = __all(lane_fast);
-    const int64_t pstride = BITS == 8 ? cols : cols / 2;
+    if constexpr (DT == FQ_BF16) {
+        // unpack x again below rather than keep the statistics phase's unpacked
+        // copy (twice the registers of the packed pieces)
 #pragma unroll
-    for (int j = 0; j < kStripLoads; ++j) {
-        const int64_t r = rbase + (int64_t)j * kStripRowsPerLoad;
-        if (r >= rows) break;
-        const float xv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        for (int j = 0; j < S::LOADS; ++j) asm volatile("" : "+v"(v[j]));
+    }
+    const uint32_t pstride = BITS == 8 ? ncols : ncols / 2;
+    const uint32_t lane_code = rbase * pstride + (BITS == 8 ? c0 : c0 / 2);  // byte offset, as lane_el
+#pragma unroll
+    for (int j = 0; j < S::LOADS; ++j) {
+        const uint32_t br = block_row(j);
+        if (br + rbase < (uint32_t)j * S::RPL) continue;  // a row an earlier j stored
+        float xv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[e] = piece_col<DT>(v[j], e);
         int code[4];
         float o[4];
         if (fast) {
@@ -454,10 +528,19 @@ __global__ __launch_bounds__(kStripThreads) void k_cols_strip(const float* __res
                 o[e] *= cp[e].x;
             }
         }
-        // fake-quant values with plain stores: the two halves of a 128-byte line
-        // come from adjacent strips on the same XCD and merge in its L2
-        store_row<4, BITS, true>(code, o, r, cols, c0, pstride, codes, nullptr);
-        if (fq) *reinterpret_cast<float4*>(fq + r * cols + c0) = make_float4(o[0], o[1], o[2], o[3]);
+        // fake-quant values with plain stores: for fp32 the two halves of a
+        // 128-byte line come from adjacent strips on the same XCD and merge in its L2
+        if (codes) {
+            FQ_GLOBAL char* cb = uniform_base(codes + (size_t)br * pstride) + lane_code;
+            if (BITS == 8)
+                *reinterpret_cast<FQ_GLOBAL uint32_t*>(cb) = pack4(code[0], code[1], code[2], code[3]);
+            else
+                *reinterpret_cast<FQ_GLOBAL uint16_t*>(cb) =
+                    (uint16_t)(nib2(code[0], code[1]) | (nib2(code[2], code[3]) << 8));
+        }
+        if (fq)
+            *reinterpret_cast<FQ_GLOBAL f32x4*>(uniform_base(fq + (size_t)br * ncols) + lane_el * 4u) =
+                f32x4{o[0], o[1], o[2], o[3]};
     }
 }
 
@@ -477,10 +560,12 @@ int launch_cols(const void* x, int64_t rows, int64_t cols, int affine, void* ws,
     const int64_t tiles = (cols + kWave * N - 1) / (kWave * N);
     const int64_t qtiles = (cols + kWave * kQuantVec - 1) / (kWave * kQuantVec);
     if (qtiles > 0x7FFFFFFF) return FQ_E_INVALID;
-    if (DT == FQ_F32 && alq && rows > kStripRows / 4 && rows <= kStripRows && cols % kStripCols == 0 &&
-        cols / kStripCols >= fqh::num_cus() / 2 && cols / kStripCols <= 0x7FFFFFFF) {
-        k_cols_strip<BITS><<<(unsigned)(cols / kStripCols), kStripThreads, 0, st>>>(
-            reinterpret_cast<const float*>(x), rows, cols, affine, codes, fq, scale, zp, flags);
+    constexpr int SC = Strip<DT>::C;
+    static_assert(Strip<DT>::RPL <= kStripRows / 4, "a strip's rows fill a block of RPL rows");
+    if (alq && rows > kStripRows / 4 && rows <= kStripRows && cols % SC == 0 && cols / SC >= fqh::num_cus() / 2 &&
+        rows * cols <= 0x7FFFFFFF) {
+        k_cols_strip<DT, BITS><<<(unsigned)(cols / SC), kStripThreads, 0, st>>>(x, rows, cols, affine, codes, fq,
+                                                                                scale, zp, flags);
         return fqh::launched();
     }
     const dim3 g1((unsigned)tiles, (unsigned)nb);

@@ -110,10 +110,13 @@ def test_strip_path_shapes(fqlib, orc, shape):
         check_cols(fqlib, orc, w, bits, scheme, f"strip {shape}")
 
 
-# bf16 at the row counts the fp32 strip kernel takes (bf16 keeps the
-# three-launch path: a bf16 strip kernel measured slower), with 4096 or more
-# columns, a column count that is not a multiple of 256, a partial 256-row load
-STRIP_SHAPES_BF16 = [(1025, 4096), (4096, 4128), (2500, 8192), (4095, 4096)]
+# bf16 shapes of the one-pass strip kernel (1024 < rows <= 4096, cols a multiple
+# of 32 with at least half as many 32-column strips as compute units): smallest
+# and largest row counts, rows that leave a partial 128-row load, a strip count
+# that is not a multiple of the eight XCDs; then column counts the strip kernel
+# does not take (a multiple of 4 but not of 32, too few strips), which go through
+# the three-launch path
+STRIP_SHAPES_BF16 = [(1025, 4096), (4096, 4128), (2500, 8192), (4095, 4096), (3000, 4100), (2048, 4064)]
 
 
 @pytest.mark.parametrize("shape", STRIP_SHAPES_BF16)
