@@ -23,11 +23,13 @@
 //
 // The digit a pass fixes is selected at the start of the next launch: every
 // workgroup of that launch sums the replicas and narrows prefix and rank of both
-// statistics itself (the same integer counts give every workgroup the same
-// selection; workgroup 0 stores it for the launches after), overlapping its first
-// loads of x.  The launch boundary orders the counts before those reads, so no
-// pass needs a counter or a fence.  A one-workgroup launch selects the last digit
-// and derives the parameters.
+// statistics itself with a scan over the workgroup (the same integer counts give
+// every workgroup the same selection; workgroup 0 stores it for the launches
+// after).  The second pass issues the loads of the counts before its first loads
+// of x and waits only for the counts, so the selection overlaps those loads; the
+// later launches issue all their independent loads at once.  The launch boundary
+// orders the counts before those reads, so no pass needs a counter or a fence.  A
+// one-workgroup launch selects the last digit and derives the parameters.
 //
 // The second pass also copies the keys that share either 11-bit prefix into a
 // per-workgroup slice of the workspace (sized for one key in 16 of the
@@ -44,7 +46,8 @@ using namespace fqk;
 namespace {
 
 // 1024 threads per workgroup (one workgroup of 16 waves per CU at the 256-workgroup
-// cap): 34.4-35.6 / 55.8-56.5 us cold at 2^20 / 2^24.  Measured slower at 2^24:
+// cap): 33.1-33.3 / 55.0-55.3 us cold at 2^20 / 2^24 (35.3-35.5 / 56.0 with a
+// one-wave selection and chained loads).  Measured slower at 2^24:
 // 512 threads with 512 or 1024 workgroups (59.4-60.0 / 74.8-74.9 us), 1024 threads
 // with 512 workgroups (69.0), eight 16-byte loads in flight (61.4-61.6), eight
 // replicas (58.5-58.6); two replicas, eight LDS copies, copies picked by lane,
@@ -122,46 +125,59 @@ __global__ __launch_bounds__(256) void k_pct_init(PctState* __restrict__ st) {
 // counts.  The next group's loads are issued before f runs on the current one.
 // The 1-3 elements after the last whole chunk form one more group in
 // workgroup 0.
+// The raw 16-byte chunks of a group (nfull >= 1).  Every lane loads (a chunk past
+// the end reloads the last one), so no branch sits between the loads and their
+// use, which the compiler would otherwise close with a wait for the loads.
 template <bool AL>
 __device__ __forceinline__ void load_group(const float* __restrict__ x, int64_t nfull, int64_t c0, int64_t stride,
-                                           float (&e)[4 * kU]) {
-    // every lane loads (a chunk past the end reloads the last one and is then
-    // replaced by NaN), so no branch separates the loads from their use
-    const float q = __builtin_nanf("");
+                                           float4 (&v)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
         const int64_t cu = c0 + threadIdx.x + u * stride;
         const int64_t cc = cu < nfull ? cu : nfull - 1;
-        float4 v;
-        if (AL) v = reinterpret_cast<const float4*>(x)[cc];
-        else v = make_float4(x[4 * cc], x[4 * cc + 1], x[4 * cc + 2], x[4 * cc + 3]);
-        const bool in = cu < nfull;
-        e[4 * u] = in ? v.x : q;
-        e[4 * u + 1] = in ? v.y : q;
-        e[4 * u + 2] = in ? v.z : q;
-        e[4 * u + 3] = in ? v.w : q;
+        if (AL) v[u] = reinterpret_cast<const float4*>(x)[cc];
+        else v[u] = make_float4(x[4 * cc], x[4 * cc + 1], x[4 * cc + 2], x[4 * cc + 3]);
     }
 }
 
-// pro() runs once, by every thread, after the first group's loads are issued
+// the group's elements, NaN (not counted) for the chunks past the end
+__device__ __forceinline__ void group_elems(const float4 (&v)[kU], int64_t nfull, int64_t c0, int64_t stride,
+                                            float (&e)[4 * kU]) {
+    const float q = __builtin_nanf("");
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+        const bool in = c0 + threadIdx.x + u * stride < nfull;
+        e[4 * u] = in ? v[u].x : q;
+        e[4 * u + 1] = in ? v[u].y : q;
+        e[4 * u + 2] = in ? v[u].z : q;
+        e[4 * u + 3] = in ? v[u].w : q;
+    }
+}
+
+// pro() runs once, by every thread, while the first group's loads are in flight;
+// each group's loads are issued before f() runs on the group before it
 template <bool AL, typename P, typename F>
 __device__ __forceinline__ void for_each_group(const float* __restrict__ x, int64_t n, P&& pro, F&& f) {
     const int64_t nfull = n >> 2;
     const int64_t stride = (int64_t)gridDim.x * kPB;
     const int64_t step = stride * kU;
-    float e[4 * kU];
     int64_t c0 = (int64_t)blockIdx.x * kPB;
-    if (c0 < nfull) load_group<AL>(x, nfull, c0, stride, e);
-    pro();
-    for (; c0 < nfull; c0 += step) {
-        float nxt[4 * kU];
-        load_group<AL>(x, nfull, c0 + step, stride, nxt);  // past the end: all NaN
-        f(e);
-#pragma unroll
-        for (int i = 0; i < 4 * kU; ++i) e[i] = nxt[i];
+    if (nfull > 0) {
+        float4 v[kU];
+        load_group<AL>(x, nfull, c0, stride, v);
+        pro();
+        for (; c0 < nfull; c0 += step) {
+            float e[4 * kU];
+            group_elems(v, nfull, c0, stride, e);
+            load_group<AL>(x, nfull, c0 + step, stride, v);  // the next group (past the end: unused)
+            f(e);
+        }
+    } else {
+        pro();
     }
     if (blockIdx.x == 0 && (n & 3)) {
         const float q = __builtin_nanf("");
+        float e[4 * kU];
 #pragma unroll
         for (int i = 0; i < 4 * kU; ++i) e[i] = q;
         if (threadIdx.x < (n & 3)) e[0] = x[4 * nfull + threadIdx.x];
@@ -211,31 +227,38 @@ __device__ __forceinline__ PctSel no_selection() {
     return z;
 }
 
+// This thread's bins of statistic s's replicas of pass PASS's histogram (agent
+// scope), in registers
+template <int PASS>
+using BinCounts = uint64_t[digit_bins(PASS) / kPB][kR];
+
+template <int PASS>
+__device__ __forceinline__ void load_counts(PctState* __restrict__ st, int s, BinCounts<PASS>& c) {
+    static_assert(digit_bins(PASS) % kPB == 0, "whole bins per thread");
+#pragma unroll
+    for (int j = 0; j < digit_bins(PASS) / kPB; ++j)
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+            c[j][r] = __hip_atomic_load(&st->hist[PASS][r][s][threadIdx.x + j * kPB], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Run by every thread of a workgroup, after the launch that filled pass PASS's
-// histograms: the replicas are summed into `sh` (LDS, 2 BINS counts; loaded at
-// agent scope), then the first wave, lane l holding bins [l PER, (l + 1) PER),
-// finds the bin holding each statistic's rank: that bin fixes the next digit,
-// and the rank becomes the rank within the bin.  The first digit also yields the
+// histograms, with c0 / c1 = load_counts of statistics 0 / 1 (c1 is read only
+// when the two prefixes differ; a caller issues these loads together with its
+// other independent loads): the replicas are summed into `sh` (LDS, 2 BINS counts),
+// then a scan over the workgroup finds the bin holding each statistic's rank:
+// that bin fixes the next digit, and the rank becomes the rank within the bin.  The first digit also yields the
 // count of finite values and the two ranks ([QAT] per_tensor_percentile:
 // floor(cf last), ceil((1 - cf) last) in f64).  The result is left in *out (LDS)
 // and returned to every thread; every workgroup of a launch derives the same one
 // from the same integer counts.
 template <int PASS>
-__device__ PctSel select_block(PctState* __restrict__ st, const PctSel& prev, double cf, uint64_t* sh,
-                               PctSel* out) {
+__device__ PctSel select_block(const PctSel& prev, double cf, uint64_t* sh, PctSel* out, const BinCounts<PASS>& c0,
+                               const BinCounts<PASS>& c1) {
     constexpr int BINS = digit_bins(PASS), SHIFT = digit_shift(PASS);
-    constexpr int PER = BINS / kWave;
-    static_assert(BINS % kPB == 0, "whole bins per thread");
     const bool shared = prev.shared != 0;
-    const int nstat = shared ? 1 : 2;
-    for (int s = 0; s < nstat; ++s) {
-        uint64_t c[BINS / kPB][kR];
-#pragma unroll
-        for (int j = 0; j < BINS / kPB; ++j)
-#pragma unroll
-            for (int r = 0; r < kR; ++r)
-                c[j][r] = __hip_atomic_load(&st->hist[PASS][r][s][threadIdx.x + j * kPB], __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
+    auto sum = [&](int s, const BinCounts<PASS>& c) {
 #pragma unroll
         for (int j = 0; j < BINS / kPB; ++j) {
             uint64_t t = 0;
@@ -243,76 +266,94 @@ __device__ PctSel select_block(PctState* __restrict__ st, const PctSel& prev, do
             for (int r = 0; r < kR; ++r) t += c[j][r];
             sh[s * BINS + threadIdx.x + j * kPB] = t;
         }
+    };
+    sum(0, c0);
+    if (!shared) sum(1, c1);
+    __syncthreads();
+    // thread t holds bins [t BPT, (t + 1) BPT) of each statistic's histogram (the
+    // first histogram for both while they share it); a scan over the workgroup
+    // (waves, then the wave totals) gives each thread the count below its bins
+    constexpr int BPT = BINS / kPB;
+    constexpr int NW = kPB / kWave;
+    __shared__ uint64_t s_wave[2][NW];
+    __shared__ uint64_t s_within[2];
+    __shared__ uint32_t s_digit[2];
+    const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
+    uint64_t hb[2][BPT], tot[2], incl[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int hs = shared ? 0 : k;
+        tot[k] = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            hb[k][j] = sh[hs * BINS + t * BPT + j];
+            tot[k] += hb[k][j];
+        }
+    }
+    incl[0] = wave_inclusive_scan(tot[0]);
+    incl[1] = shared ? incl[0] : wave_inclusive_scan(tot[1]);
+    if (lane == kWave - 1) {
+        s_wave[0][w] = incl[0];
+        s_wave[1][w] = incl[1];
+    }
+    if (t == 0) {
+        // no bin holds the rank (no finite value): digit 0, rank 0
+        s_digit[0] = s_digit[1] = 0;
+        s_within[0] = s_within[1] = 0;
     }
     __syncthreads();
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        uint64_t nfin = prev.nfin;
-        uint64_t rank[2] = {prev.rank[0], prev.rank[1]};
-        uint32_t prefix[2] = {prev.prefix[0], prev.prefix[1]};
-        uint64_t hb[PER];
-        uint64_t sum = 0;
-        auto load = [&](int s) {
-            sum = 0;
+    uint64_t below[2] = {0, 0}, all = 0;
 #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                hb[j] = sh[s * BINS + lane * PER + j];
-                sum += hb[j];
-            }
-        };
-        load(0);
-        uint64_t incl = wave_inclusive_scan(sum);
-        if (PASS == 0) {
-            // every finite value lands in a bin of the first pass
-            nfin = __shfl(incl, kWave - 1);
-            if (nfin > 0) {
-                const uint64_t last = nfin - 1;
-                const uint64_t lo = (uint64_t)floor(cf * (double)last);
-                const uint64_t hi = (uint64_t)ceil((1.0 - cf) * (double)last);
-                rank[0] = lo < last ? lo : last;
-                rank[1] = hi < last ? hi : last;
-            }
+    for (int v = 0; v < NW; ++v) {
+        const uint64_t a0 = s_wave[0][v], a1 = s_wave[1][v];
+        all += a0;
+        if (v < w) {
+            below[0] += a0;
+            below[1] += a1;
         }
+    }
+    uint64_t nfin = prev.nfin;
+    uint64_t rank[2] = {prev.rank[0], prev.rank[1]};
+    if (PASS == 0) {
+        // every finite value lands in a bin of the first pass
+        nfin = all;
         if (nfin > 0) {
+            const uint64_t last = nfin - 1;
+            const uint64_t lo = (uint64_t)floor(cf * (double)last);
+            const uint64_t hi = (uint64_t)ceil((1.0 - cf) * (double)last);
+            rank[0] = lo < last ? lo : last;
+            rank[1] = hi < last ? hi : last;
+        }
+    }
+    if (nfin > 0) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 1 && !shared) {
-                    load(1);
-                    incl = wave_inclusive_scan(sum);
-                }
-                const uint64_t excl = incl - sum, r = rank[s];
-                const bool mine = excl <= r && r < incl;
-                const uint64_t bal = __ballot(mine);
-                uint32_t digit = 0;
-                uint64_t within = 0;
-                if (mine) {
-                    uint64_t below = excl;
+        for (int k = 0; k < 2; ++k) {
+            uint64_t b = below[k] + incl[k] - tot[k];
+            const uint64_t r = rank[k];
+            if (b <= r && r < b + tot[k]) {
 #pragma unroll
-                    for (int j = 0; j < PER; ++j) {
-                        if (r < below + hb[j]) {
-                            digit = (uint32_t)(lane * PER + j);
-                            within = r - below;
-                            break;
-                        }
-                        below += hb[j];
+                for (int j = 0; j < BPT; ++j) {
+                    if (r < b + hb[k][j]) {
+                        s_digit[k] = (uint32_t)(t * BPT + j);
+                        s_within[k] = r - b;
+                        break;
                     }
+                    b += hb[k][j];
                 }
-                const int src = bal ? __builtin_ctzll(bal) : 0;
-                prefix[s] |= (uint32_t)__shfl((int)digit, src) << SHIFT;
-                rank[s] = __shfl(within, src);
             }
         }
-        if (lane == 0) {
-            PctSel r;
-            r.nfin = nfin;
-            r.rank[0] = rank[0];
-            r.rank[1] = rank[1];
-            r.prefix[0] = prefix[0];
-            r.prefix[1] = prefix[1];
-            r.mask = prev.mask | ((uint32_t)(BINS - 1) << SHIFT);
-            r.shared = prefix[0] == prefix[1] ? 1u : 0u;
-            *out = r;
-        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        PctSel r;
+        r.nfin = nfin;
+        r.rank[0] = nfin > 0 ? s_within[0] : rank[0];
+        r.rank[1] = nfin > 0 ? s_within[1] : rank[1];
+        r.prefix[0] = prev.prefix[0] | (nfin > 0 ? s_digit[0] << SHIFT : 0u);
+        r.prefix[1] = prev.prefix[1] | (nfin > 0 ? s_digit[1] << SHIFT : 0u);
+        r.mask = prev.mask | ((uint32_t)(BINS - 1) << SHIFT);
+        r.shared = r.prefix[0] == r.prefix[1] ? 1u : 0u;
+        *out = r;
     }
     __syncthreads();
     return *out;
@@ -363,9 +404,13 @@ __global__ __launch_bounds__(kPB) void k_pct_second(const float* __restrict__ x,
     bool shared = true;
     uint32_t* slice = cand + blockIdx.x * cap;
     const int lane = threadIdx.x % kWave;
+    // the counts are loaded before x, so that waiting for them (loads complete in
+    // the order they were issued) leaves the first loads of x in flight
+    BinCounts<0> c0;
+    load_counts<0>(st, 0, c0);
     for_each_group<AL>(x, n, [&] {
         // the barriers in select_block also order the zeroing above before the counts
-        const PctSel sel = select_block<0>(st, no_selection(), cf, sh, &s_sel);
+        const PctSel sel = select_block<0>(no_selection(), cf, sh, &s_sel, c0, c0);
         if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[0] = sel;
         mask = sel.mask;
         p0 = sel.prefix[0];
@@ -429,12 +474,22 @@ __global__ __launch_bounds__(kPB) void k_pct_third(const float* __restrict__ x, 
     uint32_t* h0 = h;
     uint32_t* h1 = h + BINS;
     for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h[i] = 0;
+    // every load that does not depend on another goes out at once: the selection
+    // of the first digit, both statistics' counts, the overflow flag, this
+    // workgroup's candidate count and its first candidates (slots past the count
+    // are read but not used; the slice holds cap slots)
     const PctSel prev = st->sel[0];
-    const PctSel sel = select_block<1>(st, prev, 0.0, sh, &s_sel);
+    BinCounts<1> c0, c1;
+    load_counts<1>(st, 0, c0);
+    load_counts<1>(st, 1, c1);
+    const bool from_x = st->overflow != 0;
+    const uint32_t* slice = cand + blockIdx.x * cap;
+    const uint32_t m = st->cnt[blockIdx.x];
+    const uint32_t k0 = (int64_t)threadIdx.x < cap ? slice[threadIdx.x] : 0u;
+    const PctSel sel = select_block<1>(prev, 0.0, sh, &s_sel, c0, c1);
     if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[1] = sel;
     const uint32_t mask = sel.mask, p0 = sel.prefix[0], p1 = sel.prefix[1];
     const bool shared = sel.shared != 0;
-    const bool from_x = st->overflow != 0;
     auto count = [&](uint32_t k) {
         const uint32_t bin = (k >> SHIFT) & (BINS - 1);
         if ((k & mask) == p0) atomicAdd(&h0[bin], 1u);
@@ -447,9 +502,8 @@ __global__ __launch_bounds__(kPB) void k_pct_third(const float* __restrict__ x, 
                 if (finite(e[i])) count(sort_key(e[i]));
         });
     } else {
-        const uint32_t* slice = cand + blockIdx.x * cap;
-        const uint32_t m = st->cnt[blockIdx.x];
-        for (uint32_t i = threadIdx.x; i < m; i += kPB) count(slice[i]);
+        if (threadIdx.x < m) count(k0);
+        for (uint32_t i = threadIdx.x + kPB; i < m; i += kPB) count(slice[i]);
     }
     __syncthreads();
     flush_bins<BINS>(st->hist[2][blockIdx.x % kR][0], [&](int b) { return h0[b]; });
@@ -462,7 +516,10 @@ __global__ __launch_bounds__(kPB) void k_pct_final(PctState* __restrict__ st, in
     __shared__ uint64_t sh[2 * digit_bins(2)];
     __shared__ PctSel s_sel;
     const PctSel prev = st->sel[1];
-    const PctSel sel = select_block<2>(st, prev, a.cf, sh, &s_sel);
+    BinCounts<2> c0, c1;
+    load_counts<2>(st, 0, c0);
+    load_counts<2>(st, 1, c1);
+    const PctSel sel = select_block<2>(prev, a.cf, sh, &s_sel, c0, c1);
     if (threadIdx.x != 0) return;
     const uint64_t nfin = sel.nfin;
     const float mn = nfin > 0 ? key_value(sel.prefix[0]) : __builtin_inff();
