@@ -281,11 +281,12 @@ size_t fq_cols_workspace_bytes(int64_t rows, int64_t cols);
  * float32 [rows, cols]; scale, zero_point: [cols].  workspace: device memory of
  * fq_cols_workspace_bytes(rows, cols), 16-byte aligned, contents not kept.
  * Three launches (column min / max over at most 64 bands of rows, the fold of
- * the bands, quantize with per-column parameters); x is read twice.  FQ_F32
- * tensors of 1025 to 4096 rows whose column count is a multiple of 16 (with at
- * least half as many 16-column strips as the device has compute units) and with
- * 16-byte aligned x / fq take one launch that reads x once and leaves the
- * workspace untouched. */
+ * the bands, quantize with per-column parameters); x is read twice.  Tensors of
+ * 1025 to 4096 rows with rows * cols < 2^31 whose column count is a multiple of
+ * the strip width (16 FQ_F32 or 32 FQ_BF16 columns, with at least half as many
+ * strips as the device has compute units), with x aligned to 16 (FQ_F32) or 8
+ * (FQ_BF16) bytes, fq to 16 and codes to 4 (int8) or 2 (int4) bytes, take one
+ * launch that reads x once and leaves the workspace untouched. */
 int fq_quant_cols(const void* x, int dtype, int64_t rows, int64_t cols, int bits, int scheme, void* workspace,
                   size_t workspace_bytes, void* codes, float* fq, float* scale, int32_t* zero_point, uint32_t* flags,
                   hipStream_t stream);

@@ -97,9 +97,11 @@ def test_bf16_quantize_vectors(fqlib, orc):
 
 # fp32 shapes of the one-pass strip kernel (1024 < rows <= 4096, cols a multiple
 # of 16 with at least half as many 16-column strips as compute units): smallest
-# and largest row counts, rows that leave a partial 256-row load, a strip count
-# that is not a multiple of the eight XCDs, and more strips than compute units
-STRIP_SHAPES = [(1025, 2048), (4096, 2080), (2500, 4096), (4095, 8192), (1536, 2064)]
+# and largest row counts, rows that leave a partial 256-row load, and each way of
+# dealing strips to workgroups: groups of eight adjacent strips (a strip count
+# divisible by 64), a contiguous run per XCD (136 strips: divisible by 8, not by
+# 64), strip b on workgroup b (130 and 129 strips), more strips than compute units
+STRIP_SHAPES = [(1025, 2048), (4096, 2080), (2500, 4096), (4095, 8192), (1536, 2064), (2000, 2176)]
 
 
 @pytest.mark.parametrize("shape", STRIP_SHAPES)
@@ -112,11 +114,13 @@ def test_strip_path_shapes(fqlib, orc, shape):
 
 # bf16 shapes of the one-pass strip kernel (1024 < rows <= 4096, cols a multiple
 # of 32 with at least half as many 32-column strips as compute units): smallest
-# and largest row counts, rows that leave a partial 128-row load, a strip count
-# that is not a multiple of the eight XCDs; then column counts the strip kernel
-# does not take (a multiple of 4 but not of 32, too few strips), which go through
-# the three-launch path
-STRIP_SHAPES_BF16 = [(1025, 4096), (4096, 4128), (2500, 8192), (4095, 4096), (3000, 4100), (2048, 4064)]
+# and largest row counts, rows that leave a partial 128-row load, strip counts
+# dealt in groups of eight (128, 256), as a contiguous run per XCD (136) and one
+# per workgroup (129); then column counts the strip kernel does not take (a
+# multiple of 4 but not of 32, too few strips), which go through the three-launch
+# path
+STRIP_SHAPES_BF16 = [(1025, 4096), (4096, 4128), (2500, 8192), (4095, 4096), (1999, 4352), (3000, 4100),
+                     (2048, 4064)]
 
 
 @pytest.mark.parametrize("shape", STRIP_SHAPES_BF16)
