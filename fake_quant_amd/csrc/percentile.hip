@@ -32,10 +32,18 @@
 // one-workgroup launch selects the last digit and derives the parameters.
 //
 // The second pass also copies the keys that share either 11-bit prefix into a
-// per-workgroup slice of the workspace (sized for one key in 16 of the
-// workgroup's share; typically a few percent match); the third pass then reads
-// only those slices, or x again if any slice overflowed.  Five launches (zeroing,
-// three passes, the last selection); x is read twice (three times on overflow).
+// per-workgroup slice of the workspace (one sub-slice per wave, together sized
+// for one key in 16 of the workgroup's share; typically a few percent match); the
+// third pass then reads only those slices, or x again if any slice overflowed.
+//
+// From kPredictMin elements on, the zeroing launch also predicts from a sample of
+// x which first-digit bins will hold the two statistics, and the first pass keeps
+// the keys of those bins as the candidates.  When the first digits the second
+// pass selects are among the predicted bins and nothing overflowed, the second
+// pass counts its digit over those candidates instead of x.  The selection always
+// runs on the full counts, so a wrong prediction costs time, not correctness.
+// Five launches (zeroing, three passes, the last selection); x is read once when
+// the prediction holds, twice otherwise (three times on an overflow).
 #include <cmath>
 
 #include "fq_device.h"
@@ -46,8 +54,9 @@ using namespace fqk;
 namespace {
 
 // 1024 threads per workgroup (one workgroup of 16 waves per CU at the 256-workgroup
-// cap): 33.1-33.3 / 55.0-55.3 us cold at 2^20 / 2^24 (35.3-35.5 / 56.0 with a
-// one-wave selection and chained loads).  Measured slower at 2^24:
+// cap): 33.3-33.8 / 48.5 us cold at 2^20 / 2^24 (54.7-54.9 us at 2^24 with x read
+// twice; 35.3-35.5 / 56.0 with a one-wave selection and chained loads).  Measured
+// slower at 2^24:
 // 512 threads with 512 or 1024 workgroups (59.4-60.0 / 74.8-74.9 us), 1024 threads
 // with 512 workgroups (69.0), eight 16-byte loads in flight (61.4-61.6), eight
 // replicas (58.5-58.6); two replicas, eight LDS copies, copies picked by lane,
@@ -64,6 +73,13 @@ constexpr int kU = 4;       // 16-byte loads in flight per thread
 constexpr int kR = 4;       // replicas of the device histograms
 constexpr int kCopies = 4;  // LDS copies of the first pass's histogram
 constexpr int kCandShare = 16;  // candidate slots: one per 16 elements of a workgroup's share
+constexpr int kPred = 6;         // predicted first-digit bins per order statistic, at most
+constexpr int kPredShare = 32;   // a prediction holds at most 1 in 32 of the sampled values
+constexpr int kSample = 16384;   // values the prediction samples
+constexpr int kSampleRun = 16;   // consecutive values per run of the sample
+constexpr int kSampleRuns = kSample / kSampleRun;
+constexpr int kInitThreads = 1024;
+constexpr int64_t kPredictMin = (int64_t)1 << 23;  // elements from which the first pass keeps predicted keys
 
 #ifndef FQ_PCT_MAX_BLOCKS
 #define FQ_PCT_MAX_BLOCKS 256
@@ -84,22 +100,32 @@ struct PctSel {
     uint32_t shared;  // the two prefixes agree: one histogram serves both
 };
 
+// per statistic the first-digit bins [lo, lo + nb) expected to hold it (nb = 0:
+// no prediction)
+struct PctPred {
+    uint32_t lo[2], nb[2];
+};
+
 struct PctState {
     uint64_t hist[kPasses][kR][2][kMaxBins];  // zeroed by k_pct_init
+    PctPred pp;  // the prediction (k_pct_init)
     PctSel sel[kPasses - 1];  // after the digits of passes 0 and 1 (block 0 of the next launch stores it)
-    uint32_t overflow;  // a candidate slice overflowed: the third pass reads x
-    uint32_t cnt[kMaxHistBlocks];  // candidates kept by each workgroup
+    uint32_t overflow;   // a candidate slice of the second pass overflowed: the third pass reads x
+    uint32_t overflow1;  // a candidate slice of the first pass overflowed: the second pass reads x
+    uint32_t cnt[kMaxHistBlocks][kPB / kWave];  // candidates kept by each wave (first pass, or the second when it reads x)
 };
 
 int64_t hist_blocks(int64_t n) {
     int64_t g = ((n >> 2) + (int64_t)kPB * kU - 1) / ((int64_t)kPB * kU);
     return g < 1 ? 1 : (g > kMaxHistBlocks ? kMaxHistBlocks : g);
 }
-// candidate slots per workgroup (a multiple of 4)
+// candidate slots per workgroup: one sub-slice per wave, each a multiple of 4
+// slots (together about one per kCandShare elements of the workgroup's share)
 int64_t cand_per_block(int64_t n) {
     const int64_t g = hist_blocks(n);
     const int64_t chunks = ((n >> 2) + g - 1) / g;  // 16-byte chunks of one workgroup, at most
-    return (4 * chunks / kCandShare + 64 + 3) / 4 * 4;
+    constexpr int64_t waves = kPB / kWave;
+    return (((4 * chunks / kCandShare + 64) + waves - 1) / waves + 3) / 4 * 4 * waves;
 }
 size_t state_bytes() { return (sizeof(PctState) + 255) / 256 * 256; }
 
@@ -112,19 +138,6 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 __device__ __forceinline__ bool finite(float v) { return fabsf(v) < __builtin_inff(); }
 
-constexpr int kInitWords = kPasses * kR * 2 * kMaxBins;
-
-__global__ __launch_bounds__(256) void k_pct_init(PctState* __restrict__ st) {
-    uint64_t* h = &st->hist[0][0][0][0];
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < kInitWords; i += gridDim.x * 256) h[i] = 0;
-    if (blockIdx.x == 0 && threadIdx.x == 0) st->overflow = 0;
-}
-
-// f(e) for each thread's group of 4 kU elements (kU 16-byte chunks), the loop
-// uniform over the workgroup: elements past the end are NaN, which no pass
-// counts.  The next group's loads are issued before f runs on the current one.
-// The 1-3 elements after the last whole chunk form one more group in
-// workgroup 0.
 // The raw 16-byte chunks of a group (nfull >= 1).  Every lane loads (a chunk past
 // the end reloads the last one), so no branch sits between the loads and their
 // use, which the compiler would otherwise close with a wait for the loads.
@@ -154,8 +167,12 @@ __device__ __forceinline__ void group_elems(const float4 (&v)[kU], int64_t nfull
     }
 }
 
-// pro() runs once, by every thread, while the first group's loads are in flight;
-// each group's loads are issued before f() runs on the group before it
+// f(e) for each thread's group of 4 kU elements (kU 16-byte chunks), the loop
+// uniform over the workgroup: elements past the end are NaN, which no pass
+// counts.  The 1-3 elements after the last whole chunk form one more group in
+// workgroup 0.  pro() runs once, by every thread, while the first group's loads
+// are in flight; each group's loads are issued before f() runs on the group
+// before it.
 template <bool AL, typename P, typename F>
 __device__ __forceinline__ void for_each_group(const float* __restrict__ x, int64_t n, P&& pro, F&& f) {
     const int64_t nfull = n >> 2;
@@ -359,19 +376,199 @@ __device__ PctSel select_block(const PctSel& prev, double cf, uint64_t* sh, PctS
     return *out;
 }
 
+// ---------------------------------------------------------------------------
+// Zeroing and prediction (one launch).  The workgroups zero the histograms and
+// flags.  For tensors of at least kPredictMin elements one more workgroup
+// predicts, per order statistic, the first-digit bins that will hold it, from a
+// sample of kSample values spread evenly over x: it counts the sample's first
+// digits, finds the sample ranks cf (count - 1) and (1 - cf) (count - 1) widened
+// by three standard deviations of a binomial count plus two, and keeps the run of
+// bins those ranks span when it is at most kPred bins long and holds at most 1 in
+// kPredShare sampled values (a long run or a heavy bin, as ties at a percentile
+// make, means no prediction).  A prediction only decides which keys the first
+// pass keeps; the selection always runs on the full counts, and a wrong
+// prediction sends the second pass back to x.  Below kPredictMin elements the
+// second pass reads x again, which costs less than the prediction.
+// ---------------------------------------------------------------------------
+constexpr int kHistWords = kPasses * kR * 2 * kMaxBins;
+constexpr int kSamplePer = kSample / kInitThreads;  // sample values per thread
+static_assert(kSample % kInitThreads == 0 && digit_bins(0) % kInitThreads == 0, "whole shares per thread");
+
+__device__ void predict_bins(PctState* __restrict__ st, const float* __restrict__ x, int64_t n, double cf) {
+    constexpr int BINS = digit_bins(0), SHIFT = digit_shift(0);
+    constexpr int BPT = BINS / kInitThreads, NW = kInitThreads / kWave;
+    __shared__ uint32_t h[BINS];
+    __shared__ uint32_t s_wave[NW];
+    __shared__ uint32_t s_bin[4];
+    const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
+    for (int i = t; i < BINS; i += kInitThreads) h[i] = 0;
+    if (t < 4) s_bin[t] = 0;
+    // the sample: all of x when n <= kSample, else kSampleRuns runs of
+    // kSampleRun consecutive values, run r starting at floor(r n / kSampleRuns)
+    // rounded down to a multiple of kSampleRun (the runs are distinct and whole
+    // cache lines).  Every lane loads (an index past a smaller x reloads its last
+    // value and is not counted), so the loads go out together.
+    const int64_t S = n < kSample ? n : kSample;
+    const double step = (double)n / (double)kSampleRuns;
+    float v[kSamplePer];
+#pragma unroll
+    for (int j = 0; j < kSamplePer; ++j) {
+        const int64_t i = t + j * kInitThreads;
+        int64_t e;
+        if (n <= kSample) {
+            e = i < n ? i : n - 1;
+        } else {
+            const int64_t r = i / kSampleRun;
+            e = ((int64_t)((double)r * step) & ~(int64_t)(kSampleRun - 1)) + i % kSampleRun;
+        }
+        v[j] = x[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSamplePer; ++j)
+        if (t + j * kInitThreads < S && finite(v[j])) atomicAdd(&h[sort_key(v[j]) >> SHIFT], 1u);
+    __syncthreads();
+    uint32_t hb[BPT], tot = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        hb[j] = h[t * BPT + j];
+        tot += hb[j];
+    }
+    const uint32_t incl = (uint32_t)wave_inclusive_scan(tot);
+    if (lane == kWave - 1) s_wave[w] = incl;
+    __syncthreads();
+    uint32_t below = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        all += s_wave[k];
+        if (k < w) below += s_wave[k];
+    }
+    if (all > 0) {
+        const double last = (double)(all - 1);
+        const uint32_t r[2] = {(uint32_t)floor(cf * last), (uint32_t)fmin(ceil((1.0 - cf) * last), last)};
+        const uint32_t m = (uint32_t)ceil(3.0 * sqrt((double)all * cf * (1.0 - cf))) + 2u;
+        const uint32_t ends[4] = {r[0] > m ? r[0] - m : 0u, r[0] + m < all ? r[0] + m : all - 1,
+                                  r[1] > m ? r[1] - m : 0u, r[1] + m < all ? r[1] + m : all - 1};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t b = below + incl - tot;
+            if (b <= ends[e] && ends[e] < b + tot) {
+#pragma unroll
+                for (int j = 0; j < BPT; ++j) {
+                    if (ends[e] < b + hb[j]) {
+                        s_bin[e] = (uint32_t)(t * BPT + j);
+                        break;
+                    }
+                    b += hb[j];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        PctPred p;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t lo = s_bin[2 * k], hi = s_bin[2 * k + 1];
+            const uint32_t nb = hi - lo + 1;
+            uint32_t held = 0;
+            if (nb <= kPred)
+                for (uint32_t b = lo; b <= hi; ++b) held += h[b];
+            p.lo[k] = lo;
+            p.nb[k] = all > 0 && nb <= kPred && (uint64_t)held * kPredShare <= all ? nb : 0u;
+        }
+        st->pp = p;
+    }
+}
+
+// zeroing workgroups, then (predict != 0) the predicting one
+__global__ __launch_bounds__(kInitThreads) void k_pct_init(PctState* __restrict__ st, const float* __restrict__ x,
+                                                           int64_t n, double cf, int predict) {
+    const unsigned zb = gridDim.x - (predict ? 1u : 0u);  // zeroing workgroups
+    if (blockIdx.x >= zb) {
+        predict_bins(st, x, n, cf);
+        return;
+    }
+    uint64_t* h = &st->hist[0][0][0][0];
+    for (int64_t i = (int64_t)blockIdx.x * kInitThreads + threadIdx.x; i < kHistWords; i += (int64_t)zb * kInitThreads)
+        h[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        st->overflow = 0;
+        st->overflow1 = 0;
+        if (!predict) st->pp = PctPred{{0u, 0u}, {0u, 0u}};
+    }
+}
+constexpr unsigned kInitBlocks = (kHistWords + kInitThreads - 1) / kInitThreads;
+
+// Keeps the keys of this thread's group whose bit i of mbits is set in its
+// wave's sub-slice of the candidate slice (capw slots; wcnt is the wave's count,
+// the same in every lane, and runs on past capw so that an overflow shows) and
+// calls kept(key) for each.  Candidates are rare, so only an element slot that
+// some lane keeps does any of this, and it needs no atomic: a key's position is
+// the wave's count plus the number of keeping lanes below its own.
+template <int NE, typename K>
+__device__ __forceinline__ void keep_in_wave(const uint32_t (&keys)[NE], uint32_t mbits, uint32_t* __restrict__ sub,
+                                             uint32_t capw, uint32_t& wcnt, K&& kept) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const uint64_t bal = __ballot((mbits >> i) & 1u);
+        if (bal == 0) continue;
+        if ((mbits >> i) & 1u) {
+            const uint32_t below =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            const uint32_t pos = wcnt + below;
+            if (pos < capw) sub[pos] = keys[i];
+            kept(keys[i]);
+        }
+        wcnt += (uint32_t)__builtin_popcountll(bal);
+    }
+}
+
+// the wave's count of kept candidates (at most capw) and the overflow flag
+__device__ __forceinline__ void store_wave_count(PctState* __restrict__ st, uint32_t wcnt, uint32_t capw,
+                                                 uint32_t* __restrict__ overflow) {
+    if (threadIdx.x % kWave == 0) {
+        st->cnt[blockIdx.x][threadIdx.x / kWave] = wcnt < capw ? wcnt : capw;
+        if (wcnt > capw) atomicOr(overflow, 1u);
+    }
+}
+
 // first pass: the top 11 bits of every finite key, kCopies LDS histograms (waves
-// w and w + kCopies share one)
+// w and w + kCopies share one).  With a prediction, a key in a statistic's
+// predicted bins is also kept in its wave's candidate sub-slice.
 template <bool AL>
-__global__ __launch_bounds__(kPB) void k_pct_first(const float* __restrict__ x, int64_t n, PctState* __restrict__ st) {
+__global__ __launch_bounds__(kPB) void k_pct_first(const float* __restrict__ x, int64_t n, PctState* __restrict__ st,
+                                                   uint32_t* __restrict__ cand, int64_t cap) {
     constexpr int BINS = digit_bins(0), SHIFT = digit_shift(0);
     __shared__ uint32_t h[kCopies * BINS];
+    const PctPred pp = st->pp;
+    const bool pred = pp.nb[0] != 0 && pp.nb[1] != 0;
     for (int i = threadIdx.x; i < kCopies * BINS; i += kPB) h[i] = 0;
     __syncthreads();
     uint32_t* hw = h + ((threadIdx.x / kWave) % kCopies) * BINS;
+    const uint32_t capw = (uint32_t)(cap / (kPB / kWave));
+    uint32_t* sub = cand + blockIdx.x * cap + (threadIdx.x / kWave) * capw;
+    uint32_t wcnt = 0;
     for_each_group<AL>(x, n, [] {}, [&](const float (&e)[4 * kU]) {
+        if (!pred) {
 #pragma unroll
-        for (int i = 0; i < 4 * kU; ++i)
-            if (finite(e[i])) atomicAdd(&hw[sort_key(e[i]) >> SHIFT], 1u);
+            for (int i = 0; i < 4 * kU; ++i)
+                if (finite(e[i])) atomicAdd(&hw[sort_key(e[i]) >> SHIFT], 1u);
+            return;
+        }
+        uint32_t keys[4 * kU];
+        uint32_t mbits = 0;  // bit i: element i is a candidate
+#pragma unroll
+        for (int i = 0; i < 4 * kU; ++i) {
+            const bool fin = finite(e[i]);
+            const uint32_t k = sort_key(e[i]);
+            const uint32_t b = k >> SHIFT;
+            if (fin) atomicAdd(&hw[b], 1u);
+            const bool m = fin && (b - pp.lo[0] < pp.nb[0] || b - pp.lo[1] < pp.nb[1]);
+            keys[i] = k;
+            mbits |= m ? 1u << i : 0u;
+        }
+        keep_in_wave(keys, mbits, sub, capw, wcnt, [](uint32_t) {});
     });
     __syncthreads();
     flush_bins<BINS>(st->hist[0][blockIdx.x % kR][0], [&](int b) {
@@ -380,85 +577,77 @@ __global__ __launch_bounds__(kPB) void k_pct_first(const float* __restrict__ x, 
         for (int w = 0; w < kCopies; ++w) c += h[w * BINS + b];
         return c;
     });
+    if (pred) store_wave_count(st, wcnt, capw, &st->overflow1);
 }
 
 // second pass: every workgroup first derives the first digit from the first
-// pass's histogram (while its first loads of x are in flight; workgroup 0 stores
-// the selection for the launches after it), then counts the middle 11 bits of the
-// keys that share a statistic's 11-bit prefix; those keys are also kept in this
-// workgroup's candidate slice
+// pass's histogram (workgroup 0 stores the selection for the launches after it),
+// then counts the middle 11 bits of the keys that share a statistic's 11-bit
+// prefix.  When both statistics' bins were predicted and no sub-slice
+// overflowed, those keys are among the first pass's candidates, and each wave
+// counts its own sub-slice: x is not read again and the candidates stay for the
+// third pass.  Otherwise the pass reads x and keeps the matching keys as the new
+// candidates.
 template <bool AL>
 __global__ __launch_bounds__(kPB) void k_pct_second(const float* __restrict__ x, int64_t n,
                                                     PctState* __restrict__ st, uint32_t* __restrict__ cand,
                                                     int64_t cap, double cf) {
-    constexpr int BINS = digit_bins(1), SHIFT = digit_shift(1);
+    constexpr int BINS = digit_bins(1), SHIFT = digit_shift(1), SHIFT0 = digit_shift(0);
     __shared__ uint64_t sh[2 * digit_bins(0)];
     __shared__ PctSel s_sel;
     __shared__ uint32_t h[2 * BINS];
-    __shared__ uint32_t s_cnt;
     uint32_t* h0 = h;
     uint32_t* h1 = h + BINS;
-    for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h[i] = 0;
-    if (threadIdx.x == 0) s_cnt = 0;
-    uint32_t mask = 0, p0 = 0, p1 = 0;
-    bool shared = true;
-    uint32_t* slice = cand + blockIdx.x * cap;
-    const int lane = threadIdx.x % kWave;
-    // the counts are loaded before x, so that waiting for them (loads complete in
-    // the order they were issued) leaves the first loads of x in flight
+    // the loads that do not depend on the selection go out first: the counts, the
+    // prediction, the first pass's overflow flag, this wave's candidate count and
+    // its first candidates (slots past the count are read but not used)
     BinCounts<0> c0;
     load_counts<0>(st, 0, c0);
-    for_each_group<AL>(x, n, [&] {
-        // the barriers in select_block also order the zeroing above before the counts
-        const PctSel sel = select_block<0>(no_selection(), cf, sh, &s_sel, c0, c0);
-        if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[0] = sel;
-        mask = sel.mask;
-        p0 = sel.prefix[0];
-        p1 = sel.prefix[1];
-        shared = sel.shared != 0;
-    }, [&](const float (&e)[4 * kU]) {
+    const PctPred pp = st->pp;
+    const uint32_t ovf1 = st->overflow1;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const uint32_t capw = (uint32_t)(cap / (kPB / kWave));
+    uint32_t* sub = cand + blockIdx.x * cap + w * capw;
+    const uint32_t m1 = st->cnt[blockIdx.x][w];
+    const uint32_t k0 = (uint32_t)lane < capw ? sub[lane] : 0u;
+    for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h[i] = 0;
+    // the barriers in select_block also order the zeroing above before the counts
+    const PctSel sel = select_block<0>(no_selection(), cf, sh, &s_sel, c0, c0);
+    if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[0] = sel;
+    const uint32_t d0 = (sel.prefix[0] >> SHIFT0) - pp.lo[0], d1 = (sel.prefix[1] >> SHIFT0) - pp.lo[1];
+    const bool shared = sel.shared != 0;
+    const uint32_t mask = sel.mask, p0 = sel.prefix[0], p1 = sel.prefix[1];
+    auto count = [&](uint32_t k) {
+        const uint32_t bin = (k >> SHIFT) & (BINS - 1);
+        if ((k & mask) == p0) atomicAdd(&h0[bin], 1u);
+        if (!shared && (k & mask) == p1) atomicAdd(&h1[bin], 1u);
+    };
+    if (sel.nfin > 0 && ovf1 == 0 && d0 < pp.nb[0] && d1 < pp.nb[1]) {
+        if ((uint32_t)lane < m1) count(k0);
+        for (uint32_t i = lane + kWave; i < m1; i += kWave) count(sub[i]);
+        __syncthreads();
+        flush_bins<BINS>(st->hist[1][blockIdx.x % kR][0], [&](int b) { return h0[b]; });
+        if (!shared) flush_bins<BINS>(st->hist[1][blockIdx.x % kR][1], [&](int b) { return h1[b]; });
+        return;
+    }
+    uint32_t wcnt = 0;
+    for_each_group<AL>(x, n, [] {}, [&](const float (&e)[4 * kU]) {
         uint32_t keys[4 * kU];
         uint32_t mbits = 0;  // bit i: element i is a candidate
 #pragma unroll
         for (int i = 0; i < 4 * kU; ++i) {
             const uint32_t k = sort_key(e[i]);
             const bool fin = finite(e[i]);
-            const bool m0 = fin && (k & mask) == p0;
-            const bool m1 = fin && !shared && (k & mask) == p1;
-            const uint32_t bin = (k >> SHIFT) & (BINS - 1);
-            if (m0) atomicAdd(&h0[bin], 1u);
-            if (m1) atomicAdd(&h1[bin], 1u);
+            const bool m = fin && ((k & mask) == p0 || (!shared && (k & mask) == p1));
             keys[i] = k;
-            mbits |= (m0 || m1) ? 1u << i : 0u;
+            mbits |= m ? 1u << i : 0u;
         }
-        const uint32_t cnt = (uint32_t)__builtin_popcount(mbits);
-        if (__ballot(cnt != 0) == 0) return;
-        // one LDS reservation for the wave: an inclusive scan of the lane counts
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
-            if (lane >= off) incl += y;
-        }
-        uint32_t base = 0;
-        if (lane == kWave - 1) base = atomicAdd(&s_cnt, incl);
-        base = __builtin_amdgcn_readlane(base, kWave - 1);
-        int64_t pos = (int64_t)base + incl - cnt;
-#pragma unroll
-        for (int i = 0; i < 4 * kU; ++i) {
-            if ((mbits >> i) & 1u) {
-                if (pos < cap) slice[pos] = keys[i];
-                ++pos;
-            }
-        }
+        keep_in_wave(keys, mbits, sub, capw, wcnt, count);
     });
     __syncthreads();
     flush_bins<BINS>(st->hist[1][blockIdx.x % kR][0], [&](int b) { return h0[b]; });
     if (!shared) flush_bins<BINS>(st->hist[1][blockIdx.x % kR][1], [&](int b) { return h1[b]; });
-    if (threadIdx.x == 0) {
-        st->cnt[blockIdx.x] = (int64_t)s_cnt < cap ? s_cnt : (uint32_t)cap;
-        if ((int64_t)s_cnt > cap) atomicOr(&st->overflow, 1u);
-    }
+    store_wave_count(st, wcnt, capw, &st->overflow);
 }
 
 // third pass: every workgroup derives the second digit (workgroup 0 stores the
@@ -475,17 +664,19 @@ __global__ __launch_bounds__(kPB) void k_pct_third(const float* __restrict__ x, 
     uint32_t* h1 = h + BINS;
     for (int i = threadIdx.x; i < 2 * BINS; i += kPB) h[i] = 0;
     // every load that does not depend on another goes out at once: the selection
-    // of the first digit, both statistics' counts, the overflow flag, this
-    // workgroup's candidate count and its first candidates (slots past the count
-    // are read but not used; the slice holds cap slots)
+    // of the first digit, both statistics' counts, the overflow flag, this wave's
+    // candidate count and its first candidates (slots past the count are read but
+    // not used; the wave's sub-slice holds capw slots).  Wave w reads sub-slice w.
     const PctSel prev = st->sel[0];
     BinCounts<1> c0, c1;
     load_counts<1>(st, 0, c0);
     load_counts<1>(st, 1, c1);
     const bool from_x = st->overflow != 0;
-    const uint32_t* slice = cand + blockIdx.x * cap;
-    const uint32_t m = st->cnt[blockIdx.x];
-    const uint32_t k0 = (int64_t)threadIdx.x < cap ? slice[threadIdx.x] : 0u;
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const uint32_t capw = (uint32_t)(cap / (kPB / kWave));
+    const uint32_t* sub = cand + blockIdx.x * cap + w * capw;
+    const uint32_t m = st->cnt[blockIdx.x][w];
+    const uint32_t k0 = (uint32_t)lane < capw ? sub[lane] : 0u;
     const PctSel sel = select_block<1>(prev, 0.0, sh, &s_sel, c0, c1);
     if (blockIdx.x == 0 && threadIdx.x == 0) st->sel[1] = sel;
     const uint32_t mask = sel.mask, p0 = sel.prefix[0], p1 = sel.prefix[1];
@@ -502,8 +693,8 @@ __global__ __launch_bounds__(kPB) void k_pct_third(const float* __restrict__ x, 
                 if (finite(e[i])) count(sort_key(e[i]));
         });
     } else {
-        if (threadIdx.x < m) count(k0);
-        for (uint32_t i = threadIdx.x + kPB; i < m; i += kPB) count(slice[i]);
+        if ((uint32_t)lane < m) count(k0);
+        for (uint32_t i = lane + kWave; i < m; i += kWave) count(sub[i]);
     }
     __syncthreads();
     flush_bins<BINS>(st->hist[2][blockIdx.x % kR][0], [&](int b) { return h0[b]; });
@@ -540,7 +731,7 @@ template <bool AL>
 void launch_passes(const float* x, int64_t n, PctState* st, uint32_t* cand, int64_t cap, const SelectArgs& a,
                    hipStream_t stream) {
     const unsigned G = (unsigned)hist_blocks(n);
-    k_pct_first<AL><<<G, kPB, 0, stream>>>(x, n, st);
+    k_pct_first<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap);
     k_pct_second<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap, a.cf);
     k_pct_third<AL><<<G, kPB, 0, stream>>>(x, n, st, cand, cap);
     k_pct_final<<<1, kPB, 0, stream>>>(st, n, a);
@@ -565,7 +756,8 @@ int fq_tensor_params_percentile(const float* x, int64_t n, int bits, int scheme,
     PctState* st = reinterpret_cast<PctState*>(workspace);
     uint32_t* cand = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) + state_bytes());
     const SelectArgs a{clip_fraction, bits, scheme == FQ_AFFINE ? 1 : 0, params, flags};
-    k_pct_init<<<(kInitWords + 255) / 256, 256, 0, stream>>>(st);
+    const int predict = n >= kPredictMin;
+    k_pct_init<<<kInitBlocks + (predict ? 1u : 0u), kInitThreads, 0, stream>>>(st, x, n, clip_fraction, predict);
     if (fqh::aligned(x, 16)) launch_passes<true>(x, n, st, cand, cand_per_block(n), a, stream);
     else launch_passes<false>(x, n, st, cand, cand_per_block(n), a, stream);
     return fqh::launched();

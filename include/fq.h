@@ -331,7 +331,10 @@ size_t fq_percentile_workspace_bytes(int64_t n);
  * and 10 bits of an order-preserving key, each pass's digit selected at the start
  * of the next launch, and a one-workgroup launch for the last digit and the
  * parameters; x is read twice, the third pass reading only the candidates the
- * second one kept, or x once more if they did not fit); no host
+ * second one kept, or x once more if they did not fit).  From 2^23 elements on,
+ * a sample of x predicts the statistics' first-digit bins, the first pass keeps
+ * their keys, and when the prediction holds the second pass reads those instead
+ * of x (x read once); the result does not depend on the prediction.  No host
  * synchronisation. */
 int fq_tensor_params_percentile(const float* x, int64_t n, int bits, int scheme, double clip_fraction,
                                 void* workspace, size_t workspace_bytes, fq_int_params* params, uint32_t* flags,

@@ -174,3 +174,59 @@ def test_selected_bins_of_known_size(fqlib, orc):
     x = torch.from_numpy(v).cuda()
     ref = check(fqlib, orc, x, 8, 1, 0.25, "selected bins of known size")
     assert 1.0 <= ref["sel_min"] < 1.25 and 4.0 <= ref["sel_max"] < 5.0
+
+
+# From 2^23 elements on, a sample of x (runs of 16 values from each multiple of
+# n / 1024) predicts the first-digit bins of both statistics, the first pass
+# keeps the keys of those bins, and the second pass counts them instead of x.
+# Each case below takes one branch of that path and is checked against the
+# oracle like every other.
+PRED_N = 1 << 23
+
+
+def test_prediction_hits(fqlib, orc):
+    rng = np.random.default_rng(31)
+    v = (rng.standard_normal(PRED_N) * 0.05).astype(np.float32)
+    x = torch.from_numpy(v).cuda()
+    for bits, scheme, cf in ((8, 1, 0.001), (4, 0, 0.02)):
+        check(fqlib, orc, x, bits, scheme, cf, "predicted bins hit")
+    # the unaligned form of the passes
+    check(fqlib, orc, x[1:], 8, 1, 0.001, "predicted bins hit, view +1")
+
+
+def test_prediction_misses(fqlib, orc):
+    # cf 0 (the minimum and maximum): the extremes of x lie beyond those of the
+    # sample, outside the predicted bins
+    rng = np.random.default_rng(31)
+    v = (rng.standard_normal(PRED_N) * 0.05).astype(np.float32)
+    check(fqlib, orc, torch.from_numpy(v).cuda(), 4, 0, 0.0, "extremes beyond the sample")
+    # the sampled runs are drawn twice as wide as the rest, so the predicted tail
+    # bins lie an octave out: the second pass must go back to x
+    rng = np.random.default_rng(32)
+    v = (rng.standard_normal(PRED_N) * 0.1).astype(np.float32)
+    runs = v.reshape(1024, -1)
+    runs[:, :16] = (rng.standard_normal((1024, 16)) * 0.2).astype(np.float32)
+    x = torch.from_numpy(v).cuda()
+    for bits, scheme, cf in ((8, 1, 0.001), (8, 0, 0.005)):
+        check(fqlib, orc, x, bits, scheme, cf, "predicted bins miss")
+
+
+def test_prediction_slice_overflow(fqlib, orc):
+    # sorted values: the keys of the predicted lower-tail bins all fall in the
+    # first chunks, so a few waves get far more than their sub-slices hold
+    rng = np.random.default_rng(33)
+    v = np.sort(rng.standard_normal(PRED_N).astype(np.float32))
+    x = torch.from_numpy(v).cuda()
+    for bits, scheme, cf in ((8, 1, 0.001), (4, 1, 0.01)):
+        check(fqlib, orc, x, bits, scheme, cf, "predicted keys overflow a sub-slice")
+
+
+def test_no_prediction(fqlib, orc):
+    rng = np.random.default_rng(34)
+    # half the values tie at zero, where the lower statistic lies: its bin holds
+    # far more than 1 in 32 sampled values, so nothing is predicted
+    relu = np.maximum(rng.standard_normal(PRED_N), 0.0).astype(np.float32)
+    check(fqlib, orc, torch.from_numpy(relu).cuda(), 8, 1, 0.001, "tie at the lower statistic")
+    # cf 0.3 of a normal tensor: the widened rank windows span heavy bins
+    v = rng.standard_normal(PRED_N).astype(np.float32)
+    check(fqlib, orc, torch.from_numpy(v).cuda(), 8, 0, 0.3, "heavy predicted bins")
