@@ -341,8 +341,9 @@ def ops_next_cols(fq, syn, torch, dev):
 def ops_next_percentile(fq, syn, torch, dev):
     """Percentile calibration ([QAT] QuantParams::per_tensor_percentile, clip
     fraction 0.001, int8 affine) of the 2^20 tensor and of the [4096, 4096] fp32
-    weights flattened; the algorithmic bytes are one read of the tensor, though
-    the radix selection reads it four times."""
+    weights flattened; the algorithmic bytes are one read of the tensor, which the
+    radix selection reads twice at 2^20 and once at 2^24 (where a sample predicts
+    the candidates)."""
     params = torch.empty(4, dtype=torch.int32, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
     n1 = syn.FULL["tensor"]["n"]
