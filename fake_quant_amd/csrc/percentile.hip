@@ -54,9 +54,9 @@ using namespace fqk;
 namespace {
 
 // 1024 threads per workgroup (one workgroup of 16 waves per CU at the 256-workgroup
-// cap): 33.3-33.8 / 48.5 us cold at 2^20 / 2^24 (54.7-54.9 us at 2^24 with x read
-// twice; 35.3-35.5 / 56.0 with a one-wave selection and chained loads).  Measured
-// slower at 2^24:
+// cap): 33.6-33.7 / 46.8-46.9 us cold at 2^20 / 2^24 (54.7-54.9 us at 2^24 with x
+// read twice; 35.3-35.5 / 56.0 with a one-wave selection and chained loads).
+// Measured slower at 2^24:
 // 512 threads with 512 or 1024 workgroups (59.4-60.0 / 74.8-74.9 us), 1024 threads
 // with 512 workgroups (69.0), eight 16-byte loads in flight (61.4-61.6), eight
 // replicas (58.5-58.6); two replicas, eight LDS copies, copies picked by lane,
@@ -73,11 +73,12 @@ constexpr int kU = 4;       // 16-byte loads in flight per thread
 constexpr int kR = 4;       // replicas of the device histograms
 constexpr int kCopies = 4;  // LDS copies of the first pass's histogram
 constexpr int kCandShare = 16;  // candidate slots: one per 16 elements of a workgroup's share
-constexpr int kPred = 6;         // predicted first-digit bins per order statistic, at most
+constexpr int kPred = 8;         // predicted first-digit bins per order statistic, at most
 constexpr int kPredShare = 32;   // a prediction holds at most 1 in 32 of the sampled values
-constexpr int kSample = 16384;   // values the prediction samples
+constexpr int kSample = 8192;    // values the prediction samples
 constexpr int kSampleRun = 16;   // consecutive values per run of the sample
 constexpr int kSampleRuns = kSample / kSampleRun;
+constexpr int kSampleCopies = 4;  // LDS copies of the sample's histogram (lane l counts into copy l mod 4)
 constexpr int kInitThreads = 1024;
 constexpr int64_t kPredictMin = (int64_t)1 << 23;  // elements from which the first pass keeps predicted keys
 
@@ -397,11 +398,11 @@ static_assert(kSample % kInitThreads == 0 && digit_bins(0) % kInitThreads == 0, 
 __device__ void predict_bins(PctState* __restrict__ st, const float* __restrict__ x, int64_t n, double cf) {
     constexpr int BINS = digit_bins(0), SHIFT = digit_shift(0);
     constexpr int BPT = BINS / kInitThreads, NW = kInitThreads / kWave;
-    __shared__ uint32_t h[BINS];
+    __shared__ uint32_t h[kSampleCopies * BINS];
     __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_bin[4];
     const int t = threadIdx.x, lane = t % kWave, w = t / kWave;
-    for (int i = t; i < BINS; i += kInitThreads) h[i] = 0;
+    for (int i = t; i < kSampleCopies * BINS; i += kInitThreads) h[i] = 0;
     if (t < 4) s_bin[t] = 0;
     // the sample: all of x when n <= kSample, else kSampleRuns runs of
     // kSampleRun consecutive values, run r starting at floor(r n / kSampleRuns)
@@ -424,16 +425,24 @@ __device__ void predict_bins(PctState* __restrict__ st, const float* __restrict_
         v[j] = x[e];
     }
     __syncthreads();
+    // lanes of one instruction spread over kSampleCopies histograms: most sampled
+    // values fall in a few bins, whose atomics would otherwise queue on one address
+    uint32_t* hc = h + (lane % kSampleCopies) * BINS;
 #pragma unroll
     for (int j = 0; j < kSamplePer; ++j)
-        if (t + j * kInitThreads < S && finite(v[j])) atomicAdd(&h[sort_key(v[j]) >> SHIFT], 1u);
+        if (t + j * kInitThreads < S && finite(v[j])) atomicAdd(&hc[sort_key(v[j]) >> SHIFT], 1u);
     __syncthreads();
     uint32_t hb[BPT], tot = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-        hb[j] = h[t * BPT + j];
+        hb[j] = 0;
+#pragma unroll
+        for (int c = 0; c < kSampleCopies; ++c) hb[j] += h[c * BINS + t * BPT + j];
         tot += hb[j];
     }
+    __syncthreads();  // every copy is read before the sums overwrite copy 0
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) h[t * BPT + j] = hb[j];
     const uint32_t incl = (uint32_t)wave_inclusive_scan(tot);
     if (lane == kWave - 1) s_wave[w] = incl;
     __syncthreads();

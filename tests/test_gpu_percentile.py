@@ -177,7 +177,7 @@ def test_selected_bins_of_known_size(fqlib, orc):
 
 
 # From 2^23 elements on, a sample of x (runs of 16 values from each multiple of
-# n / 1024) predicts the first-digit bins of both statistics, the first pass
+# n / 512) predicts the first-digit bins of both statistics, the first pass
 # keeps the keys of those bins, and the second pass counts them instead of x.
 # Each case below takes one branch of that path and is checked against the
 # oracle like every other.
@@ -200,8 +200,9 @@ def test_prediction_misses(fqlib, orc):
     rng = np.random.default_rng(31)
     v = (rng.standard_normal(PRED_N) * 0.05).astype(np.float32)
     check(fqlib, orc, torch.from_numpy(v).cuda(), 4, 0, 0.0, "extremes beyond the sample")
-    # the sampled runs are drawn twice as wide as the rest, so the predicted tail
-    # bins lie an octave out: the second pass must go back to x
+    # runs of 16 values from each multiple of n / 1024 (the sampled runs among
+    # them) are drawn twice as wide as the rest, so the predicted tail bins lie an
+    # octave out: the second pass must go back to x
     rng = np.random.default_rng(32)
     v = (rng.standard_normal(PRED_N) * 0.1).astype(np.float32)
     runs = v.reshape(1024, -1)
