@@ -62,7 +62,11 @@ namespace {
 // replicas (58.5-58.6); two replicas, eight LDS copies, copies picked by lane,
 // plain loads of the counts and zeroing the later histograms in the first pass
 // timed the same.  (The selection of a digit by the last workgroup of its own
-// pass, found with an agent-scope release counter, took 63.5-64.2 us at 2^24.)
+// pass, found with an agent-scope release counter, took 63.5-64.2 us at 2^24.
+// Only the last selection done so, by the workgroup of the third pass that draws
+// the last ticket of a done counter, took 49.8 / 34.9 us at 2^24 / 2^20 with one
+// agent-scope release per workgroup -- an L2 write-back each -- and 78.4 / 42.3
+// with one per wave.)
 #ifndef FQ_PCT_THREADS
 #define FQ_PCT_THREADS 1024
 #endif
