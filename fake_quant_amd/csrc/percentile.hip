@@ -54,9 +54,10 @@ using namespace fqk;
 namespace {
 
 // 1024 threads per workgroup (one workgroup of 16 waves per CU at the 256-workgroup
-// cap): 33.6-33.7 / 46.8-46.9 us cold at 2^20 / 2^24 (54.7-54.9 us at 2^24 with x
-// read twice; 35.3-35.5 / 56.0 with a one-wave selection and chained loads).
-// Measured slower at 2^24:
+// cap): 31.4-31.6 / 45.3-45.6 us cold at 2^20 / 2^24 (33.3-33.4 / 46.6-46.8 with
+// four 16-byte loads in flight per thread and a sample of 8192 values; 54.7-54.9
+// us at 2^24 with x read twice; 35.3-35.5 / 56.0 with a one-wave selection and
+// chained loads).  Measured slower at 2^24:
 // 512 threads with 512 or 1024 workgroups (59.4-60.0 / 74.8-74.9 us), 1024 threads
 // with 512 workgroups (69.0), eight 16-byte loads in flight (61.4-61.6), eight
 // replicas (58.5-58.6); two replicas, eight LDS copies, copies picked by lane,
@@ -73,13 +74,13 @@ namespace {
 constexpr int kPB = FQ_PCT_THREADS;  // threads per workgroup of the passes
 constexpr int kPasses = 3;
 constexpr int kMaxBins = 2048;
-constexpr int kU = 4;       // 16-byte loads in flight per thread
+constexpr int kU = 2;       // 16-byte loads in flight per thread (4: 1.0-1.7 us slower cold; 8 slower still)
 constexpr int kR = 4;       // replicas of the device histograms
 constexpr int kCopies = 4;  // LDS copies of the first pass's histogram
 constexpr int kCandShare = 16;  // candidate slots: one per 16 elements of a workgroup's share
 constexpr int kPred = 8;         // predicted first-digit bins per order statistic, at most
 constexpr int kPredShare = 32;   // a prediction holds at most 1 in 32 of the sampled values
-constexpr int kSample = 8192;    // values the prediction samples
+constexpr int kSample = 4096;    // values the prediction samples
 constexpr int kSampleRun = 16;   // consecutive values per run of the sample
 constexpr int kSampleRuns = kSample / kSampleRun;
 constexpr int kSampleCopies = 4;  // LDS copies of the sample's histogram (lane l counts into copy l mod 4)

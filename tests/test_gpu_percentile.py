@@ -123,16 +123,16 @@ def test_unaligned_view_and_dirty_workspace(fqlib, orc):
 
 
 def test_candidate_slice_overflow(fqlib, orc):
-    # 2^20 elements: 2^18 16-byte chunks over 64 histogram workgroups of 1024
-    # threads, chunk c taken by thread c mod 65536, so workgroup 0 owns the chunks
-    # with c mod 65536 < 1024.  Filling those with c mod 65536 < 256 with the
-    # tensor's top value sends 4096 keys into workgroup 0's candidate slice (room
-    # for about 1 in 16) while the other slices stay small: the third pass must
-    # fall back to x.
+    # 2^20 elements: 2^18 16-byte chunks over 128 histogram workgroups of 1024
+    # threads, chunk c taken by thread c mod 131072, so workgroup 0 owns the chunks
+    # with c mod 131072 < 1024.  Filling those with c mod 131072 < 256 with the
+    # tensor's top value sends 2048 keys into workgroup 0's candidate slice (room
+    # for 576, about 1 in 16 of its share) while the other slices stay small: the
+    # third pass must fall back to x.
     n = 1 << 20
     v = (np.random.default_rng(14).standard_normal(n) * 0.1).astype(np.float32)
     chunks = v.reshape(-1, 4)
-    chunks[(np.arange(chunks.shape[0]) % 65536) < 256] = 1.0
+    chunks[(np.arange(chunks.shape[0]) % 131072) < 256] = 1.0
     x = torch.from_numpy(v).cuda()
     for cf, scheme in ((0.001, 1), (0.0001, 0), (0.01, 1)):
         check(fqlib, orc, x, 8, scheme, cf, "one slice overflows")
@@ -141,8 +141,8 @@ def test_candidate_slice_overflow(fqlib, orc):
 def test_many_candidates_per_slice(fqlib, orc):
     # values +-2^e (1 + u / 8) for 32 exponents e: each sign and exponent is one
     # 11-bit prefix, so the two selected prefixes hold 1/32 of the elements, about
-    # 512 keys in each workgroup's candidate slice at 2^20 elements (many
-    # candidates, but fewer than a slice holds, 1088)
+    # 256 keys in each workgroup's candidate slice at 2^20 elements (many
+    # candidates, but fewer than a slice holds, 576)
     n = 1 << 20
     rng = np.random.default_rng(21)
     e = rng.integers(0, 32, n).astype(np.float64)
@@ -155,16 +155,17 @@ def test_many_candidates_per_slice(fqlib, orc):
 
 def test_selected_bins_of_known_size(fqlib, orc):
     # ranks lo and hi (cf 0.25) inside prefixes of exactly 128 keys in every
-    # workgroup's share: per 16384-element share of the 64 histogram workgroups at
-    # 2^20 elements, 4000 values in [0.5, 0.75), 128 in [1, 1.25) (the bin of rank
-    # lo), 8128 in [2, 2.5), 128 in [4, 5) (the bin of rank hi) and 4000 in [8, 10),
-    # so every candidate slice holds exactly 256 keys
+    # workgroup's share: per 8192-element share of the 128 histogram workgroups at
+    # 2^20 elements (chunk c in workgroup (c mod 131072) / 1024), 2000 values in
+    # [0.5, 0.75), 64 in [1, 1.25) (the bin of rank lo), 4064 in [2, 2.5), 64 in
+    # [4, 5) (the bin of rank hi) and 2000 in [8, 10), so every candidate slice
+    # holds exactly 128 keys
     n = 1 << 20
     rng = np.random.default_rng(22)
-    wg = ((np.arange(n) // 4) % 65536) // 1024
+    wg = ((np.arange(n) // 4) % 131072) // 1024
     v = np.empty(n, np.float32)
-    parts = ((4000, 0.5, 0.75), (128, 1.0, 1.25), (8128, 2.0, 2.5), (128, 4.0, 5.0), (4000, 8.0, 10.0))
-    for b in range(64):
+    parts = ((2000, 0.5, 0.75), (64, 1.0, 1.25), (4064, 2.0, 2.5), (64, 4.0, 5.0), (2000, 8.0, 10.0))
+    for b in range(128):
         idx = rng.permutation(np.flatnonzero(wg == b))
         k = 0
         for cnt, lo, hi in parts:
@@ -177,7 +178,7 @@ def test_selected_bins_of_known_size(fqlib, orc):
 
 
 # From 2^23 elements on, a sample of x (runs of 16 values from each multiple of
-# n / 512) predicts the first-digit bins of both statistics, the first pass
+# n / 256) predicts the first-digit bins of both statistics, the first pass
 # keeps the keys of those bins, and the second pass counts them instead of x.
 # Each case below takes one branch of that path and is checked against the
 # oracle like every other.
