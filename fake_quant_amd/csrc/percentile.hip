@@ -74,7 +74,7 @@ namespace {
 constexpr int kPB = FQ_PCT_THREADS;  // threads per workgroup of the passes
 constexpr int kPasses = 3;
 constexpr int kMaxBins = 2048;
-constexpr int kU = 2;       // 16-byte loads in flight per thread (4: 1.0-1.7 us slower cold; 8 slower still)
+constexpr int kU = 2;       // 16-byte loads in flight per thread (3 or 4: 1.0-1.7 us slower cold; 1 and 8 slower too)
 constexpr int kR = 4;       // replicas of the device histograms
 constexpr int kCopies = 4;  // LDS copies of the first pass's histogram
 constexpr int kCandShare = 16;  // candidate slots: one per 16 elements of a workgroup's share
