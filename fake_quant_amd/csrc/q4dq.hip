@@ -64,7 +64,12 @@ constexpr int kOccDequant = FQ_OCC_Q4DQ;
 // stores (nt, or nt sc1) no faster than global nontemporal ones.  Staging a
 // super-block's codes in LDS so that each lane stores 16 bytes (8 store
 // instructions per super-block instead of 64): 1487-1488 against 1498-1499 us
-// (three runs each, one box).
+// (three runs each, one box).  The dequantize with one super-block per workgroup
+// and plain stores ran 811-815 against 825-828 us cold on its own, but the
+// quantize + dequantize step took 2.328-2.340 against 2.321-2.333 ms (the plain
+// stores leave dirty lines for the next operation), and plain stores with four
+// super-blocks 848-853 us; two, four or any number of resident workgroups per CU
+// instead of one 876-886 us.
 #ifndef FQ_Q4_LD_CP
 #define FQ_Q4_LD_CP 2
 #endif
