@@ -25,7 +25,9 @@ constexpr int kB = fqh::kBlock;
 // 98.6-98.7 -> 96.3-96.8 us, E5M2 98.0-98.1 -> 95.1-95.4 us, dequantize -0.5 to
 // -1 us.  The same stores in the per-row kernels cost them 1-2 points cold, and
 // the per-tensor and wide-layout kernels did not move, so those keep global
-// nontemporal stores.
+// nontemporal stores.  Plain stores: the dequantize 52.6-53.0 against 54.9-55.0
+// us cold, but 57 against 48 us warm and the fp8 step 0.379-0.382 against
+// 0.341-0.346 ms (the plain stores leave dirty lines to the ops after them).
 #ifndef FQ_FP8_OUT_CP
 #define FQ_FP8_OUT_CP 18
 #endif
